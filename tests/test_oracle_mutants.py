@@ -1,0 +1,60 @@
+"""Plant plausible mistakes in copies of the oracle; some pin must catch each one."""
+import importlib.util
+import os
+import sys
+import types
+import warnings
+
+import pytest
+
+import oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "flce_oracle.py")
+
+MUTANTS = {
+    "no_max_shift": ("return m + np.log(np.exp(z - m[:, None]).sum(axis=1))",
+                     "return np.log(np.exp(z).sum(axis=1))"),
+    "nll_sign": ("nll = lse - zy", "nll = zy - lse"),
+    "label_off_by_one": ("zy[r0 + rows] = z[rows, labels[r0 + rows]]",
+                         "zy[r0 + rows] = z[rows, (labels[r0 + rows] + 1) % V]"),
+    "mean_over_all_tokens": ("mean = float(out[valid].sum() / n_valid) if n_valid else 0.0",
+                             "mean = float(out.sum() / T)"),
+    "dropped_onehot": ("g[rows, labels[rows]] -= 1.0", "pass"),
+    "logprob_grad_sign": ("    if mode == \"logprob\":\n        g = -g\n", ""),
+    "ignored_tokens_get_grad": ("return np.where(valid, g, 0.0)", "return g"),
+    "mean_grad_over_T": ("g = np.full(valid.shape, gm / n_valid if n_valid else 0.0)",
+                         "g = np.full(valid.shape, gm / len(valid))"),
+    "bf16_decode_shift": ("f32 = (b.astype(np.uint32) << np.uint32(16)).view(np.float32)",
+                          "f32 = (b.astype(np.uint32) << np.uint32(15)).view(np.float32)"),
+    "dh_uses_softmax_only": ("dh[r0:r1] = g @ w", "dh[r0:r1] = np.exp(z - l[:, None]) @ w"),
+    "dw_transposed_rows": ("dw += g.T @ h[r0:r1]", "dw += (g.T @ h[r0:r1])[::-1]"),
+}
+
+
+def _mutant(name):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site not found once: {old!r}"
+    modname = f"flce_oracle_mutant_{name}"
+    mod = types.ModuleType(modname)
+    sys.modules[modname] = mod          # dataclasses look the module up by name
+    try:
+        exec(compile(src.replace(old, new), SRC, "exec"), mod.__dict__)
+    finally:
+        del sys.modules[modname]
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _mutant(name)
+    caught = []
+    for check in pins.ALL_CHECKS:
+        with warnings.catch_warnings():
+            warnings.simplefilter("ignore")
+            try:
+                check(mod)
+            except (AssertionError, ValueError, FloatingPointError, IndexError):
+                caught.append(check.__name__)
+    assert caught, f"mutant {name} passed every pin"
