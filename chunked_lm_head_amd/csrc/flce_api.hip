@@ -1,0 +1,414 @@
+// flce_api.hip - host side of the C ABI declared in include/flce.h: argument
+// checks, the schedule for a shape, the workspace layout and the launches.
+//
+// Schedule (all tiles are 256 x 256, K steps of 64):
+//  * Forward: one fused launch over (token tile, vocabulary split).  The number
+//    of splits is chosen so that about 2048 workgroups exist (8 per CU); each
+//    walks ~n_vt/splits vocabulary tiles keeping a running log-sum-exp, so the
+//    workspace holds only splits x T partials.
+//  * Backward: rows are taken in blocks of R tokens (R <= 8192) and the
+//    vocabulary in chunks of Vc rows, with R * Vc bf16 gradient values no more
+//    than the fp32 logits of one chunk of chunk_rows rows (chunk_rows * V * 4
+//    bytes), the bound the pages' Equation 3 describes.  Per (row block,
+//    vocabulary chunk): recompute + G, dH partial sums, dW update.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "flce.h"
+#include "flce_kernels.hpp"
+
+namespace {
+
+using namespace flce;
+
+thread_local char g_last_error[512] = "";
+
+flce_status fail(flce_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+flce_status fail(flce_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+constexpr int64_t kMaxD = 1 << 16;
+constexpr int64_t kMaxTV = (int64_t)1 << 30;  // T and V each
+constexpr int64_t kRowBlockMax = 8192;
+constexpr int64_t kFwdTargetWG = 2048;
+constexpr int64_t kDhTargetWG = 512;
+constexpr int64_t kDhPartialCap = (int64_t)128 << 20;  // bytes of split-K partial sums
+constexpr int64_t kI32Bytes = ((int64_t)1 << 31) - 1;
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Plan {
+  int64_t T, D, V, chunk_rows;
+  int64_t n_tt, n_vt, splits, T_pad;          // forward
+  int64_t R, n_rb, Vc, n_vc, dh_splits, Tb;   // backward; Tb = n_rb * R
+  int64_t n_cblk;
+  size_t off_pm, off_ps, off_zl, off_bs, off_bc, fwd_bytes;
+  size_t off_c, off_l2, off_G, off_dh, bwd_bytes;
+  size_t gtile_bytes, chunk_bound;
+  size_t total;
+};
+
+flce_status check_shape(int64_t T, int64_t D, int64_t V, int64_t chunk_rows) {
+  if (T < 0) return fail(FLCE_ERR_SHAPE, "T = %lld must be >= 0", (long long)T);
+  if (D < 1 || V < 1 || chunk_rows < 1)
+    return fail(FLCE_ERR_SHAPE, "D = %lld, V = %lld, chunk_rows = %lld must be >= 1",
+                (long long)D, (long long)V, (long long)chunk_rows);
+  if (D % 8) return fail(FLCE_ERR_UNSUPPORTED, "D = %lld is not a multiple of 8", (long long)D);
+  if (D > kMaxD || T > kMaxTV || V > kMaxTV)
+    return fail(FLCE_ERR_SHAPE, "sizes out of range (D <= %lld, T and V <= %lld)",
+                (long long)kMaxD, (long long)kMaxTV);
+  return FLCE_OK;
+}
+
+flce_status make_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows, Plan &p) {
+  flce_status st = check_shape(T, D, V, chunk_rows);
+  if (st != FLCE_OK) return st;
+  memset(&p, 0, sizeof(p));
+  p.T = T;
+  p.D = D;
+  p.V = V;
+  p.chunk_rows = chunk_rows;
+  const int64_t Tn = std::max<int64_t>(T, 1);
+  p.n_tt = cdiv(Tn, kTile);
+  p.n_vt = cdiv(V, kTile);
+  p.T_pad = p.n_tt * kTile;
+  p.splits = std::min<int64_t>(std::max<int64_t>(cdiv(kFwdTargetWG, p.n_tt), 1), p.n_vt);
+  p.n_cblk = cdiv(Tn, 256);
+
+  // Backward blocking.  cap = bf16 gradient values allowed = chunk_rows*V*4 / 2.
+  if (chunk_rows > kMaxTV) chunk_rows = kMaxTV;
+  const int64_t cap = std::max<int64_t>(chunk_rows * V * 2, (int64_t)kTile * kTile);
+  // 32-bit tile addressing: any operand spanned by one tile stays below 2 GiB.
+  const int64_t vc_lim = std::max<int64_t>(kTile, (kI32Bytes / (2 * D)) / kTile * kTile);
+  int64_t R = std::min<int64_t>(kRowBlockMax, p.n_tt * kTile);
+  int64_t n_rb = cdiv(p.n_tt * kTile, R);
+  R = cdiv(p.n_tt, n_rb) * kTile;
+  int64_t vc_max = cap / R / kTile * kTile;
+  if (vc_max < kTile) {
+    R = std::max<int64_t>(kTile, cap / kTile / kTile * kTile);
+    n_rb = cdiv(p.n_tt * kTile, R);
+    R = cdiv(p.n_tt, n_rb) * kTile;
+    vc_max = kTile;
+  }
+  vc_max = std::min(vc_max, vc_lim);
+  vc_max = std::min(vc_max, std::max<int64_t>(kTile, (kI32Bytes / (2 * R)) / kTile * kTile));
+  int64_t n_vc = cdiv(p.n_vt * kTile, vc_max);
+  const int64_t tiles_per_chunk = cdiv(p.n_vt, n_vc);
+  n_vc = cdiv(p.n_vt, tiles_per_chunk);
+  p.R = R;
+  p.n_rb = cdiv(p.n_tt * kTile, R);
+  p.Tb = p.n_rb * R;
+  p.Vc = tiles_per_chunk * kTile;
+  p.n_vc = n_vc;
+  const int64_t dh_tiles = (R / kTile) * cdiv(D, kTile);
+  int64_t sp = std::max<int64_t>(1, cdiv(kDhTargetWG, dh_tiles));
+  sp = std::min(sp, std::max<int64_t>(1, kDhPartialCap / (R * D * 4)));
+  sp = std::min(sp, cdiv(p.Vc, kBK));
+  p.dh_splits = sp;
+
+  size_t off = 0;
+  p.off_pm = off; off = align256(off + (size_t)p.splits * p.T_pad * 4);
+  p.off_ps = off; off = align256(off + (size_t)p.splits * p.T_pad * 4);
+  p.off_zl = off; off = align256(off + (size_t)p.T_pad * 4);
+  p.off_bs = off; off = align256(off + (size_t)p.n_cblk * 8);
+  p.off_bc = off; off = align256(off + (size_t)p.n_cblk * 4);
+  p.fwd_bytes = off;
+  off = 0;
+  p.off_c = off;  off = align256(off + (size_t)p.Tb * 4);
+  p.off_l2 = off; off = align256(off + (size_t)p.Tb * 4);
+  p.off_G = off;  off = align256(off + (size_t)p.R * p.Vc * 2);
+  p.off_dh = off; off = align256(off + (size_t)p.dh_splits * p.R * p.D * 4);
+  p.bwd_bytes = off;
+  p.gtile_bytes = (size_t)p.R * p.Vc * 2;
+  p.chunk_bound = (size_t)p.chunk_rows * p.V * 4;
+  p.total = std::max(p.fwd_bytes, p.bwd_bytes);
+  return FLCE_OK;
+}
+
+bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+flce_status check_device() {
+  static int cache[64];  // 0 unknown, 1 ok, 2 unsupported
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FLCE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(FLCE_ERR_UNSUPPORTED, "device index %d", dev);
+  if (cache[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(FLCE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    cache[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (cache[dev] == 2) {
+      snprintf(g_last_error, sizeof(g_last_error), "device %d is %s, not gfx950", dev,
+               prop.gcnArchName);
+    }
+  }
+  if (cache[dev] != 1) return FLCE_ERR_UNSUPPORTED;
+  return FLCE_OK;
+}
+
+flce_status launched(const char *what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FLCE_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  return FLCE_OK;
+}
+
+#define FLCE_TRY(x)                      \
+  do {                                   \
+    flce_status s_ = (x);                \
+    if (s_ != FLCE_OK) return s_;        \
+  } while (0)
+
+flce_status fill(float *dst, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return FLCE_OK;
+  const int64_t blocks = std::min<int64_t>(cdiv(n, 256), 4096);
+  fill_f32_kernel<<<(unsigned)blocks, 256, 0, s>>>(dst, n, v);
+  return launched("fill");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t flce_workspace_bytes(int64_t T, int64_t D, int64_t V, int64_t chunk_rows) {
+  Plan p;
+  if (make_plan(T, D, V, chunk_rows, p) != FLCE_OK) return 0;
+  return p.total;
+}
+
+flce_status flce_describe_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows,
+                               int64_t *info) {
+  if (!info) return fail(FLCE_ERR_ARG, "info is NULL");
+  Plan p;
+  FLCE_TRY(make_plan(T, D, V, chunk_rows, p));
+  const int64_t v[12] = {p.n_tt, p.n_vt, p.splits, p.R, p.n_rb, p.Vc, p.n_vc, p.dh_splits,
+                         (int64_t)p.fwd_bytes, (int64_t)p.bwd_bytes, (int64_t)p.gtile_bytes,
+                         (int64_t)p.chunk_bound};
+  memcpy(info, v, sizeof(v));
+  return FLCE_OK;
+}
+
+const char *flce_status_string(int status) {
+  switch (status) {
+    case FLCE_OK: return "ok";
+    case FLCE_ERR_ARG: return "invalid argument (pointer, alignment or mode)";
+    case FLCE_ERR_SHAPE: return "invalid or too large shape";
+    case FLCE_ERR_WORKSPACE: return "workspace too small";
+    case FLCE_ERR_UNSUPPORTED: return "unsupported shape or device";
+    case FLCE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *flce_last_error(void) { return g_last_error; }
+
+flce_status flce_forward(const void *hidden, const void *weight, const int64_t *labels,
+                         int64_t T, int64_t D, int64_t V, int64_t ignore_index,
+                         int64_t chunk_rows, int mode, float *out, float *lse, float *mean_out,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+  g_last_error[0] = 0;
+  Plan p;
+  FLCE_TRY(make_plan(T, D, V, chunk_rows, p));
+  if (mode != FLCE_MODE_NLL && mode != FLCE_MODE_LOGPROB)
+    return fail(FLCE_ERR_ARG, "mode %d is neither NLL (0) nor LOGPROB (1)", mode);
+  if (T > 0) {
+    if (!hidden || !weight || !labels || !out || !lse || !workspace)
+      return fail(FLCE_ERR_ARG, "a required pointer is NULL");
+    if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(labels, 8) ||
+        !aligned(out, 4) || !aligned(lse, 4) || !aligned(workspace, 16) ||
+        (mean_out && !aligned(mean_out, 4)))
+      return fail(FLCE_ERR_ARG, "misaligned pointer (hidden/weight/workspace need 16 bytes)");
+    if (workspace_bytes < p.total)
+      return fail(FLCE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
+                  p.total);
+  }
+  FLCE_TRY(check_device());
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) return mean_out ? fill(mean_out, 1, 0.f, s) : FLCE_OK;
+
+  char *ws = (char *)workspace;
+  FwdLseParams a;
+  a.hidden = (const uint16_t *)hidden;
+  a.weight = (const uint16_t *)weight;
+  a.labels = labels;
+  a.ignore_index = ignore_index;
+  a.T = (int)T;
+  a.D = (int)D;
+  a.V = (int)V;
+  a.n_tt = (int)p.n_tt;
+  a.n_vt = (int)p.n_vt;
+  a.splits = (int)p.splits;
+  a.T_pad = (int)p.T_pad;
+  a.part_m = (float *)(ws + p.off_pm);
+  a.part_s = (float *)(ws + p.off_ps);
+  a.zlab = (float *)(ws + p.off_zl);
+  fwd_lse_kernel<<<(unsigned)(p.n_tt * p.splits), kThreads, 0, s>>>(a);
+  FLCE_TRY(launched("fwd_lse"));
+
+  FwdCombineParams c;
+  c.part_m = a.part_m;
+  c.part_s = a.part_s;
+  c.zlab = a.zlab;
+  c.labels = labels;
+  c.ignore_index = ignore_index;
+  c.T = (int)T;
+  c.V = (int)V;
+  c.splits = (int)p.splits;
+  c.T_pad = (int)p.T_pad;
+  c.mode = mode;
+  c.out = out;
+  c.lse = lse;
+  c.blk_sum = (double *)(ws + p.off_bs);
+  c.blk_cnt = (int *)(ws + p.off_bc);
+  fwd_combine_kernel<<<(unsigned)p.n_cblk, 256, 0, s>>>(c);
+  FLCE_TRY(launched("fwd_combine"));
+  if (mean_out) {
+    fwd_mean_kernel<<<1, 256, 0, s>>>(c.blk_sum, c.blk_cnt, (int)p.n_cblk, mean_out);
+    FLCE_TRY(launched("fwd_mean"));
+  }
+  return FLCE_OK;
+}
+
+flce_status flce_backward(const void *hidden, const void *weight, const int64_t *labels,
+                          const float *lse, int64_t T, int64_t D, int64_t V,
+                          int64_t ignore_index, int64_t chunk_rows, int mode,
+                          const float *grad_out, const float *grad_mean, void *grad_hidden,
+                          float *grad_weight, int accumulate_grad_weight, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  g_last_error[0] = 0;
+  Plan p;
+  FLCE_TRY(make_plan(T, D, V, chunk_rows, p));
+  if (mode != FLCE_MODE_NLL && mode != FLCE_MODE_LOGPROB)
+    return fail(FLCE_ERR_ARG, "mode %d is neither NLL (0) nor LOGPROB (1)", mode);
+  if ((grad_out == nullptr) == (grad_mean == nullptr))
+    return fail(FLCE_ERR_ARG, "exactly one of grad_out and grad_mean must be given");
+  if (!grad_weight) return fail(FLCE_ERR_ARG, "grad_weight is NULL");
+  if (!aligned(grad_weight, 16)) return fail(FLCE_ERR_ARG, "grad_weight not 16-byte aligned");
+  if (T > 0) {
+    if (!hidden || !weight || !labels || !lse || !grad_hidden || !workspace)
+      return fail(FLCE_ERR_ARG, "a required pointer is NULL");
+    if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(labels, 8) ||
+        !aligned(lse, 4) || !aligned(grad_hidden, 16) || !aligned(workspace, 16) ||
+        (grad_out && !aligned(grad_out, 4)) || (grad_mean && !aligned(grad_mean, 4)))
+      return fail(FLCE_ERR_ARG, "misaligned pointer");
+    if (workspace_bytes < p.total)
+      return fail(FLCE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
+                  p.total);
+  }
+  FLCE_TRY(check_device());
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) return accumulate_grad_weight ? FLCE_OK : fill(grad_weight, V * D, 0.f, s);
+
+  char *ws = (char *)workspace;
+  float *cbuf = (float *)(ws + p.off_c);
+  float *l2buf = (float *)(ws + p.off_l2);
+  uint16_t *G = (uint16_t *)(ws + p.off_G);
+  float *dhacc = (float *)(ws + p.off_dh);
+
+  BwdPrepParams pr;
+  pr.labels = labels;
+  pr.lse = lse;
+  pr.grad_out = grad_out;
+  pr.grad_mean = grad_mean;
+  pr.ignore_index = ignore_index;
+  pr.T = (int)T;
+  pr.V = (int)V;
+  pr.T_pad = (int)p.Tb;
+  pr.mode = mode;
+  pr.c = cbuf;
+  pr.lse2 = l2buf;
+  bwd_prep_kernel<<<1, 1024, 0, s>>>(pr);
+  FLCE_TRY(launched("bwd_prep"));
+
+  const int tiles_h = (int)cdiv(D, kTile);
+  for (int64_t rb = 0; rb < p.n_rb; ++rb) {
+    const int64_t rb0 = rb * p.R;
+    const int64_t rcount = std::min<int64_t>(p.R, T - rb0);
+    if (rcount <= 0) break;
+    for (int64_t vc = 0; vc < p.n_vc; ++vc) {
+      const int64_t vc0 = vc * p.Vc;
+      const int64_t vcount = std::min<int64_t>(p.Vc, V - vc0);
+      if (vcount <= 0) break;
+
+      BwdGradParams g;
+      g.hidden = (const uint16_t *)hidden;
+      g.weight = (const uint16_t *)weight;
+      g.labels = labels;
+      g.c = cbuf;
+      g.lse2 = l2buf;
+      g.ignore_index = ignore_index;
+      g.T = (int)T;
+      g.D = (int)D;
+      g.V = (int)V;
+      g.rb0 = (int)rb0;
+      g.vc0 = (int)vc0;
+      g.tiles_m = (int)(p.Vc / kTile);
+      g.tiles_n = (int)(p.R / kTile);
+      g.G = G;
+      g.Gp = (int)p.Vc;
+      bwd_grad_kernel<<<(unsigned)(g.tiles_m * g.tiles_n), kThreads, 0, s>>>(g);
+      FLCE_TRY(launched("bwd_grad"));
+
+      BwdDhParams h;
+      h.G = G;
+      h.weight = (const uint16_t *)weight;
+      h.Gp = (int)p.Vc;
+      h.D = (int)D;
+      h.V = (int)V;
+      h.vc0 = (int)vc0;
+      h.vcount = (int)vcount;
+      h.Kc = (int)p.Vc;
+      h.R = (int)p.R;
+      h.tiles_m = (int)(p.R / kTile);
+      h.tiles_n = tiles_h;
+      h.splits = (int)p.dh_splits;
+      h.acc = dhacc;
+      h.accumulate = vc > 0;
+      bwd_dh_kernel<<<(unsigned)(h.tiles_m * h.tiles_n * h.splits), kThreads, 0, s>>>(h);
+      FLCE_TRY(launched("bwd_dh"));
+
+      BwdDwParams w;
+      w.G = G;
+      w.hidden = (const uint16_t *)hidden;
+      w.Gp = (int)p.Vc;
+      w.D = (int)D;
+      w.V = (int)V;
+      w.rb0 = (int)rb0;
+      w.rcount = (int)rcount;
+      w.vc0 = (int)vc0;
+      w.tiles_m = (int)(p.Vc / kTile);
+      w.tiles_n = tiles_h;
+      w.dW = grad_weight;
+      w.accumulate = (accumulate_grad_weight || rb > 0) ? 1 : 0;
+      bwd_dw_kernel<<<(unsigned)(w.tiles_m * w.tiles_n), kThreads, 0, s>>>(w);
+      FLCE_TRY(launched("bwd_dw"));
+    }
+    BwdDhOutParams o;
+    o.acc = dhacc;
+    o.dH = (uint16_t *)grad_hidden;
+    o.D = (int)D;
+    o.R = (int)p.R;
+    o.splits = (int)p.dh_splits;
+    o.rb0 = (int)rb0;
+    o.rcount = (int)rcount;
+    const int64_t work = rcount * (D / 8);
+    bwd_dh_out_kernel<<<(unsigned)std::min<int64_t>(cdiv(work, 256), 8192), 256, 0, s>>>(o);
+    FLCE_TRY(launched("bwd_dh_out"));
+  }
+  return FLCE_OK;
+}
+
+}  // extern "C"

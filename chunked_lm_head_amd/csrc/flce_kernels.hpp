@@ -1,0 +1,516 @@
+// flce_kernels.hpp - HIP kernels of the chunked LM-head + cross-entropy path.
+//
+// Forward (Unsloth GRPO long-context page, section "Chunking der abgeflachten
+// Sequenzlaenge": chunked logits, fp32, selective log-softmax; TRL v1.13
+// article, section on the four hurdles: chunked NLL):
+//   fwd_lse     one launch over (256-token tile, vocabulary split) pairs.  Each
+//               workgroup walks the 256-row vocabulary tiles of its split,
+//               computing the logit tile z^T = W_tile H_tile^T on MFMA and
+//               folding it at once into a running (max, sum exp) per token, in
+//               base 2; it also picks out the label's logit.  Logits never
+//               leave registers.  Output: per-(split, token) partials.
+//   fwd_combine merges the splits -> lse, per-token NLL / log-prob.
+//   fwd_mean    fixed-order sum over tokens -> mean over non-ignored tokens.
+// Backward (same page, section "Auslagern von Aktivierungen fuer Log-Softmax":
+// recompute, then back-propagate the per-token grad_output):
+//   bwd_prep    per-token scale c_t and lse_t * log2(e).
+//   bwd_grad    recomputes one logit tile and writes
+//               G = c_t (softmax - onehot) as bf16 into a bounded block of the
+//               workspace ([rows of a row block] x [vocabulary chunk]).
+//   bwd_dh      fp32 partial sums of G W for the row block (split over K).
+//   bwd_dw      dW (+)= G^T H for the vocabulary chunk.
+//   bwd_dh_out  sums the K splits and rounds grad_hidden to bf16.
+#pragma once
+
+#include "flce_tile.hpp"
+
+namespace flce {
+
+constexpr float kInf = __builtin_inff();
+
+// ---------------------------------------------------------------------------
+// Forward: fused logit GEMM + online log-sum-exp + label gather.
+// ---------------------------------------------------------------------------
+struct FwdLseParams {
+  const uint16_t *hidden;   // [T, D] bf16
+  const uint16_t *weight;   // [V, D] bf16
+  const int64_t *labels;    // [T]
+  int64_t ignore_index;
+  int T, D, V;
+  int n_tt, n_vt, splits, T_pad;
+  float *part_m;            // [splits, T_pad] running max of z*log2(e)
+  float *part_s;            // [splits, T_pad] sum of 2^(z*log2(e) - max)
+  float *zlab;              // [T_pad] logit of the label
+};
+
+constexpr int kLdsFwd = kPipeBytes + 2048;
+
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(1, 1))) fwd_lse_kernel(FwdLseParams p) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[kLdsFwd];
+  lds_t *smem = (lds_t *)smem_raw;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  int tt, sp;
+  grouped_tile(xcd_contiguous(blockIdx.x, gridDim.x), p.n_tt, p.splits, 8, tt, sp);
+  const int vt0 = (int)((int64_t)sp * p.n_vt / p.splits);
+  const int vt1 = (int)((int64_t)(sp + 1) * p.n_vt / p.splits);
+  const int t0 = tt * kTile;
+
+  OperandK B;
+  B.init(p.hidden + (size_t)t0 * p.D, p.D, min(kTile, p.T - t0), p.D);
+  const int nk = (p.D + kBK - 1) / kBK;
+
+  int lab[4];
+  float mrun[4], srun[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int t = t0 + wn * 128 + nb * 32 + (lane & 31);
+    int y = -1;
+    if (t < p.T) {
+      const int64_t yy = p.labels[t];
+      if (yy != p.ignore_index && yy >= 0 && yy < p.V) y = (int)yy;
+    }
+    lab[nb] = y;
+    mrun[nb] = -kInf;
+    srun[nb] = 0.f;
+  }
+
+  Acc acc;
+  for (int vt = vt0; vt < vt1; ++vt) {
+    const int v0 = vt * kTile;
+    OperandK A;
+    A.init(p.weight + (size_t)v0 * p.D, p.D, min(kTile, p.V - v0), p.D);
+    acc.zero();
+    tile_mainloop(A, B, nk, smem, acc, tid);
+
+    const int vw = v0 + wm * 128;  // first vocabulary row of this wave's half
+    if (v0 + kTile > p.V) {        // ragged last tile: rows >= V do not exist
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (vw + acc_row(mb, r, lane) >= p.V)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) acc.v[mb][nb][r] = -kInf;
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      // label logit: exactly one (tile, wave, lane, register) holds it
+      const int rel = lab[nb] - vw;
+      if ((unsigned)rel < 128u) {
+        const int mb_ = rel >> 5, i = rel & 31;
+        if (((i >> 2) & 1) == (lane >> 5)) {
+          const int r_ = (i & 3) | ((i >> 3) << 2);
+          float z = 0.f;
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (mb == mb_ && r == r_) z = acc.v[mb][nb][r];
+          p.zlab[t0 + wn * 128 + nb * 32 + (lane & 31)] = z;
+        }
+      }
+      float zmax = -kInf;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) zmax = fmaxf(zmax, acc.v[mb][nb][r]);
+      const float mold = mrun[nb];
+      const float mnew = fmaxf(mold, zmax * kLog2e);
+      if (mnew != -kInf) {
+        float s = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s += fast_exp2(__builtin_fmaf(acc.v[mb][nb][r], kLog2e, -mnew));
+        srun[nb] = (mold == -kInf ? 0.f : srun[nb] * fast_exp2(mold - mnew)) + s;
+        mrun[nb] = mnew;
+      }
+    }
+  }
+
+  // Merge the two lanes holding one token (l, l ^ 32), then the two waves (wm).
+  lds_f32x2 *xch = (lds_f32x2 *)(smem + kPipeBytes);  // [wn][nb][32]
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const float m2 = __shfl_xor(mrun[nb], 32);
+    const float s2 = __shfl_xor(srun[nb], 32);
+    const float M = fmaxf(mrun[nb], m2);
+    float S = 0.f;
+    if (M != -kInf) {
+      S = (mrun[nb] == -kInf ? 0.f : srun[nb] * fast_exp2(mrun[nb] - M)) +
+          (m2 == -kInf ? 0.f : s2 * fast_exp2(m2 - M));
+    }
+    mrun[nb] = M;
+    srun[nb] = S;
+    if (wm == 1 && lane < 32) xch[(wn * 4 + nb) * 32 + lane] = f32x2{M, S};
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 32) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const f32x2 o = xch[(wn * 4 + nb) * 32 + lane];
+      const float M = fmaxf(mrun[nb], o[0]);
+      float S = 0.f;
+      if (M != -kInf) {
+        S = (mrun[nb] == -kInf ? 0.f : srun[nb] * fast_exp2(mrun[nb] - M)) +
+            (o[0] == -kInf ? 0.f : o[1] * fast_exp2(o[0] - M));
+      }
+      const int t = t0 + wn * 128 + nb * 32 + lane;
+      p.part_m[(size_t)sp * p.T_pad + t] = M;
+      p.part_s[(size_t)sp * p.T_pad + t] = S;
+    }
+  }
+}
+
+struct FwdCombineParams {
+  const float *part_m, *part_s, *zlab;
+  const int64_t *labels;
+  int64_t ignore_index;
+  int T, V, splits, T_pad, mode;
+  float *out, *lse;
+  double *blk_sum;
+  int *blk_cnt;
+};
+
+__global__ void __launch_bounds__(256) fwd_combine_kernel(FwdCombineParams p) {
+  __shared__ double ssum[256];
+  __shared__ int scnt[256];
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  double contrib = 0.0;
+  int cnt = 0;
+  if (t < p.T) {
+    float M = -kInf;
+    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.part_m[(size_t)s * p.T_pad + t]);
+    float S = 0.f;
+    for (int s = 0; s < p.splits; ++s) {
+      const float m = p.part_m[(size_t)s * p.T_pad + t];
+      if (m != -kInf) S += p.part_s[(size_t)s * p.T_pad + t] * fast_exp2(m - M);
+    }
+    const float lse = (M + fast_log2(S)) * kLn2;
+    const int64_t y = p.labels[t];
+    float o;
+    if (y == p.ignore_index) {
+      o = 0.f;
+    } else if (y < 0 || y >= p.V) {
+      o = __builtin_nanf("");
+      contrib = (double)o;
+      cnt = 1;
+    } else {
+      const float nll = lse - p.zlab[t];
+      o = p.mode == 0 ? nll : -nll;
+      contrib = (double)o;
+      cnt = 1;
+    }
+    p.out[t] = o;
+    p.lse[t] = lse;
+  }
+  ssum[threadIdx.x] = contrib;
+  scnt[threadIdx.x] = cnt;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      ssum[threadIdx.x] += ssum[threadIdx.x + w];
+      scnt[threadIdx.x] += scnt[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    p.blk_sum[blockIdx.x] = ssum[0];
+    p.blk_cnt[blockIdx.x] = scnt[0];
+  }
+}
+
+__global__ void __launch_bounds__(256)
+    fwd_mean_kernel(const double *blk_sum, const int *blk_cnt, int nblk, float *mean_out) {
+  __shared__ double ssum[256];
+  __shared__ int scnt[256];
+  double s = 0.0;
+  int c = 0;
+  for (int i = threadIdx.x; i < nblk; i += 256) {
+    s += blk_sum[i];
+    c += blk_cnt[i];
+  }
+  ssum[threadIdx.x] = s;
+  scnt[threadIdx.x] = c;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      ssum[threadIdx.x] += ssum[threadIdx.x + w];
+      scnt[threadIdx.x] += scnt[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) mean_out[0] = scnt[0] ? (float)(ssum[0] / (double)scnt[0]) : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// Backward.
+// ---------------------------------------------------------------------------
+struct BwdPrepParams {
+  const int64_t *labels;
+  const float *lse;
+  const float *grad_out;   // [T] or null
+  const float *grad_mean;  // scalar or null
+  int64_t ignore_index;
+  int T, V, T_pad, mode;
+  float *c;     // [T_pad] per-token scale (0 where the row has no gradient)
+  float *lse2;  // [T_pad] lse * log2(e); +inf where c == 0 so softmax terms vanish
+};
+
+__global__ void __launch_bounds__(1024) bwd_prep_kernel(BwdPrepParams p) {
+  __shared__ int scnt[1024];
+  int cnt = 0;
+  for (int t = threadIdx.x; t < p.T; t += 1024) cnt += (p.labels[t] != p.ignore_index);
+  scnt[threadIdx.x] = cnt;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) scnt[threadIdx.x] += scnt[threadIdx.x + w];
+    __syncthreads();
+  }
+  const int n_valid = scnt[0];
+  const float sign = p.mode == 0 ? 1.f : -1.f;
+  float gm = 0.f;
+  if (!p.grad_out && n_valid > 0) gm = p.grad_mean[0] / (float)n_valid;
+  for (int t = threadIdx.x; t < p.T_pad; t += 1024) {
+    float c = 0.f, l2 = kInf;
+    if (t < p.T) {
+      const int64_t y = p.labels[t];
+      if (y != p.ignore_index && y >= 0 && y < p.V) {
+        c = sign * (p.grad_out ? p.grad_out[t] : gm);
+        if (c != 0.f) l2 = p.lse[t] * kLog2e;
+      }
+    }
+    if (c == 0.f) l2 = kInf;
+    p.c[t] = c;
+    p.lse2[t] = l2;
+  }
+}
+
+struct BwdGradParams {
+  const uint16_t *hidden, *weight;
+  const int64_t *labels;
+  const float *c, *lse2;
+  int64_t ignore_index;
+  int T, D, V;
+  int rb0, vc0;          // first token / vocabulary row of this block
+  int tiles_m, tiles_n;  // vocabulary tiles of the chunk, token tiles of the row block
+  uint16_t *G;           // [R, Gp] bf16, row = token - rb0, col = vocab - vc0
+  int Gp;
+};
+
+constexpr int kGPitch = kTile * 2 + 16;                 // bytes per LDS row of the G tile
+constexpr int kLdsGrad = (kTile * kGPitch > kPipeBytes) ? kTile * kGPitch : kPipeBytes;
+
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(1, 1))) bwd_grad_kernel(BwdGradParams p) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[kLdsGrad];
+  lds_t *smem = (lds_t *)smem_raw;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  grouped_tile(xcd_contiguous(blockIdx.x, gridDim.x), p.tiles_m, p.tiles_n, 8, tm, tn);
+  const int v0 = p.vc0 + tm * kTile;
+  const int t0 = p.rb0 + tn * kTile;
+
+  Acc acc;
+  acc.zero();
+  if (v0 < p.V && t0 < p.T) {
+    OperandK A, B;
+    A.init(p.weight + (size_t)v0 * p.D, p.D, min(kTile, p.V - v0), p.D);
+    B.init(p.hidden + (size_t)t0 * p.D, p.D, min(kTile, p.T - t0), p.D);
+    tile_mainloop(A, B, (p.D + kBK - 1) / kBK, smem, acc, tid);
+  }
+
+  const int vw = v0 + wm * 128;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int tl = wn * 128 + nb * 32 + (lane & 31);  // token within the tile
+    const int t = t0 + tl;                            // < rb0 + R <= T_pad
+    const float c = p.c[t];
+    const float l2 = p.lse2[t];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float g = c * fast_exp2(__builtin_fmaf(acc.v[mb][nb][r], kLog2e, -l2));
+        acc.v[mb][nb][r] = (vw + acc_row(mb, r, lane) < p.V) ? g : 0.f;
+      }
+    int y = -1;
+    if (c != 0.f) y = (int)p.labels[t];  // c != 0 implies 0 <= y < V
+    const int rel = y - vw;
+    if ((unsigned)rel < 128u) {
+      const int mb_ = rel >> 5, i = rel & 31;
+      if (((i >> 2) & 1) == (lane >> 5)) {
+        const int r_ = (i & 3) | ((i >> 3) << 2);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (mb == mb_ && r == r_) acc.v[mb][nb][r] -= c;
+      }
+    }
+    // 4 consecutive vocabulary rows per register group -> one 8-byte LDS write
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x2 w;
+        w[0] = pack_bf16(acc.v[mb][nb][4 * q + 0], acc.v[mb][nb][4 * q + 1]);
+        w[1] = pack_bf16(acc.v[mb][nb][4 * q + 2], acc.v[mb][nb][4 * q + 3]);
+        const int vl = wm * 128 + mb * 32 + q * 8 + ((lane >> 5) << 2);
+        *(lds_u32x2 *)(smem + tl * kGPitch + vl * 2) = w;
+      }
+  }
+  __syncthreads();
+  // LDS [token][vocab] -> G rows, 16 bytes per lane, 512 contiguous bytes per 32 lanes.
+  uint16_t *gbase = p.G + (size_t)(tn * kTile) * p.Gp + tm * kTile;
+#pragma unroll 4
+  for (int i = 0; i < 32; ++i) {
+    const int q = i * kThreads + tid;
+    const int row = q >> 5, col16 = q & 31;
+    const u32x4 v = *(const lds_u32x4 *)(smem + row * kGPitch + col16 * 16);
+    *(u32x4 *)(gbase + (size_t)row * p.Gp + col16 * 8) = v;
+  }
+}
+
+struct BwdDhParams {
+  const uint16_t *G;
+  const uint16_t *weight;
+  int Gp, D, V;
+  int vc0, vcount;       // vocabulary rows [vc0, vc0 + vcount) of this chunk exist
+  int Kc;                // K extent of the chunk (columns of G)
+  int R;                 // rows of the row block (multiple of 256)
+  int tiles_m, tiles_n, splits;
+  float *acc;            // [splits, R, D] fp32
+  int accumulate;
+};
+
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(1, 1))) bwd_dh_kernel(BwdDhParams p) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[kPipeBytes];
+  lds_t *smem = (lds_t *)smem_raw;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int L = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int per_split = p.tiles_m * p.tiles_n;
+  const int s = L / per_split;
+  int tm, tn;
+  grouped_tile(L - s * per_split, p.tiles_m, p.tiles_n, 8, tm, tn);
+
+  const int ktiles = (p.Kc + kBK - 1) / kBK;
+  const int kbeg = (int)((int64_t)s * ktiles / p.splits) * kBK;
+  const int kend = min(p.Kc, (int)((int64_t)(s + 1) * ktiles / p.splits) * kBK);
+  const int h0 = tn * kTile;
+
+  OperandK A;      // G rows of this tile, K = vocabulary (contiguous)
+  A.init(p.G + (size_t)(tm * kTile) * p.Gp + kbeg, p.Gp, kTile, kend - kbeg);
+  OperandMN B;     // W[vc0 + k][h0 + n]: K = vocabulary rows
+  B.init(p.weight + (size_t)(p.vc0 + kbeg) * p.D + h0, p.D, min(kTile, p.D - h0),
+         min(kend, p.vcount) - kbeg);
+  Acc acc;
+  acc.zero();
+  tile_mainloop(A, B, (kend - kbeg + kBK - 1) / kBK, smem, acc, tid);
+
+  float *dst = p.acc + (size_t)s * p.R * p.D;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int h = h0 + wn * 128 + nb * 32 + (lane & 31);
+    if (h >= p.D) continue;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = tm * kTile + wm * 128 + acc_row(mb, r, lane);
+        float *q = dst + (size_t)row * p.D + h;
+        *q = p.accumulate ? *q + acc.v[mb][nb][r] : acc.v[mb][nb][r];
+      }
+  }
+}
+
+struct BwdDwParams {
+  const uint16_t *G;
+  const uint16_t *hidden;
+  int Gp, D, V;
+  int rb0, rcount;       // tokens [rb0, rb0 + rcount) of this row block exist
+  int vc0;
+  int tiles_m, tiles_n;
+  float *dW;             // [V, D] fp32
+  int accumulate;
+};
+
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(1, 1))) bwd_dw_kernel(BwdDwParams p) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[kPipeBytes];
+  lds_t *smem = (lds_t *)smem_raw;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  grouped_tile(xcd_contiguous(blockIdx.x, gridDim.x), p.tiles_m, p.tiles_n, 8, tm, tn);
+  const int v0 = p.vc0 + tm * kTile;
+  if (v0 >= p.V) return;  // the whole tile lies past the vocabulary
+  const int h0 = tn * kTile;
+
+  OperandMN A;     // G^T: G[k = token][m = vocabulary]
+  A.init(p.G + tm * kTile, p.Gp, kTile, p.rcount);
+  OperandMN B;     // H[rb0 + k][h0 + n]
+  B.init(p.hidden + (size_t)p.rb0 * p.D + h0, p.D, min(kTile, p.D - h0), p.rcount);
+  Acc acc;
+  acc.zero();
+  tile_mainloop(A, B, (p.rcount + kBK - 1) / kBK, smem, acc, tid);
+
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int h = h0 + wn * 128 + nb * 32 + (lane & 31);
+    if (h >= p.D) continue;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = v0 + wm * 128 + acc_row(mb, r, lane);
+        if (v < p.V) {
+          float *q = p.dW + (size_t)v * p.D + h;
+          *q = p.accumulate ? *q + acc.v[mb][nb][r] : acc.v[mb][nb][r];
+        }
+      }
+  }
+}
+
+struct BwdDhOutParams {
+  const float *acc;   // [splits, R, D]
+  uint16_t *dH;       // [T, D] bf16
+  int D, R, splits, rb0, rcount;
+};
+
+__global__ void __launch_bounds__(256) bwd_dh_out_kernel(BwdDhOutParams p) {
+  const int per_row = p.D >> 3;
+  const int64_t n = (int64_t)p.rcount * per_row;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int row = (int)(i / per_row), c8 = (int)(i - (int64_t)row * per_row) * 8;
+    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < p.splits; ++s) {
+      const float *src = p.acc + ((size_t)s * p.R + row) * p.D + c8;
+      lo += *(const f32x4 *)src;
+      hi += *(const f32x4 *)(src + 4);
+    }
+    u32x4 o;
+    o[0] = pack_bf16(lo[0], lo[1]);
+    o[1] = pack_bf16(lo[2], lo[3]);
+    o[2] = pack_bf16(hi[0], hi[1]);
+    o[3] = pack_bf16(hi[2], hi[3]);
+    *(u32x4 *)(p.dH + (size_t)(p.rb0 + row) * p.D + c8) = o;
+  }
+}
+
+__global__ void __launch_bounds__(256) fill_f32_kernel(float *dst, int64_t n, float value) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    dst[i] = value;
+}
+
+}  // namespace flce

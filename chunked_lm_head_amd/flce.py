@@ -1,0 +1,202 @@
+"""Python binding of libflce.so (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels behind the C ABI of
+``include/flce.h``; this module checks tensor dtypes, devices and layouts,
+allocates outputs and the workspace with PyTorch, and passes raw pointers and
+the current HIP stream.  There is no fallback: if the library is missing the
+import fails.
+
+The autograd wrapper follows the pattern of Unsloth's offloaded log-softmax
+(GRPO long-context page, section "Auslagern von Aktivierungen fuer
+Log-Softmax"): the forward keeps no logits, only what the backward needs to
+recompute them (hidden states, lm_head, labels and the per-token lse).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libflce.so")
+
+MODE_NLL = 0
+MODE_LOGPROB = 1
+_MODES = {"nll": MODE_NLL, "logprob": MODE_LOGPROB}
+STATUS = {0: "FLCE_OK", 1: "FLCE_ERR_ARG", 2: "FLCE_ERR_SHAPE", 3: "FLCE_ERR_WORKSPACE",
+          4: "FLCE_ERR_UNSUPPORTED", 5: "FLCE_ERR_HIP"}
+EXPORTS = ("flce_workspace_bytes", "flce_forward", "flce_backward", "flce_describe_plan",
+           "flce_status_string", "flce_last_error")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, f32p, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t
+    lib.flce_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.flce_workspace_bytes.restype = sz
+    lib.flce_forward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int,
+                                 f32p, f32p, f32p, vp, sz, vp]
+    lib.flce_forward.restype = ctypes.c_int
+    lib.flce_backward.argtypes = [vp, vp, vp, f32p, i64, i64, i64, i64, i64, ctypes.c_int,
+                                  f32p, f32p, vp, f32p, ctypes.c_int, vp, sz, vp]
+    lib.flce_backward.restype = ctypes.c_int
+    lib.flce_describe_plan.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
+    lib.flce_describe_plan.restype = ctypes.c_int
+    lib.flce_status_string.argtypes = [ctypes.c_int]
+    lib.flce_status_string.restype = ctypes.c_char_p
+    lib.flce_last_error.argtypes = []
+    lib.flce_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+class FlceError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        msg = lib.flce_last_error().decode() or lib.flce_status_string(status).decode()
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise FlceError(status)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_bytes(T: int, D: int, V: int, chunk_rows: int = 256) -> int:
+    n = lib.flce_workspace_bytes(T, D, V, chunk_rows)
+    if n == 0:
+        raise ValueError(f"invalid shape T={T} D={D} V={V} chunk_rows={chunk_rows}")
+    return n
+
+
+PLAN_KEYS = ("token_tiles", "vocab_tiles", "fwd_splits", "row_block", "row_blocks",
+             "vocab_chunk", "vocab_chunks", "dh_splits", "fwd_workspace", "bwd_workspace",
+             "grad_tile_bytes", "chunk_logit_bytes")
+
+
+def describe_plan(T: int, D: int, V: int, chunk_rows: int = 256) -> dict:
+    info = (ctypes.c_int64 * 12)()
+    _check(lib.flce_describe_plan(T, D, V, chunk_rows, info))
+    return dict(zip(PLAN_KEYS, list(info)))
+
+
+def _validate(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor) -> None:
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("hidden and weight must be bfloat16")
+    if labels.dtype != torch.int64:
+        raise TypeError("labels must be int64")
+    if hidden.dim() != 2 or weight.dim() != 2 or labels.dim() != 1:
+        raise ValueError("hidden [T, D], weight [V, D], labels [T] expected")
+    if hidden.shape[1] != weight.shape[1] or labels.shape[0] != hidden.shape[0]:
+        raise ValueError("shape mismatch between hidden, weight and labels")
+    for t in (hidden, weight, labels):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous and on the GPU")
+        if t.device != hidden.device:
+            raise ValueError("tensors on different devices")
+
+
+def alloc_workspace(T: int, D: int, V: int, chunk_rows: int, device) -> torch.Tensor:
+    return torch.empty(workspace_bytes(T, D, V, chunk_rows), dtype=torch.uint8, device=device)
+
+
+def forward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor, *,
+            ignore_index: int = -100, chunk_rows: int = 256, mode: str = "nll",
+            workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, mean: Optional[torch.Tensor] = None):
+    """(out [T], lse [T], mean []) fp32: per-token NLL or log-prob, lse, mean over used tokens."""
+    _validate(hidden, weight, labels)
+    T, D = hidden.shape
+    V = weight.shape[0]
+    dev = hidden.device
+    out = torch.empty(T, dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty(T, dtype=torch.float32, device=dev) if lse is None else lse
+    mean = torch.empty((), dtype=torch.float32, device=dev) if mean is None else mean
+    if workspace is None:
+        workspace = alloc_workspace(T, D, V, chunk_rows, dev)
+    _check(lib.flce_forward(_ptr(hidden), _ptr(weight), _ptr(labels), T, D, V, ignore_index,
+                            chunk_rows, _MODES[mode], _ptr(out), _ptr(lse), _ptr(mean),
+                            _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out, lse, mean
+
+
+def backward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor,
+             lse: torch.Tensor, *, grad_out: Optional[torch.Tensor] = None,
+             grad_mean: Optional[torch.Tensor] = None, ignore_index: int = -100,
+             chunk_rows: int = 256, mode: str = "nll",
+             grad_hidden: Optional[torch.Tensor] = None,
+             grad_weight: Optional[torch.Tensor] = None, accumulate: bool = False,
+             workspace: Optional[torch.Tensor] = None):
+    """(dH [T, D] bf16, dW [V, D] fp32) of the loss given dL/d out (per token) or dL/d mean."""
+    _validate(hidden, weight, labels)
+    T, D = hidden.shape
+    V = weight.shape[0]
+    dev = hidden.device
+    if (grad_out is None) == (grad_mean is None):
+        raise ValueError("give exactly one of grad_out and grad_mean")
+    for t in (lse, grad_out, grad_mean):
+        if t is not None and (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("lse / grad_out / grad_mean must be contiguous fp32 on the GPU")
+    if grad_hidden is None:
+        grad_hidden = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    if grad_weight is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing grad_weight")
+        grad_weight = torch.empty((V, D), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(T, D, V, chunk_rows, dev)
+    _check(lib.flce_backward(_ptr(hidden), _ptr(weight), _ptr(labels), _ptr(lse), T, D, V,
+                             ignore_index, chunk_rows, _MODES[mode], _ptr(grad_out),
+                             _ptr(grad_mean), _ptr(grad_hidden), _ptr(grad_weight),
+                             1 if accumulate else 0, _ptr(workspace), workspace.numel(),
+                             _stream(dev)))
+    return grad_hidden, grad_weight
+
+
+class _ChunkedLinearCE(torch.autograd.Function):
+    """Mean NLL (``reduction="mean"``) or per-token NLL / log-prob (``"none"``)."""
+
+    @staticmethod
+    def forward(ctx, hidden, weight, labels, ignore_index, chunk_rows, mode, reduction):
+        out, lse, mean = forward(hidden, weight, labels, ignore_index=ignore_index,
+                                 chunk_rows=chunk_rows, mode=mode)
+        ctx.save_for_backward(hidden, weight, labels, lse)
+        ctx.cfg = (ignore_index, chunk_rows, mode, reduction)
+        return mean if reduction == "mean" else out
+
+    @staticmethod
+    def backward(ctx, grad):
+        hidden, weight, labels, lse = ctx.saved_tensors
+        ignore_index, chunk_rows, mode, reduction = ctx.cfg
+        g = grad.float().contiguous()
+        kw = dict(grad_mean=g.reshape(())) if reduction == "mean" else dict(grad_out=g)
+        dh, dw = backward(hidden, weight, labels, lse, ignore_index=ignore_index,
+                          chunk_rows=chunk_rows, mode=mode, **kw)
+        return dh, dw.to(weight.dtype), None, None, None, None, None
+
+
+def chunked_linear_cross_entropy(hidden, weight, labels, *, ignore_index=-100, chunk_rows=256,
+                                 reduction="mean"):
+    """Autograd-aware chunked NLL of ``hidden @ weight.T`` against ``labels``."""
+    return _ChunkedLinearCE.apply(hidden, weight, labels, ignore_index, chunk_rows, "nll",
+                                  reduction)
+
+
+def selective_log_softmax(hidden, weight, labels, *, ignore_index=-100, chunk_rows=256):
+    """Autograd-aware per-token log p(label) without materialising the logits."""
+    return _ChunkedLinearCE.apply(hidden, weight, labels, ignore_index, chunk_rows, "logprob",
+                                  "none")

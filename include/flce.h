@@ -1,0 +1,144 @@
+/*
+ * flce.h - chunked fused linear cross-entropy / selective log-softmax on
+ * AMD Instinct MI355X (gfx950).  C ABI; plain pointers and sizes only.
+ *
+ * What the library computes
+ * -------------------------
+ * Given flattened hidden states H [T x D] and an lm_head W [V x D] (both
+ * bfloat16, row-major), labels y [T] and an ignore index, the logits are
+ * z_t = W h_t (bf16 x bf16 products accumulated in fp32, never rounded back to
+ * bf16) and for every token
+ *     lse_t = log sum_v exp(z_tv),
+ *     NLL_t = lse_t - z_{t,y_t}            (mode FLCE_MODE_NLL),
+ *     log p_t = z_{t,y_t} - lse_t          (mode FLCE_MODE_LOGPROB).
+ * The full [T x V] logit matrix never exists in device memory.
+ *
+ * Sources on the pages:
+ *  - Unsloth, "Reinforcement Learning GRPO mit 7x laengerem Kontext", section
+ *    "Chunking der abgeflachten Sequenzlaenge": the flattened (batch x context)
+ *    rows are processed in chunks so that the logits are never materialised in
+ *    full (Equations 1-3 give their memory); the chunk logits are handled in
+ *    float32; the call returns the selective log-softmax at the completion ids.
+ *  - same page, section "Auslagern von Aktivierungen fuer Log-Softmax": the
+ *    forward runs without autograd state, the backward recomputes the chunked
+ *    logits and back-propagates a per-token grad_output.
+ *  - TRL v1.13 article (arex-research.com), section on the four hurdles:
+ *    loss_type "chunked_nll" computes the loss 256 rows at a time and sums;
+ *    section on the chunked loss returning to tensor cores: the GEMM operands
+ *    stay bf16 (no float32 copy of the lm_head), forward plus backward.
+ *
+ * Conventions common to every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is DEVICE memory owned by the caller; the library
+ *    never allocates, frees or synchronises.  Work is enqueued on `stream`
+ *    (a hipStream_t; NULL = the default stream); buffers must stay alive until
+ *    the stream has passed the call.  One workspace must not be used by two
+ *    calls that can run at the same time.
+ *  - Layouts: hidden [T x D] and weight [V x D] bf16 row-major, rows 16-byte
+ *    aligned (D a multiple of 8, base pointers 16-byte aligned); labels int64
+ *    [T]; per-token outputs fp32 [T].
+ *  - Arguments are checked on the host before anything is enqueued; a failed
+ *    check returns a status and enqueues nothing.  The library never aborts.
+ *    The last failure's text is available from flce_last_error() (per thread).
+ *  - A label outside [0, V) that is not ignore_index is a caller error: that
+ *    token's output is NaN (so is the mean) and its gradient row is zero.
+ *    Tokens whose label equals ignore_index output 0, get a zero gradient row
+ *    and are left out of the mean's denominator.
+ *  - Results are deterministic: repeated calls with the same inputs give the
+ *    same bits (no floating-point atomics).
+ */
+#ifndef FLCE_H
+#define FLCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum flce_status {
+  FLCE_OK = 0,
+  FLCE_ERR_ARG = 1,          /* NULL or misaligned pointer, unknown mode, both/neither grad */
+  FLCE_ERR_SHAPE = 2,        /* T < 0, D/V/chunk_rows < 1, or sizes too large for the ABI */
+  FLCE_ERR_WORKSPACE = 3,    /* workspace smaller than flce_workspace_bytes() */
+  FLCE_ERR_UNSUPPORTED = 4,  /* D not a multiple of 8, or the device is not gfx950 */
+  FLCE_ERR_HIP = 5           /* a HIP runtime call or kernel launch failed */
+} flce_status;
+
+enum { FLCE_MODE_NLL = 0, FLCE_MODE_LOGPROB = 1 };
+
+/*
+ * Bytes of device workspace that flce_forward and flce_backward need for this
+ * shape (one size serves both).  It is bounded by the logit memory of one
+ * chunk, chunk_rows x V x 4 bytes (the fp32 chunk logits of the pages'
+ * Equation 3), plus terms linear in T and in D, and does not grow with T x V:
+ * the backward stages the softmax gradient of a block of rows in bf16 within
+ * that bound.  The minimum is one 256 x 256 bf16 tile.  Returns 0 when the
+ * arguments are invalid (same rules as the entry points) or overflow.
+ */
+size_t flce_workspace_bytes(int64_t T, int64_t D, int64_t V, int64_t chunk_rows);
+
+/*
+ * Forward.  Writes, for t < T:
+ *   out[t]  = NLL_t or log p_t (mode), 0 where labels[t] == ignore_index;
+ *   lse[t]  = log-sum-exp of the logit row (written for ignored rows too;
+ *             the backward takes it back);
+ *   *mean_out (if mean_out != NULL; one fp32 in device memory)
+ *           = sum of out over non-ignored tokens / their number (0 if none).
+ * chunk_rows only bounds the workspace (see flce_workspace_bytes); the
+ * results do not depend on it beyond fp32 rounding order.  T == 0 is valid:
+ * nothing is written except *mean_out = 0.
+ */
+flce_status flce_forward(const void *hidden, const void *weight, const int64_t *labels,
+                         int64_t T, int64_t D, int64_t V, int64_t ignore_index,
+                         int64_t chunk_rows, int mode,
+                         float *out, float *lse, float *mean_out,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward.  Recomputes the logits chunk by chunk and writes
+ *   grad_hidden [T x D] bf16  = G W,
+ *   grad_weight [V x D] fp32  = G^T H      (added to the existing contents if
+ *                                           accumulate_grad_weight != 0),
+ * with G_tv = c_t (softmax(z_t)_v - [v == y_t]) and
+ *   c_t = s * grad_out[t]            if grad_out != NULL (dL/d out_t),
+ *   c_t = s * (*grad_mean) / N_valid if grad_out == NULL (dL/d mean; device scalar),
+ * s = +1 for FLCE_MODE_NLL and -1 for FLCE_MODE_LOGPROB, c_t = 0 for ignored
+ * (and out-of-range) labels, N_valid = number of tokens whose label is not
+ * ignore_index (c_t = 0 for all t if N_valid == 0).  Exactly one of grad_out
+ * and grad_mean must be non-NULL.  lse must be the forward's output for the
+ * same inputs.  T == 0 is valid: grad_weight is zeroed unless accumulating.
+ */
+flce_status flce_backward(const void *hidden, const void *weight, const int64_t *labels,
+                          const float *lse, int64_t T, int64_t D, int64_t V,
+                          int64_t ignore_index, int64_t chunk_rows, int mode,
+                          const float *grad_out, const float *grad_mean,
+                          void *grad_hidden, float *grad_weight, int accumulate_grad_weight,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The schedule the library would use for this shape, for inspection and
+ * tests (host only, no device call).  Fills info[0..11] with:
+ *   0 token tiles of 256 rows     1 vocabulary tiles of 256 rows
+ *   2 forward vocabulary splits   3 backward row block (tokens)
+ *   4 number of row blocks        5 backward vocabulary chunk
+ *   6 number of vocabulary chunks 7 split-K factor of the grad_hidden GEMM
+ *   8 forward workspace bytes     9 backward workspace bytes
+ *  10 bf16 gradient-tile bytes   11 chunk-logit bound chunk_rows*V*4
+ * Returns FLCE_OK or the status flce_workspace_bytes would fail with.
+ */
+flce_status flce_describe_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows,
+                               int64_t *info);
+
+/* Static text for a status code. */
+const char *flce_status_string(int status);
+
+/* Text of the last failure on the calling thread ("" if none). */
+const char *flce_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H */

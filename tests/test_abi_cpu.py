@@ -1,0 +1,108 @@
+"""The C-ABI library on the host: it loads, exports what include/flce.h declares, and
+rejects bad arguments before touching a GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def flce():
+    from chunked_lm_head_amd import flce as m
+    return m
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "flce.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(flce_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(flce):
+    names = _declared()
+    assert set(names) == set(flce.EXPORTS), names
+    for n in names:
+        assert hasattr(flce.lib, n), n
+
+
+def test_status_strings(flce):
+    for s in range(6):
+        assert flce.lib.flce_status_string(s)
+    assert b"unknown" in flce.lib.flce_status_string(99)
+
+
+def test_shape_checks(flce):
+    ws = flce.lib.flce_workspace_bytes
+    assert ws(-1, 64, 100, 16) == 0
+    assert ws(10, 0, 100, 16) == 0
+    assert ws(10, 64, 0, 16) == 0
+    assert ws(10, 64, 100, 0) == 0
+    assert ws(10, 60, 100, 16) == 0        # D not a multiple of 8
+    assert ws(0, 64, 100, 16) > 0          # empty batch is valid
+    assert ws(67, 128, 1000, 16) > 0
+
+
+def _fwd(flce, **over):
+    args = dict(hidden=16, weight=16, labels=8, T=4, D=64, V=100, ign=-100, cr=16, mode=0,
+                out=4, lse=4, mean=0, ws=16, wsb=1 << 30, stream=0)
+    args.update(over)
+    return flce.lib.flce_forward(args["hidden"], args["weight"], args["labels"], args["T"],
+                                 args["D"], args["V"], args["ign"], args["cr"], args["mode"],
+                                 args["out"], args["lse"], args["mean"] or None, args["ws"],
+                                 args["wsb"], args["stream"] or None)
+
+
+def test_forward_rejects_before_launch(flce):
+    assert _fwd(flce, T=-3) == 2
+    assert _fwd(flce, D=12) == 4
+    assert _fwd(flce, mode=7) == 1
+    assert _fwd(flce, hidden=0) == 1
+    assert _fwd(flce, hidden=8) == 1                 # misaligned
+    assert _fwd(flce, wsb=16) == 3                   # workspace too small
+    assert b"workspace" in flce.lib.flce_last_error()
+
+
+def test_backward_rejects_before_launch(flce):
+    b = flce.lib.flce_backward
+    # neither grad given
+    assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, None, None, 16, 16, 0, 16, 1 << 30, None) == 1
+    # both given
+    assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, 4, 4, 16, 16, 0, 16, 1 << 30, None) == 1
+    # grad_weight missing
+    assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, 4, None, 16, None, 0, 16, 1 << 30, None) == 1
+    # tiny workspace
+    assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, 4, None, 16, 16, 0, 16, 8, None) == 3
+
+
+def test_workspace_bound_independent_of_tokens_times_vocab(flce):
+    """Workspace: at most one chunk of fp32 logits (chunk_rows*V*4) for the bf16 gradient
+    block, plus terms linear in T and in D; the long-context shape needs about what the
+    16k-token shape needs although T*V is 8x larger."""
+    D, V, cr = 4096, 151936, 256
+    a = flce.describe_plan(16384, D, V, cr)
+    b = flce.describe_plan(131072, D, V, cr)
+    assert a["grad_tile_bytes"] <= cr * V * 4 and b["grad_tile_bytes"] <= cr * V * 4
+    wa, wb = flce.workspace_bytes(16384, D, V, cr), flce.workspace_bytes(131072, D, V, cr)
+    assert wb - wa <= 64 * (131072 - 16384)          # O(T) growth only
+    assert wb < 0.02 * 131072 * V * 4                 # far below the full fp32 logits
+    for T, D, V, cr in [(67, 128, 1000, 16), (256, 2048, 248320, 256), (32768, 4096, 128000, 256),
+                        (8500, 64, 700, 256), (300, 256, 5000, 1)]:
+        p = flce.describe_plan(T, D, V, cr)
+        assert p["grad_tile_bytes"] <= max(cr * V * 4, 256 * 256 * 2)
+        assert p["row_block"] % 256 == 0 and p["vocab_chunk"] % 256 == 0
+        assert p["row_block"] * p["row_blocks"] >= T
+        assert p["vocab_chunk"] * p["vocab_chunks"] >= V
+        assert (p["vocab_chunks"] - 1) * p["vocab_chunk"] < V
+        assert (p["row_blocks"] - 1) * p["row_block"] < T
+        assert p["fwd_splits"] <= p["vocab_tiles"]
+
+
+def test_plan_at_the_workload_shapes(flce):
+    p = flce.describe_plan(16384, 4096, 151936, 256)
+    assert p["token_tiles"] == 64 and p["vocab_tiles"] == 594
+    assert p["token_tiles"] * p["fwd_splits"] >= 1024
+    p = flce.describe_plan(256, 2048, 248320, 256)
+    assert p["vocab_chunks"] == 1 and p["row_blocks"] == 1
