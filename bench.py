@@ -1,0 +1,206 @@
+"""Throughput of the chunked LM-head + cross-entropy forward + backward on one MI355X.
+
+One step = flce_forward + flce_backward (mean NLL, upstream grad 1) over the
+whole synthetic batch, inputs resident in HBM, workspace preallocated.  Work
+per step is 8*T*V*D FLOPs: the logit GEMM (2TVD), its recompute in the backward
+(2TVD), dH = G W (2TVD) and dW = G^T H (2TVD).
+
+Prints one JSON line.  ``roofline`` describes the fused forward kernel
+(logit GEMM + online log-sum-exp), the largest single launch of the step,
+timed with HIP events on the stream it runs on; ``cpu_baseline`` times the
+float64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "LM-head+CE fwd+bwd tokens/s & % bf16 MFMA peak (H=4096, V=151,936)"
+PEAK_BF16 = 2.5e15          # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12           # MI355X HBM3E, B/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_8b_sft")
+    ap.add_argument("--chunk-rows", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--cpu-sample-vocab", type=int, default=65536)
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per launch from rocprofv3 counters (optional)")
+    return ap.parse_args()
+
+
+def cpu_baseline(x, n_tokens: int, n_vocab: int) -> dict:
+    """The oracle, untouched, on a bounded sample: the first n_tokens tokens against the
+    first n_vocab vocabulary rows (labels folded into that range).  Its work is linear in
+    the vocabulary, so the rate is scaled by n_vocab / V to full-vocabulary tokens/s."""
+    import numpy as np
+
+    from oracle import flce_oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    V = x.weight.shape[0]
+    n_vocab = min(n_vocab, V)
+    h = x.hidden[:n_tokens]
+    wt = x.weight[:n_vocab]
+    y = x.labels[:n_tokens].copy()
+    used = y != -100
+    y[used] %= n_vocab
+    t0 = time.perf_counter()
+    f = flce_oracle.forward(h, wt, y)
+    flce_oracle.backward(h, wt, y, lse=f.lse, grad_mean=1.0)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_tokens / dt * n_vocab / V, 3), "unit": "tokens/s",
+            "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n_tokens} tokens x first {n_vocab} of {V} vocabulary rows "
+                      f"(labels folded into the slice), float64 numpy forward + backward in "
+                      f"{dt:.1f} s; rate scaled by {n_vocab}/{V}"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the design notes describe how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from chunked_lm_head_amd import flce, synth
+
+    w = synth.WORKLOADS[args.workload]
+    chunk_rows = args.chunk_rows or w.chunk_rows
+    t_gen = time.perf_counter()
+    x = synth.make_inputs(w)
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    h = torch.from_numpy(x.hidden.view(np.int16)).view(torch.bfloat16).to(dev)
+    W = torch.from_numpy(x.weight.view(np.int16)).view(torch.bfloat16).to(dev)
+    y = torch.from_numpy(x.labels).to(dev)
+    T, D, V = w.T, w.H, w.V
+    ws = flce.alloc_workspace(T, D, V, chunk_rows, dev)
+    out = torch.empty(T, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    mean = torch.empty((), dtype=torch.float32, device=dev)
+    dh = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((V, D), dtype=torch.float32, device=dev)
+    gmean = torch.ones((), dtype=torch.float32, device=dev)
+    gout = None
+    if w.reduction == "none":
+        gout = torch.from_numpy(x.grad_out).to(dev)
+    gkw = dict(grad_out=gout) if gout is not None else dict(grad_mean=gmean)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        flce.forward(h, W, y, chunk_rows=chunk_rows, mode=w.mode, workspace=ws, out=out,
+                     lse=lse, mean=mean)
+        if ev is not None:
+            ev[1].record()
+        flce.backward(h, W, y, lse, chunk_rows=chunk_rows, mode=w.mode, grad_hidden=dh,
+                      grad_weight=dw, workspace=ws, **gkw)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms = total_ms / args.steps
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    bwd_avg = sum(bwd_ms) / len(bwd_ms)
+    tokens_per_s = T / (ms / 1e3)
+    step_flops = 8.0 * T * V * D
+    fwd_flops = 2.0 * T * V * D
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            rec = tj.get(args.workload, {}).get("fwd_lse_kernel")
+            if rec and rec.get("source_sha") == _kernel_sha():
+                traffic = rec["hbm_bytes_per_launch"]
+        except Exception:
+            traffic = None
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "hidden": D, "vocab": V,
+                   "chunk_rows": chunk_rows, "mode": w.mode, "reduction": w.reduction,
+                   "ignored_tokens": w.ignore_count},
+        "mfma_frac_of_step": round(step_flops / (ms / 1e3) / PEAK_BF16, 4),
+        "fwd_ms": round(fwd_avg, 4),
+        "bwd_ms": round(bwd_avg, 4),
+        "workspace_bytes": int(ws.numel()),
+        "roofline": {
+            "kernel": "fwd_lse_kernel",
+            "bound": "mfma",
+            "achieved": round(fwd_flops / (fwd_avg / 1e3) / 1e12, 2),
+            "peak": PEAK_BF16 / 1e12,
+            "unit": "TFLOP/s",
+            "frac": round(fwd_flops / (fwd_avg / 1e3) / PEAK_BF16, 4),
+            "traffic": traffic,
+            "algorithmic_flops_per_launch": fwd_flops,
+            "note": "event pair brackets flce_forward: the fused kernel plus two O(T) kernels",
+        },
+    }
+    print(f"[bench] {args.workload}: inputs drawn in {t_gen:.1f} s; step {ms:.3f} ms "
+          f"(fwd {fwd_avg:.3f}, bwd {bwd_avg:.3f})", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(x, min(args.cpu_sample_tokens, T),
+                                           args.cpu_sample_vocab)
+    print(json.dumps(line), flush=True)
+
+
+def _kernel_sha() -> str:
+    import hashlib
+
+    hsh = hashlib.sha256()
+    for f in ("flce_tile.hpp", "flce_kernels.hpp", "flce_api.hip"):
+        with open(os.path.join(ROOT, "chunked_lm_head_amd", "csrc", f), "rb") as fh:
+            hsh.update(fh.read())
+    return hsh.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()
