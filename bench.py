@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
     ap.add_argument("--cpu-sample-vocab", type=int, default=65536)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (reference for HBM counters)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch from rocprofv3 counters (optional)")
     return ap.parse_args()
@@ -83,6 +85,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = 64 << 20  # fp32 elements: 256 MiB read + 256 MiB written per copy
+        a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "copies": 3}))
+        return
 
     from chunked_lm_head_amd import flce, synth
 

@@ -104,9 +104,13 @@ flce_status make_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows, Plan 
   }
   vc_max = std::min(vc_max, vc_lim);
   vc_max = std::min(vc_max, std::max<int64_t>(kTile, (kI32Bytes / (2 * R)) / kTile * kTile));
-  int64_t n_vc = cdiv(p.n_vt * kTile, vc_max);
-  const int64_t tiles_per_chunk = cdiv(p.n_vt, n_vc);
-  n_vc = cdiv(p.n_vt, tiles_per_chunk);
+  // Chunks of a multiple of 16 vocabulary tiles keep the dW grid (chunk tiles x
+  // 16 hidden tiles at D = 4096) a multiple of the 256 CUs.
+  int64_t tiles_per_chunk = vc_max / kTile;
+  if (tiles_per_chunk >= 16 && (tiles_per_chunk / 16 * 16) * 20 >= tiles_per_chunk * 17)
+    tiles_per_chunk = tiles_per_chunk / 16 * 16;
+  tiles_per_chunk = std::min(tiles_per_chunk, p.n_vt);
+  const int64_t n_vc = cdiv(p.n_vt, tiles_per_chunk);
   p.R = R;
   p.n_rb = cdiv(p.n_tt * kTile, R);
   p.Tb = p.n_rb * R;

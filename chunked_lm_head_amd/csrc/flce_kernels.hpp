@@ -1,7 +1,7 @@
 // flce_kernels.hpp - HIP kernels of the chunked LM-head + cross-entropy path.
 //
 // Forward (Unsloth GRPO long-context page, section "Chunking der abgeflachten
-// Sequenzlaenge": chunked logits, fp32, selective log-softmax; TRL v1.13
+// Sequenzlaenge": chunked logits kept in fp32, selective log-softmax; TRL v1.13
 // article, section on the four hurdles: chunked NLL):
 //   fwd_lse     one launch over (256-token tile, vocabulary split) pairs.  Each
 //               workgroup walks the 256-row vocabulary tiles of its split,
@@ -20,6 +20,10 @@
 //   bwd_dh      fp32 partial sums of G W for the row block (split over K).
 //   bwd_dw      dW (+)= G^T H for the vocabulary chunk.
 //   bwd_dh_out  sums the K splits and rounds grad_hidden to bf16.
+//
+// Accumulators are read in the epilogues through acc_read(), one register at a
+// time where it is consumed, so that they stay in AGPRs and the epilogue needs
+// few VGPRs.
 #pragma once
 
 #include "flce_tile.hpp"
@@ -27,6 +31,30 @@
 namespace flce {
 
 constexpr float kInf = __builtin_inff();
+
+// One accumulator value out of its AGPR, at the point of use.
+__device__ __forceinline__ float acc_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
+__device__ __forceinline__ void store_f32(__amdgpu_buffer_rsrc_t rs, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), rs, off, 0, 0);
+}
+__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+}
+
+// Per lane and token column: which accumulator register of the wave's 128
+// rows holds vocabulary row `rel` (-1 if none): row = 32 mb + 8 (r / 4) +
+// 4 (lane / 32) + r % 4.
+__device__ __forceinline__ int label_reg(int rel, int lane) {
+  if ((unsigned)rel >= 128u) return -1;
+  const int i = rel & 31;
+  if (((i >> 2) & 1) != (lane >> 5)) return -1;
+  return (rel >> 5) * 16 + ((i & 3) | ((i >> 3) << 2));
+}
 
 // ---------------------------------------------------------------------------
 // Forward: fused logit GEMM + online log-sum-exp + label gather.
@@ -60,11 +88,11 @@ __global__ void __launch_bounds__(kThreads)
   const int t0 = tt * kTile;
 
   OperandK B;
-  B.init(p.hidden + (size_t)t0 * p.D, p.D, min(kTile, p.T - t0), p.D);
+  B.init(p.hidden + (size_t)t0 * p.D, p.D, min(kTile, p.T - t0), p.D, wave, lane);
   const int nk = (p.D + kBK - 1) / kBK;
 
   int lab[4];
-  float mrun[4], srun[4];
+  float mrun[4], srun[4], zl[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int t = t0 + wn * 128 + nb * 32 + (lane & 31);
@@ -76,61 +104,84 @@ __global__ void __launch_bounds__(kThreads)
     lab[nb] = y;
     mrun[nb] = -kInf;
     srun[nb] = 0.f;
+    zl[nb] = 0.f;
   }
+  unsigned have = 0;  // bit nb: this lane captured the label logit of token column nb
 
+  // The next vocabulary tile's first stages are issued before the current
+  // tile's epilogue, which touches neither LDS nor memory.
+  OperandK A;
+  A.init(p.weight + (size_t)vt0 * kTile * p.D, p.D, min(kTile, p.V - vt0 * kTile), p.D, wave,
+         lane);
+  wait_vmcnt<0>();
+  __syncthreads();
+  pipe_prologue(A, B, nk, smem, wave);
   Acc acc;
   for (int vt = vt0; vt < vt1; ++vt) {
     const int v0 = vt * kTile;
-    OperandK A;
-    A.init(p.weight + (size_t)v0 * p.D, p.D, min(kTile, p.V - v0), p.D);
     acc.zero();
-    tile_mainloop(A, B, nk, smem, acc, tid);
-
-    const int vw = v0 + wm * 128;  // first vocabulary row of this wave's half
-    if (v0 + kTile > p.V) {        // ragged last tile: rows >= V do not exist
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (vw + acc_row(mb, r, lane) >= p.V)
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) acc.v[mb][nb][r] = -kInf;
+    pipe_run(A, B, nk, smem, acc, wave, lane);
+    if (vt + 1 < vt1) {
+      A.init(p.weight + (size_t)(v0 + kTile) * p.D, p.D, min(kTile, p.V - v0 - kTile), p.D,
+             wave, lane);
+      pipe_prologue(A, B, nk, smem, wave);
     }
+
+    const int vw = v0 + wm * 128;           // first vocabulary row of this wave's half
+    const int vlim = p.V - vw;               // wave-relative rows >= vlim do not exist
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       // label logit: exactly one (tile, wave, lane, register) holds it
-      const int rel = lab[nb] - vw;
-      if ((unsigned)rel < 128u) {
-        const int mb_ = rel >> 5, i = rel & 31;
-        if (((i >> 2) & 1) == (lane >> 5)) {
-          const int r_ = (i & 3) | ((i >> 3) << 2);
-          float z = 0.f;
+      const int lr = label_reg(lab[nb] - vw, lane);
+      if (__builtin_amdgcn_ballot_w64(lr >= 0)) {
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (mb == mb_ && r == r_) z = acc.v[mb][nb][r];
-          p.zlab[t0 + wn * 128 + nb * 32 + (lane & 31)] = z;
-        }
+        for (int q = 0; q < 64; ++q)
+          if (lr == q) zl[nb] = acc_read(acc.v[q >> 4][nb][q & 15]);
+        if (lr >= 0) have |= 1u << nb;
       }
       float zmax = -kInf;
+      if (vlim >= 128) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) zmax = fmaxf(zmax, acc.v[mb][nb][r]);
+          for (int r = 0; r < 16; ++r) zmax = fmaxf(zmax, acc_read(acc.v[mb][nb][r]));
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float z = acc_read(acc.v[mb][nb][r]);
+            zmax = fmaxf(zmax, acc_row(mb, r, lane) < vlim ? z : -kInf);
+          }
+      }
       const float mold = mrun[nb];
       const float mnew = fmaxf(mold, zmax * kLog2e);
       if (mnew != -kInf) {
         float s = 0.f;
+        if (vlim >= 128) {
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+          for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s += fast_exp2(__builtin_fmaf(acc.v[mb][nb][r], kLog2e, -mnew));
+            for (int r = 0; r < 16; ++r)
+              s += fast_exp2(__builtin_fmaf(acc_read(acc.v[mb][nb][r]), kLog2e, -mnew));
+        } else {
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float e =
+                  fast_exp2(__builtin_fmaf(acc_read(acc.v[mb][nb][r]), kLog2e, -mnew));
+              s += acc_row(mb, r, lane) < vlim ? e : 0.f;
+            }
+        }
         srun[nb] = (mold == -kInf ? 0.f : srun[nb] * fast_exp2(mold - mnew)) + s;
         mrun[nb] = mnew;
       }
     }
   }
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+    if (have & (1u << nb)) p.zlab[t0 + wn * 128 + nb * 32 + (lane & 31)] = zl[nb];
 
   // Merge the two lanes holding one token (l, l ^ 32), then the two waves (wm).
   lds_f32x2 *xch = (lds_f32x2 *)(smem + kPipeBytes);  // [wn][nb][32]
@@ -321,47 +372,43 @@ __global__ void __launch_bounds__(kThreads)
   acc.zero();
   if (v0 < p.V && t0 < p.T) {
     OperandK A, B;
-    A.init(p.weight + (size_t)v0 * p.D, p.D, min(kTile, p.V - v0), p.D);
-    B.init(p.hidden + (size_t)t0 * p.D, p.D, min(kTile, p.T - t0), p.D);
-    tile_mainloop(A, B, (p.D + kBK - 1) / kBK, smem, acc, tid);
+    A.init(p.weight + (size_t)v0 * p.D, p.D, min(kTile, p.V - v0), p.D, wave, lane);
+    B.init(p.hidden + (size_t)t0 * p.D, p.D, min(kTile, p.T - t0), p.D, wave, lane);
+    tile_mainloop(A, B, (p.D + kBK - 1) / kBK, smem, acc, wave, lane);
   }
 
   const int vw = v0 + wm * 128;
+  const int vlim = p.V - vw;  // wave-relative rows >= vlim do not exist
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int tl = wn * 128 + nb * 32 + (lane & 31);  // token within the tile
     const int t = t0 + tl;                            // < rb0 + R <= T_pad
     const float c = p.c[t];
     const float l2 = p.lse2[t];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float g = c * fast_exp2(__builtin_fmaf(acc.v[mb][nb][r], kLog2e, -l2));
-        acc.v[mb][nb][r] = (vw + acc_row(mb, r, lane) < p.V) ? g : 0.f;
-      }
     int y = -1;
     if (c != 0.f) y = (int)p.labels[t];  // c != 0 implies 0 <= y < V
-    const int rel = y - vw;
-    if ((unsigned)rel < 128u) {
-      const int mb_ = rel >> 5, i = rel & 31;
-      if (((i >> 2) & 1) == (lane >> 5)) {
-        const int r_ = (i & 3) | ((i >> 3) << 2);
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (mb == mb_ && r == r_) acc.v[mb][nb][r] -= c;
-      }
-    }
-    // 4 consecutive vocabulary rows per register group -> one 8-byte LDS write
+    const int lr = label_reg(y - vw, lane);
+    const bool any_label = __builtin_amdgcn_ballot_w64(lr >= 0) != 0;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        float g[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q + e;
+          const float z = acc_read(acc.v[mb][nb][r]);
+          const float v = c * fast_exp2(__builtin_fmaf(z, kLog2e, -l2));
+          g[e] = acc_row(mb, r, lane) < vlim ? v : 0.f;
+        }
+        if (any_label) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (lr == mb * 16 + 4 * q + e) g[e] -= c;
+        }
         u32x2 w;
-        w[0] = pack_bf16(acc.v[mb][nb][4 * q + 0], acc.v[mb][nb][4 * q + 1]);
-        w[1] = pack_bf16(acc.v[mb][nb][4 * q + 2], acc.v[mb][nb][4 * q + 3]);
+        w[0] = pack_bf16(g[0], g[1]);
+        w[1] = pack_bf16(g[2], g[3]);
         const int vl = wm * 128 + mb * 32 + q * 8 + ((lane >> 5) << 2);
         *(lds_u32x2 *)(smem + tl * kGPitch + vl * 2) = w;
       }
@@ -375,6 +422,49 @@ __global__ void __launch_bounds__(kThreads)
     const int row = q >> 5, col16 = q & 31;
     const u32x4 v = *(const lds_u32x4 *)(smem + row * kGPitch + col16 * 16);
     *(u32x4 *)(gbase + (size_t)row * p.Gp + col16 * 8) = v;
+  }
+}
+
+// Writes (or adds) a wave's 128 x 128 fp32 accumulator block to row-major
+// memory through a buffer descriptor; lanes whose column lies past `cols`
+// and rows past the descriptor's range are dropped by the hardware.  When
+// adding, the 16 old values of a 32 x 32 block are loaded together before any
+// is consumed, so their latencies overlap.
+__device__ __forceinline__ void store_acc_block(const Acc &acc, __amdgpu_buffer_rsrc_t rs,
+                                                int ld, int row0, int col0, int cols,
+                                                bool accumulate, int lane) {
+  if (accumulate) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int col = col0 + nb * 32 + (lane & 31);
+      const bool col_ok = col < cols;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        uint32_t off[16];
+        float old[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          off[r] = col_ok ? (uint32_t)((row0 + acc_row(mb, r, lane)) * ld + col) * 4u : kOOB;
+          old[r] = load_f32(rs, off[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) store_f32(rs, off[r], acc_read(acc.v[mb][nb][r]) + old[r]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int col = col0 + nb * 32 + (lane & 31);
+      const bool col_ok = col < cols;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t off =
+              col_ok ? (uint32_t)((row0 + acc_row(mb, r, lane)) * ld + col) * 4u : kOOB;
+          store_f32(rs, off, acc_read(acc.v[mb][nb][r]));
+        }
+    }
   }
 }
 
@@ -409,28 +499,18 @@ __global__ void __launch_bounds__(kThreads)
   const int h0 = tn * kTile;
 
   OperandK A;      // G rows of this tile, K = vocabulary (contiguous)
-  A.init(p.G + (size_t)(tm * kTile) * p.Gp + kbeg, p.Gp, kTile, kend - kbeg);
+  A.init(p.G + (size_t)(tm * kTile) * p.Gp + kbeg, p.Gp, kTile, kend - kbeg, wave, lane);
   OperandMN B;     // W[vc0 + k][h0 + n]: K = vocabulary rows
   B.init(p.weight + (size_t)(p.vc0 + kbeg) * p.D + h0, p.D, min(kTile, p.D - h0),
-         min(kend, p.vcount) - kbeg);
+         min(kend, p.vcount) - kbeg, wave, lane);
   Acc acc;
   acc.zero();
-  tile_mainloop(A, B, (kend - kbeg + kBK - 1) / kBK, smem, acc, tid);
+  tile_mainloop(A, B, (kend - kbeg + kBK - 1) / kBK, smem, acc, wave, lane);
 
-  float *dst = p.acc + (size_t)s * p.R * p.D;
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int h = h0 + wn * 128 + nb * 32 + (lane & 31);
-    if (h >= p.D) continue;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = tm * kTile + wm * 128 + acc_row(mb, r, lane);
-        float *q = dst + (size_t)row * p.D + h;
-        *q = p.accumulate ? *q + acc.v[mb][nb][r] : acc.v[mb][nb][r];
-      }
-  }
+  // rows [tm*256, tm*256 + 256) of split s, all inside the R x D slice
+  const float *tile = p.acc + ((size_t)s * p.R + (size_t)tm * kTile) * p.D;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, (uint32_t)kTile * (uint32_t)p.D * 4u);
+  store_acc_block(acc, rs, p.D, wm * 128, h0 + wn * 128, p.D, p.accumulate != 0, lane);
 }
 
 struct BwdDwParams {
@@ -458,28 +538,17 @@ __global__ void __launch_bounds__(kThreads)
   const int h0 = tn * kTile;
 
   OperandMN A;     // G^T: G[k = token][m = vocabulary]
-  A.init(p.G + tm * kTile, p.Gp, kTile, p.rcount);
+  A.init(p.G + tm * kTile, p.Gp, kTile, p.rcount, wave, lane);
   OperandMN B;     // H[rb0 + k][h0 + n]
-  B.init(p.hidden + (size_t)p.rb0 * p.D + h0, p.D, min(kTile, p.D - h0), p.rcount);
+  B.init(p.hidden + (size_t)p.rb0 * p.D + h0, p.D, min(kTile, p.D - h0), p.rcount, wave, lane);
   Acc acc;
   acc.zero();
-  tile_mainloop(A, B, (p.rcount + kBK - 1) / kBK, smem, acc, tid);
+  tile_mainloop(A, B, (p.rcount + kBK - 1) / kBK, smem, acc, wave, lane);
 
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int h = h0 + wn * 128 + nb * 32 + (lane & 31);
-    if (h >= p.D) continue;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int v = v0 + wm * 128 + acc_row(mb, r, lane);
-        if (v < p.V) {
-          float *q = p.dW + (size_t)v * p.D + h;
-          *q = p.accumulate ? *q + acc.v[mb][nb][r] : acc.v[mb][nb][r];
-        }
-      }
-  }
+  // rows [v0, min(V, v0 + 256)) of dW
+  const uint32_t rows = (uint32_t)min(kTile, p.V - v0);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.dW + (size_t)v0 * p.D, rows * (uint32_t)p.D * 4u);
+  store_acc_block(acc, rs, p.D, wm * 128, h0 + wn * 128, p.D, p.accumulate != 0, lane);
 }
 
 struct BwdDhOutParams {

@@ -2,25 +2,31 @@
 // chunked LM-head + cross-entropy path on gfx950 (CDNA4).
 //
 // One workgroup of 256 threads (4 wave64s in a 2 x 2 grid) computes a
-// 256 x 256 fp32 tile C[m][n] = sum_k A[m][k] B[n][k] with
+// 256 x 256 fp32 tile C[m][n] = sum_k A(m, k) B(n, k) with
 // v_mfma_f32_32x32x16_bf16; each wave owns 128 x 128 of it as 4 x 4 MFMA blocks
-// (256 fp32 accumulators per lane).  K advances 64 at a time through a
-// double-buffered LDS pipeline (2 stages x (A + B) x 32 KiB = 128 KiB of the
-// 160 KiB LDS).
+// (256 fp32 accumulators per lane, held in AGPRs).
 //
-// Operands are read with buffer loads whose descriptor covers exactly the
-// valid bytes, and masked lanes use an offset past the descriptor's range, so
-// ragged edges read zeros and no load can leave its tensor.  Two operand
-// kinds exist:
-//   * K-contiguous (row-major [mn][k], e.g. H and W in the logit GEMM): copied
-//     global -> LDS with the direct-to-LDS form of buffer_load_dwordx4, no
-//     registers involved;
-//   * MN-contiguous (row-major [k][mn], e.g. W in dH = G W and H in
-//     dW = G^T H): each thread loads an 8 x 8 block of bf16 into registers,
-//     transposes it with v_perm_b32 and writes 8 k-contiguous rows to LDS.
-// Both land in the same LDS layout: 256 rows of 64 bf16 (128 B), the 16-byte
-// chunk c of row r stored at chunk c ^ ((r >> 1) & 7), so that the MFMA
-// fragment reads (32 consecutive rows, one chunk) spread over all banks.
+// Pipeline: K advances 32 at a time through a 4-stage LDS ring (4 x 32 KiB);
+// stage k + 3 is in flight while stage k is multiplied.  Every operand moves
+// global -> LDS by the direct-to-LDS form of buffer_load_dwordx4 (no
+// registers, no VALU), from a buffer descriptor that covers exactly the valid
+// bytes; masked lanes use an offset past its end, so ragged edges read zeros
+// and no load can leave its tensor.  One barrier per K step, placed between
+// the two 16-wide halves of the step so that the fragment reads of the next
+// stage overlap the MFMAs of the current one.
+//
+// Two operand layouts in global memory, two layouts in LDS:
+//  * K-contiguous ([mn][k], e.g. H and W in the logit GEMM): LDS rows of 32 k
+//    (64 B); chunk c of row r sits at chunk c ^ ((r >> 2) & 3).  Fragments are
+//    ds_read_b128.
+//  * MN-contiguous ([k][mn], e.g. W in dH = G W, H and G in dW = G^T H): LDS
+//    rows of 256 mn (512 B) per k; 16-byte chunk c of row k sits at
+//    c ^ (4 * (k & 3)).  Fragments are two ds_read_b64_tr_b16, which transpose
+//    4 x 4 blocks of 16-bit values across lanes: within each group of 16
+//    lanes, lane i receives element i % 4 of the 8-byte chunks addressed by
+//    lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 of the group.
+// Both swizzles make the fragment reads of a wave conflict-free across the
+// LDS banks.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,22 +39,24 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) f32x2 lds_f32x2;
 
 constexpr int kTile = 256;                                   // macro tile (rows = cols)
-constexpr int kBK = 64;                                      // K per pipeline stage
+constexpr int kBK = 32;                                      // K per pipeline stage
+constexpr int kStages = 4;                                   // LDS ring depth
 constexpr int kThreads = 256;                                // 4 wave64s
-constexpr int kOperandStageBytes = kTile * kBK * 2;          // 32 KiB
+constexpr int kOperandStageBytes = kTile * kBK * 2;          // 16 KiB
 constexpr int kStageBytes = 2 * kOperandStageBytes;          // A + B
-constexpr int kPipeBytes = 2 * kStageBytes;                  // 128 KiB, double buffered
+constexpr int kPipeBytes = kStages * kStageBytes;            // 128 KiB
 constexpr uint32_t kOOB = 0x80000000u;                       // offset past every descriptor
 constexpr int kRsrcWord3 = 0x00020000;                       // gfx9 raw buffer, 32-bit data
 
@@ -68,6 +76,20 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   f32x2 f = {lo, hi};
   bf16x2 b = __builtin_convertvector(f, bf16x2);
   return __builtin_bit_cast(uint32_t, b);
+}
+
+// Bytes left past an advance, kept in a scalar register so that the buffer
+// descriptor stays scalar (a VALU saturating subtract would force a
+// readfirstlane loop around every load).
+__device__ __forceinline__ uint32_t remaining(uint32_t nbytes, uint32_t adv) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(adv < nbytes ? nbytes - adv : 0u));
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // Workgroup id -> logical tile id such that each XCD (ids are dealt to the 8
@@ -91,101 +113,109 @@ __device__ __forceinline__ void grouped_tile(int L, int tiles_m, int tiles_n, in
 }
 
 // ---------------------------------------------------------------------------
-// Operands.
+// Operands.  Each wave issues 4 DMA instructions per operand per stage.
 // ---------------------------------------------------------------------------
 
-// Row-major [mn][k]: element (r, k) at byte (r * ld + k) * 2 from the base.
+// Row-major [mn][k]: element (r, k) at byte (r * ld + k) * 2 from base.
 struct OperandK {
-  __amdgpu_buffer_rsrc_t rs;
-  int ld;    // elements between rows
-  int rows;  // valid rows of this tile (0..256)
-  int kext;  // valid K extent (multiple of 8)
-  struct Stage {};
+  const char *base;  // tile origin (row 0, k 0)
+  uint32_t nbytes;   // valid bytes from base
+  int kext;          // valid K extent (multiple of 8)
+  uint32_t voff[4];  // per lane: row/chunk offset within a stage, kOOB for rows past the tile
+  int kc[4];         // per lane: k offset of its chunk within a stage
 
-  __device__ __forceinline__ void init(const uint16_t *base, int ld_, int rows_, int kext_) {
-    ld = ld_;
-    rows = rows_ < 0 ? 0 : rows_;
+  __device__ __forceinline__ void init(const uint16_t *base_, int ld, int rows, int kext_,
+                                       int wave, int lane) {
+    base = (const char *)base_;
+    rows = rows < 0 ? 0 : rows;
     kext = kext_ < 0 ? 0 : kext_;
-    const uint32_t nbytes =
-        (rows > 0 && kext > 0) ? (uint32_t)(((rows - 1) * ld + kext) * 2) : 0u;
-    rs = make_rsrc(base, nbytes);
-  }
-
-  // Each wave copies 64 rows (8 instructions of 8 rows x 128 B) straight into LDS.
-  __device__ __forceinline__ void prefetch(lds_t *stage, int k0, int wave, int lane, Stage &) const {
+    nbytes = (rows > 0 && kext > 0) ? (uint32_t)((rows - 1) * ld + kext) * 2u : 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rbase = wave * 64 + i * 8;
-      const int r = rbase + (lane >> 3);
-      const int c = (lane & 7) ^ ((r >> 1) & 7);   // logical chunk stored at lane's slot
-      const int k = k0 + c * 8;
-      const bool ok = (r < rows) && (k < kext);
-      const uint32_t voff = ok ? (uint32_t)(r * ld + k) * 2u : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(stage + rbase * 128), 16, voff,
-                                               0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int r = wave * 64 + i * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((r >> 2) & 3);
+      kc[i] = c * 8;
+      voff[i] = r < rows ? (uint32_t)(r * ld + c * 8) * 2u : kOOB;
     }
   }
-  __device__ __forceinline__ void commit(lds_t *, int, Stage &) const {}
+
+  __device__ __forceinline__ void issue(lds_t *stage, int k0, int wave) const {
+    const uint32_t adv = (uint32_t)k0 * 2u;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + adv, remaining(nbytes, adv));
+    const bool full = k0 + kBK <= kext;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = (full || k0 + kc[i] < kext) ? voff[i] : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_void_t *)(stage + (wave * 64 + i * 16) * (kBK * 2)), 16, off, 0, 0, 0);
+    }
+  }
+
+  // Rows row0 .. row0+31, k = 16 ks + 8 (lane / 32) .. +7.
+  __device__ __forceinline__ static bf16x8 frag(const lds_t *stage, int row0, int ks, int lane) {
+    const int r = row0 + (lane & 31);
+    const int c = ks * 2 + (lane >> 5);
+    const int phys = c ^ ((r >> 2) & 3);
+    return *(const lds_bf16x8 *)(stage + r * (kBK * 2) + phys * 16);
+  }
 };
 
-// Row-major [k][mn]: element (c, k) at byte (k * ld + c) * 2 from the base.
+// Row-major [k][mn]: element (c, k) at byte (k * ld + c) * 2 from base.
 struct OperandMN {
-  __amdgpu_buffer_rsrc_t rs;
-  int ld;    // elements between k rows
-  int cols;  // valid mn columns of this tile (0..256, multiple of 8)
-  int kext;  // valid K extent
-  struct Stage {
-    u32x4 v[8];
-  };
+  const char *base;   // tile origin (k 0, column 0)
+  uint32_t nbytes;    // valid bytes from base
+  uint32_t row_bytes; // ld * 2
+  int kext;           // valid K extent
+  uint32_t voff[4];   // per lane: k-row/chunk offset within a stage, kOOB past the columns
+  int kr[4];          // per lane: k row of its chunk within a stage
 
-  __device__ __forceinline__ void init(const uint16_t *base, int ld_, int cols_, int kext_) {
-    ld = ld_;
-    cols = cols_ < 0 ? 0 : cols_;
+  __device__ __forceinline__ void init(const uint16_t *base_, int ld, int cols, int kext_,
+                                       int wave, int lane) {
+    base = (const char *)base_;
+    cols = cols < 0 ? 0 : cols;
     kext = kext_ < 0 ? 0 : kext_;
-    const uint32_t nbytes =
-        (cols > 0 && kext > 0) ? (uint32_t)(((kext - 1) * ld + cols) * 2) : 0u;
-    rs = make_rsrc(base, nbytes);
-  }
-
-  // Thread (kb = tid % 8, cb = tid / 8) loads k rows kb*8 .. kb*8+7 of columns cb*8 .. cb*8+7.
-  __device__ __forceinline__ void prefetch(lds_t *, int k0, int wave, int lane, Stage &st) const {
-    const int tid = wave * 64 + lane;
-    const int kb = tid & 7, c = (tid >> 3) * 8;
+    row_bytes = (uint32_t)ld * 2u;
+    nbytes = (cols > 0 && kext > 0) ? (uint32_t)((kext - 1) * ld + cols) * 2u : 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = k0 + kb * 8 + i;
-      const bool ok = (k < kext) && (c < cols);
-      const uint32_t voff = ok ? (uint32_t)(k * ld + c) * 2u : kOOB;
-      st.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+    for (int i = 0; i < 4; ++i) {
+      const int k = wave * 8 + i * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (k & 3));
+      kr[i] = k;
+      voff[i] = c * 8 < cols ? (uint32_t)(k * ld + c * 8) * 2u : kOOB;
     }
   }
 
-  // Transpose the 8 x 8 block and store column j as LDS row cb*8 + j (8 consecutive k).
-  __device__ __forceinline__ void commit(lds_t *stage, int tid, Stage &st) const {
-    const int kb = tid & 7, cb = tid >> 3;
+  __device__ __forceinline__ void issue(lds_t *stage, int k0, int wave) const {
+    const uint32_t adv = (uint32_t)k0 * row_bytes;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + adv, remaining(nbytes, adv));
+    const bool full = k0 + kBK <= kext;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      u32x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t a = st.v[2 * e][j >> 1], b = st.v[2 * e + 1][j >> 1];
-        o[e] = (j & 1) ? __builtin_amdgcn_perm(b, a, 0x07060302u)
-                       : __builtin_amdgcn_perm(b, a, 0x05040100u);
-      }
-      const int r = cb * 8 + j;
-      const int phys = kb ^ ((r >> 1) & 7);
-      *(lds_u32x4 *)(stage + r * 128 + phys * 16) = o;
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = (full || k0 + kr[i] < kext) ? voff[i] : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_void_t *)(stage + (wave * 8 + i * 2) * (kTile * 2)), 16, off, 0, 0, 0);
     }
+  }
+
+  // Columns mn0 .. mn0+31 (one per lane % 32), k = 16 ks + 8 (lane / 32) .. +7.
+  __device__ __forceinline__ static bf16x8 frag(const lds_t *stage, int mn0, int ks, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const int c = (mn0 >> 3) + 2 * (g & 1) + ((j & 3) >> 1);
+    const int sub = 8 * (j & 1);
+    s16x4 h[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int k = ks * 16 + 8 * (g >> 1) + 4 * half + (j >> 2);
+      const int phys = c ^ (4 * (k & 3));
+      h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4 *)(stage + k * (kTile * 2) + phys * 16 + sub));
+    }
+    const s16x4 lo = h[0], hi = h[1];
+    const short v8 __attribute__((ext_vector_type(8))) = {lo[0], lo[1], lo[2], lo[3],
+                                                           hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v8);
   }
 };
-
-// MFMA fragment: rows row0 .. row0+31 of a staged tile, k = 16*ks + 8*(lane/32) .. +7.
-__device__ __forceinline__ bf16x8 read_frag(const lds_t *tile, int row0, int ks, int lane) {
-  const int r = row0 + (lane & 31);
-  const int c = ks * 2 + (lane >> 5);
-  const int phys = c ^ ((r >> 1) & 7);
-  return *(const lds_bf16x8 *)(tile + r * 128 + phys * 16);
-}
 
 struct Acc {
   f32x16 v[4][4];  // [mb][nb]: rows mb*32.., cols nb*32.. of the wave's 128 x 128
@@ -204,56 +234,90 @@ __device__ __forceinline__ int acc_row(int mb, int r, int lane) {
   return mb * 32 + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
 }
 
-__device__ __forceinline__ void mma_stage(const lds_t *sA, const lds_t *sB, Acc &acc, int wm,
-                                          int wn, int lane) {
+struct Frags {
+  bf16x8 a[4], b[4];
+};
+
+template <class OA, class OB>
+__device__ __forceinline__ void load_frags(Frags &f, const lds_t *stage, int ks, int wm, int wn,
+                                           int lane) {
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    bf16x8 a[4], b[4];
+  for (int i = 0; i < 4; ++i) f.a[i] = OA::frag(stage, wm * 128 + i * 32, ks, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = read_frag(sA, wm * 128 + i * 32, ks, lane);
+  for (int j = 0; j < 4; ++j)
+    f.b[j] = OB::frag(stage + kOperandStageBytes, wn * 128 + j * 32, ks, lane);
+}
+
+__device__ __forceinline__ void mma(const Frags &f, Acc &acc) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = read_frag(sB, wn * 128 + j * 32, ks, lane);
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j)
+      acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc.v[i][j], 0, 0, 0);
+}
+
+// Issues the first kStages-1 stages of a tile's K loop (after a barrier that
+// frees the LDS ring, with no other vector-memory operation in flight).
+template <class OA, class OB>
+__device__ __forceinline__ void pipe_prologue(const OA &A, const OB &B, int nk, lds_t *smem,
+                                              int wave) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.v[i][j], 0, 0, 0);
+  for (int s = 0; s < kStages - 1; ++s) {
+    if (s < nk) {
+      A.issue(smem + s * kStageBytes, s * kBK, wave);
+      B.issue(smem + s * kStageBytes + kOperandStageBytes, s * kBK, wave);
+    }
   }
 }
 
-// acc += A_tile * B_tile^T over nk K-steps of 64.  Ends with a barrier, so the
-// caller may reuse the LDS pipeline area afterwards.
+// acc += A_tile * B_tile^T over nk K-steps of 32, with the prologue already
+// issued and its loads the only vector-memory operations in flight.  Ends
+// with a barrier, so the caller may reuse the LDS ring afterwards.
+template <class OA, class OB>
+__device__ __forceinline__ void pipe_run(const OA &A, const OB &B, int nk, lds_t *smem, Acc &acc,
+                                         int wave, int lane) {
+  const int wm = wave >> 1, wn = wave & 1;
+  if (nk <= 0) return;
+  // stage 0 landed (own loads) once at most the loads of stages 1 and 2 are pending
+  if (nk >= 3) wait_vmcnt<16>();
+  else if (nk == 2) wait_vmcnt<8>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+  Frags f0, f1;
+  load_frags<OA, OB>(f0, smem, 0, wm, wn, lane);
+  for (int kt = 0; kt < nk; ++kt) {
+    const lds_t *cur = smem + (kt & (kStages - 1)) * kStageBytes;
+    load_frags<OA, OB>(f1, cur, 1, wm, wn, lane);
+    mma(f0, acc);
+    if (kt + 1 < nk) {
+      // own loads of stage kt+1 done (stage kt+2 may still be in flight), then publish
+      if (kt + 2 < nk) wait_vmcnt<8>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+      if (kt + 3 < nk) {
+        lds_t *st = smem + ((kt + 3) & (kStages - 1)) * kStageBytes;
+        A.issue(st, (kt + 3) * kBK, wave);
+        B.issue(st + kOperandStageBytes, (kt + 3) * kBK, wave);
+      }
+    }
+    // Unconditional, so that both paths leave the same LDS reads in flight and the
+    // MFMAs below only wait for f1 (after the last step this reads a stale stage
+    // whose values are never used).
+    load_frags<OA, OB>(f0, smem + ((kt + 1) & (kStages - 1)) * kStageBytes, 0, wm, wn, lane);
+    mma(f1, acc);
+  }
+  __syncthreads();
+}
+
+// acc += A_tile * B_tile^T over nk K-steps of 32.  Starts and ends with a
+// barrier, so the caller may use the LDS area before and after.
 template <class OA, class OB>
 __device__ __forceinline__ void tile_mainloop(const OA &A, const OB &B, int nk, lds_t *smem,
-                                              Acc &acc, int tid) {
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  typename OA::Stage stA;
-  typename OB::Stage stB;
-  if (nk <= 0) return;
-  A.prefetch(smem, 0, wave, lane, stA);
-  B.prefetch(smem + kOperandStageBytes, 0, wave, lane, stB);
-  A.commit(smem, tid, stA);
-  B.commit(smem + kOperandStageBytes, tid, stB);
-  __builtin_amdgcn_s_waitcnt(0);
+                                              Acc &acc, int wave, int lane) {
+  wait_vmcnt<0>();  // no older vector-memory operation may hide in the counts below
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    lds_t *cur = smem + (kt & 1) * kStageBytes;
-    lds_t *nxt = smem + ((kt & 1) ^ 1) * kStageBytes;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      A.prefetch(nxt, (kt + 1) * kBK, wave, lane, stA);
-      B.prefetch(nxt + kOperandStageBytes, (kt + 1) * kBK, wave, lane, stB);
-    }
-    mma_stage(cur, cur + kOperandStageBytes, acc, wm, wn, lane);
-    if (more) {
-      A.commit(nxt, tid, stA);
-      B.commit(nxt + kOperandStageBytes, tid, stB);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
+  pipe_prologue(A, B, nk, smem, wave);
+  pipe_run(A, B, nk, smem, acc, wave, lane);
 }
 
 }  // namespace flce
