@@ -115,20 +115,19 @@ __global__ void __launch_bounds__(kThreads)
          lane);
   wait_vmcnt<0>();
   __syncthreads();
-  pipe_prologue(A, B, nk, smem, wave);
+  pipe_prologue(A, B, smem, wave);
   Acc acc;
   for (int vt = vt0; vt < vt1; ++vt) {
     const int v0 = vt * kTile;
-    acc.zero();
+    const int vw = v0 + wm * 128;  // first vocabulary row of this wave's half
+    acc.init_rows(p.V - vw, lane);  // rows past the vocabulary end at -inf
     pipe_run(A, B, nk, smem, acc, wave, lane);
     if (vt + 1 < vt1) {
       A.init(p.weight + (size_t)(v0 + kTile) * p.D, p.D, min(kTile, p.V - v0 - kTile), p.D,
              wave, lane);
-      pipe_prologue(A, B, nk, smem, wave);
+      pipe_prologue(A, B, smem, wave);
     }
 
-    const int vw = v0 + wm * 128;           // first vocabulary row of this wave's half
-    const int vlim = p.V - vw;               // wave-relative rows >= vlim do not exist
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       // label logit: exactly one (tile, wave, lane, register) holds it
@@ -140,40 +139,19 @@ __global__ void __launch_bounds__(kThreads)
         if (lr >= 0) have |= 1u << nb;
       }
       float zmax = -kInf;
-      if (vlim >= 128) {
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) zmax = fmaxf(zmax, acc_read(acc.v[mb][nb][r]));
-      } else {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float z = acc_read(acc.v[mb][nb][r]);
-            zmax = fmaxf(zmax, acc_row(mb, r, lane) < vlim ? z : -kInf);
-          }
-      }
+        for (int r = 0; r < 16; ++r) zmax = fmaxf(zmax, acc_read(acc.v[mb][nb][r]));
       const float mold = mrun[nb];
       const float mnew = fmaxf(mold, zmax * kLog2e);
       if (mnew != -kInf) {
         float s = 0.f;
-        if (vlim >= 128) {
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              s += fast_exp2(__builtin_fmaf(acc_read(acc.v[mb][nb][r]), kLog2e, -mnew));
-        } else {
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float e =
-                  fast_exp2(__builtin_fmaf(acc_read(acc.v[mb][nb][r]), kLog2e, -mnew));
-              s += acc_row(mb, r, lane) < vlim ? e : 0.f;
-            }
-        }
+          for (int r = 0; r < 16; ++r)
+            s += fast_exp2(__builtin_fmaf(acc_read(acc.v[mb][nb][r]), kLog2e, -mnew));
         srun[nb] = (mold == -kInf ? 0.f : srun[nb] * fast_exp2(mold - mnew)) + s;
         mrun[nb] = mnew;
       }
@@ -368,8 +346,9 @@ __global__ void __launch_bounds__(kThreads)
   const int v0 = p.vc0 + tm * kTile;
   const int t0 = p.rb0 + tn * kTile;
 
+  const int vw = v0 + wm * 128;
   Acc acc;
-  acc.zero();
+  acc.init_rows(p.V - vw, lane);  // rows past the vocabulary end at -inf, i.e. G = 0
   if (v0 < p.V && t0 < p.T) {
     OperandK A, B;
     A.init(p.weight + (size_t)v0 * p.D, p.D, min(kTile, p.V - v0), p.D, wave, lane);
@@ -377,8 +356,6 @@ __global__ void __launch_bounds__(kThreads)
     tile_mainloop(A, B, (p.D + kBK - 1) / kBK, smem, acc, wave, lane);
   }
 
-  const int vw = v0 + wm * 128;
-  const int vlim = p.V - vw;  // wave-relative rows >= vlim do not exist
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int tl = wn * 128 + nb * 32 + (lane & 31);  // token within the tile
@@ -398,8 +375,7 @@ __global__ void __launch_bounds__(kThreads)
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * q + e;
           const float z = acc_read(acc.v[mb][nb][r]);
-          const float v = c * fast_exp2(__builtin_fmaf(z, kLog2e, -l2));
-          g[e] = acc_row(mb, r, lane) < vlim ? v : 0.f;
+          g[e] = c * fast_exp2(__builtin_fmaf(z, kLog2e, -l2));
         }
         if (any_label) {
 #pragma unroll

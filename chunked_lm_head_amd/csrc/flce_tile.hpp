@@ -68,6 +68,36 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                            kRsrcWord3);
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// The same descriptor as 4 scalar dwords, for the inline-asm loads below.
+__device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t nbytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)nbytes);
+  r[3] = kRsrcWord3;
+  return r;
+}
+
+// One direct-to-LDS load: every lane copies 16 bytes from rsrc + voff to LDS
+// address lds + 16 * lane.  Written in assembly so that the compiler does not
+// order later LDS reads of *other* ring stages behind it (it cannot tell the
+// stages apart and would wait for every such load); the K loop orders them
+// itself with explicit vmcnt waits and barriers.  M0 is saved and restored.
+__device__ __forceinline__ void dma16(i32x4 rs, uint32_t voff, const lds_t *lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)lds;
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rs), "s"(m0));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -118,6 +148,7 @@ __device__ __forceinline__ void grouped_tile(int L, int tiles_m, int tiles_n, in
 
 // Row-major [mn][k]: element (r, k) at byte (r * ld + k) * 2 from base.
 struct OperandK {
+  static constexpr int kReads = 1;  // LDS reads per MFMA fragment
   const char *base;  // tile origin (row 0, k 0)
   uint32_t nbytes;   // valid bytes from base
   int kext;          // valid K extent (multiple of 8)
@@ -141,13 +172,12 @@ struct OperandK {
 
   __device__ __forceinline__ void issue(lds_t *stage, int k0, int wave) const {
     const uint32_t adv = (uint32_t)k0 * 2u;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + adv, remaining(nbytes, adv));
+    const i32x4 rs = rsrc_words(base + adv, remaining(nbytes, adv));
     const bool full = k0 + kBK <= kext;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t off = (full || k0 + kc[i] < kext) ? voff[i] : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_void_t *)(stage + (wave * 64 + i * 16) * (kBK * 2)), 16, off, 0, 0, 0);
+      dma16(rs, off, stage + (wave * 64 + i * 16) * (kBK * 2));
     }
   }
 
@@ -162,6 +192,7 @@ struct OperandK {
 
 // Row-major [k][mn]: element (c, k) at byte (k * ld + c) * 2 from base.
 struct OperandMN {
+  static constexpr int kReads = 2;  // LDS reads per MFMA fragment
   const char *base;   // tile origin (k 0, column 0)
   uint32_t nbytes;    // valid bytes from base
   uint32_t row_bytes; // ld * 2
@@ -187,13 +218,12 @@ struct OperandMN {
 
   __device__ __forceinline__ void issue(lds_t *stage, int k0, int wave) const {
     const uint32_t adv = (uint32_t)k0 * row_bytes;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + adv, remaining(nbytes, adv));
+    const i32x4 rs = rsrc_words(base + adv, remaining(nbytes, adv));
     const bool full = k0 + kBK <= kext;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t off = (full || k0 + kr[i] < kext) ? voff[i] : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_void_t *)(stage + (wave * 8 + i * 2) * (kTile * 2)), 16, off, 0, 0, 0);
+      dma16(rs, off, stage + (wave * 8 + i * 2) * (kTile * 2));
     }
   }
 
@@ -217,6 +247,11 @@ struct OperandMN {
   }
 };
 
+// Row (within the wave's 128) of accumulator register r of block mb, for this lane.
+__device__ __forceinline__ int acc_row(int mb, int r, int lane) {
+  return mb * 32 + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
+}
+
 struct Acc {
   f32x16 v[4][4];  // [mb][nb]: rows mb*32.., cols nb*32.. of the wave's 128 x 128
   __device__ __forceinline__ void zero() {
@@ -227,16 +262,44 @@ struct Acc {
 #pragma unroll
         for (int r = 0; r < 16; ++r) v[i][j][r] = 0.f;
   }
+  // Zero, except rows >= rows_valid (wave-relative) start at -inf.  Their
+  // operand rows read as zeros, so they end the K loop at exactly -inf, which
+  // the log-sum-exp and softmax epilogues treat as absent without masking.
+  __device__ __forceinline__ void init_rows(int rows_valid, int lane) {
+    if (rows_valid >= 128) {
+      zero();
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = acc_row(i, r, lane) < rows_valid ? 0.f : -__builtin_inff();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[i][j][r] = x;
+      }
+  }
 };
-
-// Row (within the wave's 128) of accumulator register r of block mb, for this lane.
-__device__ __forceinline__ int acc_row(int mb, int r, int lane) {
-  return mb * 32 + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
-}
 
 struct Frags {
   bf16x8 a[4], b[4];
 };
+
+// Scheduling pattern for one half step: the 16 MFMAs alternate with the NR LDS
+// fragment reads of the other half and NV global->LDS loads, spread evenly, so
+// that neither the matrix pipe nor the LDS queue sees a long burst (issue is in
+// order per wave).
+template <int NR, int NV, int I = 0>
+__device__ __forceinline__ void interleave() {
+  if constexpr (I < 16) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    constexpr int nread = ((I + 1) * NR) / 16 - (I * NR) / 16;
+    if constexpr (nread > 0) __builtin_amdgcn_sched_group_barrier(0x100, nread, 0);  // DS reads
+    constexpr int nvmem = ((I + 1) * NV) / 16 - (I * NV) / 16;
+    if constexpr (nvmem > 0) __builtin_amdgcn_sched_group_barrier(0x020, nvmem, 0);  // loads
+    interleave<NR, NV, I + 1>();
+  }
+}
 
 template <class OA, class OB>
 __device__ __forceinline__ void load_frags(Frags &f, const lds_t *stage, int ks, int wm, int wn,
@@ -258,54 +321,52 @@ __device__ __forceinline__ void mma(const Frags &f, Acc &acc) {
 
 // Issues the first kStages-1 stages of a tile's K loop (after a barrier that
 // frees the LDS ring, with no other vector-memory operation in flight).
+// Stages past the end of K are issued too, as loads from an empty range that
+// zero-fill ring slots nobody reads; the counts in pipe_run rely on it.
 template <class OA, class OB>
-__device__ __forceinline__ void pipe_prologue(const OA &A, const OB &B, int nk, lds_t *smem,
-                                              int wave) {
+__device__ __forceinline__ void pipe_prologue(const OA &A, const OB &B, lds_t *smem, int wave) {
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s) {
-    if (s < nk) {
-      A.issue(smem + s * kStageBytes, s * kBK, wave);
-      B.issue(smem + s * kStageBytes + kOperandStageBytes, s * kBK, wave);
-    }
+    A.issue(smem + s * kStageBytes, s * kBK, wave);
+    B.issue(smem + s * kStageBytes + kOperandStageBytes, s * kBK, wave);
   }
 }
 
-// acc += A_tile * B_tile^T over nk K-steps of 32, with the prologue already
-// issued and its loads the only vector-memory operations in flight.  Ends
-// with a barrier, so the caller may reuse the LDS ring afterwards.
+// acc += A_tile * B_tile^T over nk >= 1 K-steps of 32, with the prologue
+// already issued and its loads the only vector-memory operations in flight.
+// Each step: MFMAs of the first 16-wide half (the second half's fragments
+// loading in between), publish the next stage (wait for own loads, barrier),
+// issue the stage three ahead, MFMAs of the second half (the next stage's
+// first fragments and the new loads in between).  The last step is peeled so
+// that the loop body has no branch.  Ends with all loads landed and a barrier,
+// so the caller may reuse the LDS ring afterwards.
 template <class OA, class OB>
 __device__ __forceinline__ void pipe_run(const OA &A, const OB &B, int nk, lds_t *smem, Acc &acc,
                                          int wave, int lane) {
+  constexpr int kReads = OA::kReads * 4 + OB::kReads * 4;  // LDS reads per half step
   const int wm = wave >> 1, wn = wave & 1;
-  if (nk <= 0) return;
-  // stage 0 landed (own loads) once at most the loads of stages 1 and 2 are pending
-  if (nk >= 3) wait_vmcnt<16>();
-  else if (nk == 2) wait_vmcnt<8>();
-  else wait_vmcnt<0>();
+  wait_vmcnt<16>();  // own loads of stage 0 landed; stages 1 and 2 may be in flight
   __syncthreads();
   Frags f0, f1;
   load_frags<OA, OB>(f0, smem, 0, wm, wn, lane);
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = 0; kt < nk - 1; ++kt) {
     const lds_t *cur = smem + (kt & (kStages - 1)) * kStageBytes;
     load_frags<OA, OB>(f1, cur, 1, wm, wn, lane);
     mma(f0, acc);
-    if (kt + 1 < nk) {
-      // own loads of stage kt+1 done (stage kt+2 may still be in flight), then publish
-      if (kt + 2 < nk) wait_vmcnt<8>();
-      else wait_vmcnt<0>();
-      __syncthreads();
-      if (kt + 3 < nk) {
-        lds_t *st = smem + ((kt + 3) & (kStages - 1)) * kStageBytes;
-        A.issue(st, (kt + 3) * kBK, wave);
-        B.issue(st + kOperandStageBytes, (kt + 3) * kBK, wave);
-      }
-    }
-    // Unconditional, so that both paths leave the same LDS reads in flight and the
-    // MFMAs below only wait for f1 (after the last step this reads a stale stage
-    // whose values are never used).
+    interleave<kReads, 0>();
+    wait_vmcnt<8>();  // own loads of stage kt+1 landed (kt+2 may be in flight)
+    __syncthreads();  // ... and everyone's; everyone is done with stage kt-1
+    lds_t *st = smem + ((kt + 3) & (kStages - 1)) * kStageBytes;
+    A.issue(st, (kt + 3) * kBK, wave);
+    B.issue(st + kOperandStageBytes, (kt + 3) * kBK, wave);
     load_frags<OA, OB>(f0, smem + ((kt + 1) & (kStages - 1)) * kStageBytes, 0, wm, wn, lane);
     mma(f1, acc);
+    interleave<kReads, 8>();
   }
+  load_frags<OA, OB>(f1, smem + ((nk - 1) & (kStages - 1)) * kStageBytes, 1, wm, wn, lane);
+  mma(f0, acc);
+  mma(f1, acc);
+  wait_vmcnt<0>();  // loads past the end still write LDS: let them land
   __syncthreads();
 }
 
@@ -316,7 +377,8 @@ __device__ __forceinline__ void tile_mainloop(const OA &A, const OB &B, int nk, 
                                               Acc &acc, int wave, int lane) {
   wait_vmcnt<0>();  // no older vector-memory operation may hide in the counts below
   __syncthreads();
-  pipe_prologue(A, B, nk, smem, wave);
+  if (nk <= 0) return;
+  pipe_prologue(A, B, smem, wave);
   pipe_run(A, B, nk, smem, acc, wave, lane);
 }
 
