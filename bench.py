@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
     ap.add_argument("--cpu-sample-vocab", type=int, default=65536)
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="only time the vendor GEMM (torch.mm -> hipBLASLt) at this path's shapes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for HBM counters)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -97,6 +99,10 @@ def main():
         return
 
     from chunked_lm_head_amd import flce, synth
+
+    if args.gemm_ceiling:
+        gemm_ceiling(synth.WORKLOADS[args.workload])
+        return
 
     w = synth.WORKLOADS[args.workload]
     chunk_rows = args.chunk_rows or w.chunk_rows
@@ -202,6 +208,47 @@ def main():
         line["cpu_baseline"] = cpu_baseline(x, min(args.cpu_sample_tokens, T),
                                            args.cpu_sample_vocab)
     print(json.dumps(line), flush=True)
+
+
+def gemm_ceiling(w) -> None:
+    """Vendor bf16 GEMMs (plain 2-D torch.mm, fp32 accumulate, bf16 out) at the logit
+    shape T x V x D and at the backward block shapes, as a practical ceiling."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    def timeit(fn, flops, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        return ms, flops / (ms / 1e3) / 1e12
+
+    T, D, V = w.T, w.H, w.V
+    res = {}
+    h, W = rnd(T, D), rnd(V, D)
+    z = torch.empty(T, V, dtype=torch.bfloat16, device=dev)
+    res["logits_T_V_D"] = timeit(lambda: torch.mm(h, W.t(), out=z), 2.0 * T * V * D)
+    del z
+    R, Vc = min(T, 8192), 8192
+    G = rnd(R, Vc)
+    Wc = W[:Vc].contiguous()
+    hb = h[:R].contiguous()
+    res["dH_R_D_Vc"] = timeit(lambda: torch.mm(G, Wc), 2.0 * R * Vc * D)
+    res["dW_Vc_D_R"] = timeit(lambda: torch.mm(G.t(), hb), 2.0 * R * Vc * D)
+    out = {k: {"ms": round(v[0], 3), "TFLOP/s": round(v[1], 1),
+               "frac_of_2.5PF": round(v[1] / (PEAK_BF16 / 1e12), 4)} for k, v in res.items()}
+    print(json.dumps({"gemm_ceiling": out, "workload": w.name}), flush=True)
 
 
 def _kernel_sha() -> str:

@@ -71,7 +71,7 @@ struct FwdLseParams {
   float *zlab;              // [T_pad] logit of the label
 };
 
-constexpr int kLdsFwd = kPipeBytes + 2048;
+constexpr int kLdsFwd = kPipeBytes;  // the partial-merge exchange reuses the ring
 
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(1, 1))) fwd_lse_kernel(FwdLseParams p) {
@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(kThreads)
     if (have & (1u << nb)) p.zlab[t0 + wn * 128 + nb * 32 + (lane & 31)] = zl[nb];
 
   // Merge the two lanes holding one token (l, l ^ 32), then the two waves (wm).
-  lds_f32x2 *xch = (lds_f32x2 *)(smem + kPipeBytes);  // [wn][nb][32]
+  lds_f32x2 *xch = (lds_f32x2 *)smem;  // [wn][nb][32], in the (idle) ring
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const float m2 = __shfl_xor(mrun[nb], 32);

@@ -20,7 +20,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libflce.so")
+# FLCE_LIB may name another build of the same library (e.g. to compare two builds).
+LIB_PATH = os.environ.get("FLCE_LIB") or os.path.join(_HERE, "libflce.so")
 
 MODE_NLL = 0
 MODE_LOGPROB = 1

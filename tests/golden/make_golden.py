@@ -1,0 +1,80 @@
+"""Write oracle values for the full-size workloads (run on the CPU; calls only the oracle).
+
+For each workload the inputs are re-drawn with the seeded generator and the
+float64 oracle computes, over ALL tokens and the FULL vocabulary:
+  * the per-token output and lse of a sample of tokens, and the mean;
+  * the grad_hidden rows of those tokens;
+  * the grad_weight rows of a sample of vocabulary entries (these need the
+    lse of every token, hence the full forward).
+The samples include the first and last tokens and vocabulary rows, tile
+boundaries, the ragged tail, ignored tokens and labels of sampled tokens.
+
+Usage:  python tests/golden/make_golden.py [workload ...]
+"""
+from __future__ import annotations
+
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+from chunked_lm_head_amd import synth  # noqa: E402  (inputs only)
+from oracle import flce_oracle as o  # noqa: E402
+
+FULL = ("single_chunk", "qwen3_8b_sft", "grpo_logprob", "long_context")
+
+
+def sample_tokens(w: synth.Workload, labels: np.ndarray, rng) -> np.ndarray:
+    T = w.T
+    picks = {0, 1, 255, 256, T // 2, T - 1, T - 2}
+    picks |= {T - 1 - int(i) for i in range(0, min(T, 300), 37)}     # ragged / last tile
+    ign = np.nonzero(labels == synth.IGNORE_INDEX)[0]
+    picks |= set(int(i) for i in ign[:3])
+    if w.prompt_len:
+        picks |= {w.seq_len + 5, w.prompt_len - 1, w.prompt_len}    # zero / nonzero grads
+    while len(picks) < 24:
+        picks.add(int(rng.integers(0, T)))
+    return np.array(sorted(p for p in picks if 0 <= p < T), dtype=np.int64)
+
+
+def sample_vocab(w: synth.Workload, labels: np.ndarray, tokens: np.ndarray, rng) -> np.ndarray:
+    V = w.V
+    picks = {0, 255, 256, V - 1, V - 2}
+    used = labels[tokens][labels[tokens] != synth.IGNORE_INDEX]
+    picks |= set(int(x) for x in used[:4])
+    while len(picks) < 12:
+        picks.add(int(rng.integers(0, V)))
+    return np.array(sorted(picks), dtype=np.int64)
+
+
+def make(name: str) -> str:
+    w = synth.WORKLOADS[name]
+    t0 = time.time()
+    x = synth.make_inputs(w)
+    rng = np.random.default_rng(w.seed + 77)
+    f = o.forward(x.hidden, x.weight, x.labels, synth.IGNORE_INDEX, w.mode)
+    tokens = sample_tokens(w, x.labels, rng)
+    vocab = sample_vocab(w, x.labels, tokens, rng)
+    if w.reduction == "mean":
+        c = o.token_scale(x.labels, w.V, synth.IGNORE_INDEX, w.mode, grad_mean=1.0)
+    else:
+        c = o.token_scale(x.labels, w.V, synth.IGNORE_INDEX, w.mode, grad_out=x.grad_out)
+    dh = o.grad_hidden_rows(x.hidden, x.weight, x.labels, tokens, c[tokens], synth.IGNORE_INDEX)
+    dw = o.grad_weight_rows(x.hidden, x.weight, x.labels, vocab, c, f.lse)
+    path = os.path.join(HERE, f"{name}.npz")
+    np.savez(path, tokens=tokens, out=f.out[tokens], lse=f.lse[tokens], mean=np.float64(f.mean),
+             n_valid=np.int64(f.n_valid), vocab=vocab, dh=dh.astype(np.float32),
+             dw=dw.astype(np.float32), dw_norm_rows=np.linalg.norm(dw, axis=1),
+             seed=np.int64(w.seed))
+    print(f"{name}: {time.time() - t0:.0f} s -> {path}", flush=True)
+    return path
+
+
+if __name__ == "__main__":
+    for n in (sys.argv[1:] or FULL):
+        make(n)

@@ -1,0 +1,115 @@
+"""Full-size workloads on the GPU, in the launch configuration bench.py times.
+
+Expected values are oracle outputs for sampled tokens and vocabulary rows,
+written by tests/golden/make_golden.py (float64 CPU oracle over all tokens and
+the full vocabulary).  Beyond the samples, properties that hold at any size
+are checked on the complete outputs:
+  * each row of G sums to zero, so the vocabulary sum of dW vanishes;
+  * <dH, H> = <dW, W> (both equal sum_tv G_tv z_tv);
+  * ignored tokens and tokens with zero upstream grad have exactly zero dH rows
+    (and ignored tokens output exactly 0).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from chunked_lm_head_amd import synth
+
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+NAMES = ["single_chunk", "qwen3_8b_sft", "grpo_logprob", "long_context"]
+
+
+def _golden(name):
+    path = os.path.join(HERE, "golden", f"{name}.npz")
+    if not os.path.exists(path):
+        pytest.fail(f"missing {path}; run tests/golden/make_golden.py")
+    return np.load(path)
+
+
+def _run_full(name):
+    from chunked_lm_head_amd import flce
+
+    w = synth.WORKLOADS[name]
+    print(f"case {name}: T={w.T} D={w.H} V={w.V} chunk_rows={w.chunk_rows}", flush=True)
+    x = synth.make_inputs(w)
+    dev = gu.device()
+    h = gu.bf16_tensor(x.hidden, dev)
+    W = gu.bf16_tensor(x.weight, dev)
+    y = torch.from_numpy(x.labels).to(dev)
+    ws = flce.alloc_workspace(w.T, w.H, w.V, w.chunk_rows, dev)
+    out, lse, mean = flce.forward(h, W, y, chunk_rows=w.chunk_rows, mode=w.mode, workspace=ws)
+    if x.grad_out is not None:
+        kw = dict(grad_out=torch.from_numpy(x.grad_out).to(dev))
+    else:
+        kw = dict(grad_mean=torch.ones((), dtype=torch.float32, device=dev))
+    dh, dw = flce.backward(h, W, y, lse, chunk_rows=w.chunk_rows, mode=w.mode, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    return w, x, h, W, out, lse, mean, dh, dw
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_full_size_against_oracle_samples(name):
+    g = _golden(name)
+    w, x, h, W, out, lse, mean, dh, dw = _run_full(name)
+    assert int(g["seed"]) == w.seed
+    tok = torch.from_numpy(g["tokens"]).to(h.device)
+    voc = torch.from_numpy(g["vocab"]).to(h.device)
+    out_s = out[tok].cpu().numpy()
+    lse_s = lse[tok].cpu().numpy()
+    assert gu.max_abs(out_s, g["out"]) <= gu.OUT_TOL, gu.max_abs(out_s, g["out"])
+    assert gu.max_abs(lse_s, g["lse"]) <= gu.OUT_TOL, gu.max_abs(lse_s, g["lse"])
+    assert abs(float(mean.cpu()) - float(g["mean"])) <= gu.OUT_TOL
+    dh_s = dh[tok].float().cpu().numpy()
+    dw_s = dw[voc].cpu().numpy()
+    e_dh = gu.rel_fro(dh_s, g["dh"].astype(np.float64))
+    e_dw = gu.rel_fro(dw_s, g["dw"].astype(np.float64))
+    print(f"{name}: |d out| {gu.max_abs(out_s, g['out']):.2e} |d lse| "
+          f"{gu.max_abs(lse_s, g['lse']):.2e} |d mean| {abs(float(mean.cpu()) - float(g['mean'])):.2e}"
+          f" dH rel {e_dh:.2e} dW rel {e_dw:.2e}", flush=True)
+    assert e_dh <= gu.GRAD_TOL, e_dh
+    assert e_dw <= gu.GRAD_TOL, e_dw
+
+    # properties on the complete outputs (fp64 reductions on the GPU)
+    dw64 = dw.double()
+    col = dw64.sum(dim=0)
+    fro = torch.linalg.norm(dw64)
+    assert float(torch.linalg.norm(col) / fro) <= 1e-2
+    lhs = float((dh.double() * h.double()).sum())
+    rhs = float((dw64 * W.double()).sum())
+    assert abs(lhs - rhs) <= 1e-2 * max(abs(lhs), abs(rhs), 1e-30), (lhs, rhs)
+    yl = torch.from_numpy(x.labels).to(h.device)
+    ign = yl == synth.IGNORE_INDEX
+    if bool(ign.any()):
+        assert bool((out[ign] == 0).all())
+        assert bool((dh[ign] == 0).all())
+    if x.grad_out is not None:
+        zero = torch.from_numpy(x.grad_out == 0).to(h.device)
+        assert bool((dh[zero] == 0).all())
+    assert bool(torch.isfinite(out[~ign]).all())
+
+
+def test_long_context_memory_is_one_chunk_of_logits():
+    """Device memory the step needs beyond inputs and outputs is the workspace, which is
+    bounded by one chunk of fp32 logits plus terms linear in T and D (not T x V)."""
+    from chunked_lm_head_amd import flce
+
+    w = synth.WORKLOADS["long_context"]
+    p = flce.describe_plan(w.T, w.H, w.V, w.chunk_rows)
+    wsb = flce.workspace_bytes(w.T, w.H, w.V, w.chunk_rows)
+    assert p["grad_tile_bytes"] <= w.chunk_rows * w.V * 4
+    full_logits = w.T * w.V * 4
+    assert wsb < full_logits / 50
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    _, _, h, W, out, lse, mean, dh, dw = _run_full("long_context")
+    peak = torch.cuda.max_memory_allocated() - base
+    io = sum(t.numel() * t.element_size() for t in (h, W, out, lse, mean, dh, dw))
+    io += w.T * 8  # labels
+    assert peak - io <= wsb + (64 << 20), (peak, io, wsb)
