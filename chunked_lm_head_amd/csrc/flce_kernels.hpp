@@ -46,14 +46,23 @@ __device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t rs, uint32_t of
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
 }
 
-// Per lane and token column: which accumulator register of the wave's 128
-// rows holds vocabulary row `rel` (-1 if none): row = 32 mb + 8 (r / 4) +
-// 4 (lane / 32) + r % 4.
+// Per lane and token column: which accumulator register (4 mb + r) of the
+// wave's 128 rows holds vocabulary row `rel` (-1 if none): row = 16 mb +
+// 4 (lane / 16) + r.
 __device__ __forceinline__ int label_reg(int rel, int lane) {
   if ((unsigned)rel >= 128u) return -1;
-  const int i = rel & 31;
-  if (((i >> 2) & 1) != (lane >> 5)) return -1;
-  return (rel >> 5) * 16 + ((i & 3) | ((i >> 3) << 2));
+  if (((rel >> 2) & 3) != (lane >> 4)) return -1;
+  return (rel >> 4) * 4 + (rel & 3);
+}
+
+// Merges two (max, sum of 2^(x - max)) pairs of the base-2 log-sum-exp.
+__device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  float S = 0.f;
+  if (M != -kInf)
+    S = (m == -kInf ? 0.f : s * fast_exp2(m - M)) + (m2 == -kInf ? 0.f : s2 * fast_exp2(m2 - M));
+  m = M;
+  s = S;
 }
 
 // ---------------------------------------------------------------------------
@@ -91,11 +100,11 @@ __global__ void __launch_bounds__(kThreads)
   B.init(p.hidden + (size_t)t0 * p.D, p.D, min(kTile, p.T - t0), p.D, wave, lane);
   const int nk = (p.D + kBK - 1) / kBK;
 
-  int lab[4];
-  float mrun[4], srun[4], zl[4];
+  int lab[8];
+  float mrun[8], srun[8], zl[8];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int t = t0 + wn * 128 + nb * 32 + (lane & 31);
+  for (int nb = 0; nb < 8; ++nb) {
+    const int t = t0 + wn * 128 + nb * 16 + (lane & 15);
     int y = -1;
     if (t < p.T) {
       const int64_t yy = p.labels[t];
@@ -129,28 +138,28 @@ __global__ void __launch_bounds__(kThreads)
     }
 
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
+    for (int nb = 0; nb < 8; ++nb) {
       // label logit: exactly one (tile, wave, lane, register) holds it
       const int lr = label_reg(lab[nb] - vw, lane);
       if (__builtin_amdgcn_ballot_w64(lr >= 0)) {
 #pragma unroll
-        for (int q = 0; q < 64; ++q)
-          if (lr == q) zl[nb] = acc_read(acc.v[q >> 4][nb][q & 15]);
+        for (int q = 0; q < 32; ++q)
+          if (lr == q) zl[nb] = acc_read(acc.v[q >> 2][nb][q & 3]);
         if (lr >= 0) have |= 1u << nb;
       }
       float zmax = -kInf;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) zmax = fmaxf(zmax, acc_read(acc.v[mb][nb][r]));
+        for (int r = 0; r < 4; ++r) zmax = fmaxf(zmax, acc_read(acc.v[mb][nb][r]));
       const float mold = mrun[nb];
       const float mnew = fmaxf(mold, zmax * kLog2e);
       if (mnew != -kInf) {
         float s = 0.f;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
+          for (int r = 0; r < 4; ++r)
             s += fast_exp2(__builtin_fmaf(acc_read(acc.v[mb][nb][r]), kLog2e, -mnew));
         srun[nb] = (mold == -kInf ? 0.f : srun[nb] * fast_exp2(mold - mnew)) + s;
         mrun[nb] = mnew;
@@ -158,37 +167,26 @@ __global__ void __launch_bounds__(kThreads)
     }
   }
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-    if (have & (1u << nb)) p.zlab[t0 + wn * 128 + nb * 32 + (lane & 31)] = zl[nb];
+  for (int nb = 0; nb < 8; ++nb)
+    if (have & (1u << nb)) p.zlab[t0 + wn * 128 + nb * 16 + (lane & 15)] = zl[nb];
 
-  // Merge the two lanes holding one token (l, l ^ 32), then the two waves (wm).
-  lds_f32x2 *xch = (lds_f32x2 *)smem;  // [wn][nb][32], in the (idle) ring
+  // Merge the four lanes holding one token (l, l ^ 16, l ^ 32, l ^ 48), then
+  // the two waves (wm).
+  lds_f32x2 *xch = (lds_f32x2 *)smem;  // [wn][nb][16], in the (idle) ring
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const float m2 = __shfl_xor(mrun[nb], 32);
-    const float s2 = __shfl_xor(srun[nb], 32);
-    const float M = fmaxf(mrun[nb], m2);
-    float S = 0.f;
-    if (M != -kInf) {
-      S = (mrun[nb] == -kInf ? 0.f : srun[nb] * fast_exp2(mrun[nb] - M)) +
-          (m2 == -kInf ? 0.f : s2 * fast_exp2(m2 - M));
-    }
-    mrun[nb] = M;
-    srun[nb] = S;
-    if (wm == 1 && lane < 32) xch[(wn * 4 + nb) * 32 + lane] = f32x2{M, S};
+  for (int nb = 0; nb < 8; ++nb) {
+    lse_merge(mrun[nb], srun[nb], __shfl_xor(mrun[nb], 16), __shfl_xor(srun[nb], 16));
+    lse_merge(mrun[nb], srun[nb], __shfl_xor(mrun[nb], 32), __shfl_xor(srun[nb], 32));
+    if (wm == 1 && lane < 16) xch[(wn * 8 + nb) * 16 + lane] = f32x2{mrun[nb], srun[nb]};
   }
   __syncthreads();
-  if (wm == 0 && lane < 32) {
+  if (wm == 0 && lane < 16) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const f32x2 o = xch[(wn * 4 + nb) * 32 + lane];
-      const float M = fmaxf(mrun[nb], o[0]);
-      float S = 0.f;
-      if (M != -kInf) {
-        S = (mrun[nb] == -kInf ? 0.f : srun[nb] * fast_exp2(mrun[nb] - M)) +
-            (o[0] == -kInf ? 0.f : o[1] * fast_exp2(o[0] - M));
-      }
-      const int t = t0 + wn * 128 + nb * 32 + lane;
+    for (int nb = 0; nb < 8; ++nb) {
+      const f32x2 o = xch[(wn * 8 + nb) * 16 + lane];
+      float M = mrun[nb], S = srun[nb];
+      lse_merge(M, S, o[0], o[1]);
+      const int t = t0 + wn * 128 + nb * 16 + lane;
       p.part_m[(size_t)sp * p.T_pad + t] = M;
       p.part_s[(size_t)sp * p.T_pad + t] = S;
     }
@@ -357,8 +355,8 @@ __global__ void __launch_bounds__(kThreads)
   }
 
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int tl = wn * 128 + nb * 32 + (lane & 31);  // token within the tile
+  for (int nb = 0; nb < 8; ++nb) {
+    const int tl = wn * 128 + nb * 16 + (lane & 15);  // token within the tile
     const int t = t0 + tl;                            // < rb0 + R <= T_pad
     const float c = p.c[t];
     const float l2 = p.lse2[t];
@@ -367,27 +365,24 @@ __global__ void __launch_bounds__(kThreads)
     const int lr = label_reg(y - vw, lane);
     const bool any_label = __builtin_amdgcn_ballot_w64(lr >= 0) != 0;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 8; ++mb) {
+      float g[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float g[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * q + e;
-          const float z = acc_read(acc.v[mb][nb][r]);
-          g[e] = c * fast_exp2(__builtin_fmaf(z, kLog2e, -l2));
-        }
-        if (any_label) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (lr == mb * 16 + 4 * q + e) g[e] -= c;
-        }
-        u32x2 w;
-        w[0] = pack_bf16(g[0], g[1]);
-        w[1] = pack_bf16(g[2], g[3]);
-        const int vl = wm * 128 + mb * 32 + q * 8 + ((lane >> 5) << 2);
-        *(lds_u32x2 *)(smem + tl * kGPitch + vl * 2) = w;
+      for (int e = 0; e < 4; ++e) {
+        const float z = acc_read(acc.v[mb][nb][e]);
+        g[e] = c * fast_exp2(__builtin_fmaf(z, kLog2e, -l2));
       }
+      if (any_label) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (lr == mb * 4 + e) g[e] -= c;
+      }
+      u32x2 w;
+      w[0] = pack_bf16(g[0], g[1]);
+      w[1] = pack_bf16(g[2], g[3]);
+      const int vl = wm * 128 + acc_row(mb, 0, lane);  // 4 consecutive vocabulary rows
+      *(lds_u32x2 *)(smem + tl * kGPitch + vl * 2) = w;
+    }
   }
   __syncthreads();
   // LDS [token][vocab] -> G rows, 16 bytes per lane, 512 contiguous bytes per 32 lanes.
@@ -404,38 +399,40 @@ __global__ void __launch_bounds__(kThreads)
 // Writes (or adds) a wave's 128 x 128 fp32 accumulator block to row-major
 // memory through a buffer descriptor; lanes whose column lies past `cols`
 // and rows past the descriptor's range are dropped by the hardware.  When
-// adding, the 16 old values of a 32 x 32 block are loaded together before any
-// is consumed, so their latencies overlap.
+// adding, the 16 old values of four 16 x 16 blocks are loaded together before
+// any is consumed, so their latencies overlap.
 __device__ __forceinline__ void store_acc_block(const Acc &acc, __amdgpu_buffer_rsrc_t rs,
                                                 int ld, int row0, int col0, int cols,
                                                 bool accumulate, int lane) {
   if (accumulate) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int col = col0 + nb * 32 + (lane & 31);
+    for (int nb = 0; nb < 8; ++nb) {
+      const int col = col0 + nb * 16 + (lane & 15);
       const bool col_ok = col < cols;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int m4 = 0; m4 < 8; m4 += 4) {
         uint32_t off[16];
         float old[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          off[r] = col_ok ? (uint32_t)((row0 + acc_row(mb, r, lane)) * ld + col) * 4u : kOOB;
-          old[r] = load_f32(rs, off[r]);
+        for (int q = 0; q < 16; ++q) {
+          const int row = row0 + acc_row(m4 + (q >> 2), q & 3, lane);
+          off[q] = col_ok ? (uint32_t)(row * ld + col) * 4u : kOOB;
+          old[q] = load_f32(rs, off[q]);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) store_f32(rs, off[r], acc_read(acc.v[mb][nb][r]) + old[r]);
+        for (int q = 0; q < 16; ++q)
+          store_f32(rs, off[q], acc_read(acc.v[m4 + (q >> 2)][nb][q & 3]) + old[q]);
       }
     }
   } else {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int col = col0 + nb * 32 + (lane & 31);
+    for (int nb = 0; nb < 8; ++nb) {
+      const int col = col0 + nb * 16 + (lane & 15);
       const bool col_ok = col < cols;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < 4; ++r) {
           const uint32_t off =
               col_ok ? (uint32_t)((row0 + acc_row(mb, r, lane)) * ld + col) * 4u : kOOB;
           store_f32(rs, off, acc_read(acc.v[mb][nb][r]));

@@ -3,8 +3,11 @@
 //
 // One workgroup of 256 threads (4 wave64s in a 2 x 2 grid) computes a
 // 256 x 256 fp32 tile C[m][n] = sum_k A(m, k) B(n, k) with
-// v_mfma_f32_32x32x16_bf16; each wave owns 128 x 128 of it as 4 x 4 MFMA blocks
-// (256 fp32 accumulators per lane, held in AGPRs).
+// v_mfma_f32_16x16x32_bf16; each wave owns 128 x 128 of it as 8 x 8 MFMA blocks
+// (256 fp32 accumulators per lane, held in AGPRs).  On MI355X this shape
+// sustains about 16% more bf16 throughput than 32x32x16 under the clock the
+// chip holds at full load, which is why it is used although it needs the
+// same LDS traffic per FLOP.
 //
 // Pipeline: K advances 32 at a time through a 4-stage LDS ring (4 x 32 KiB);
 // stage k + 3 is in flight while stage k is multiplied.  Every operand moves
@@ -12,16 +15,16 @@
 // registers, no VALU), from a buffer descriptor that covers exactly the valid
 // bytes; masked lanes use an offset past its end, so ragged edges read zeros
 // and no load can leave its tensor.  One barrier per K step, placed between
-// the two 16-wide halves of the step so that the fragment reads of the next
+// the MFMAs of B blocks 0..3 and 4..7, so that the fragment reads of the next
 // stage overlap the MFMAs of the current one.
 //
 // Two operand layouts in global memory, two layouts in LDS:
 //  * K-contiguous ([mn][k], e.g. H and W in the logit GEMM): LDS rows of 32 k
-//    (64 B); chunk c of row r sits at chunk c ^ ((r >> 2) & 3).  Fragments are
+//    (64 B); chunk c of row r sits at chunk c ^ k_swizzle(r).  Fragments are
 //    ds_read_b128.
 //  * MN-contiguous ([k][mn], e.g. W in dH = G W, H and G in dW = G^T H): LDS
 //    rows of 256 mn (512 B) per k; 16-byte chunk c of row k sits at
-//    c ^ (4 * (k & 3)).  Fragments are two ds_read_b64_tr_b16, which transpose
+//    c ^ mn_swizzle(k).  Fragments are two ds_read_b64_tr_b16, which transpose
 //    4 x 4 blocks of 16-bit values across lanes: within each group of 16
 //    lanes, lane i receives element i % 4 of the 8-byte chunks addressed by
 //    lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 of the group.
@@ -36,7 +39,6 @@ namespace flce {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -122,6 +124,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt with the vector-memory and LDS counters constrained (gfx9 encoding).
+template <int VM, int LG>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  static_assert(VM >= 0 && VM < 64 && LG >= 0 && LG < 16, "waitcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LG << 8));
+}
+
 // Workgroup id -> logical tile id such that each XCD (ids are dealt to the 8
 // XCDs round-robin) receives one contiguous range of logical ids.
 __device__ __forceinline__ int xcd_contiguous(int bid, int n) {
@@ -146,6 +155,22 @@ __device__ __forceinline__ void grouped_tile(int L, int tiles_m, int tiles_n, in
 // Operands.  Each wave issues 4 DMA instructions per operand per stage.
 // ---------------------------------------------------------------------------
 
+// Chunk swizzle of the K-major LDS layout (rows of four 16-byte chunks): a
+// fragment read takes chunk c of 16 consecutive rows in each 16-lane group;
+// folding row bits 1 and 2 into the chunk index spreads them over all banks
+// (measured conflict-free with the LDS bank-conflict counter at every 1 KiB
+// offset of the ring, where folding bits 2 and 3 costs four extra cycles per
+// read).
+__device__ __forceinline__ int k_swizzle(int r) { return (r >> 1) & 3; }
+
+// One stage's K slice of an operand: its buffer descriptor (scalar), first k,
+// and whether the whole slice lies inside the valid K extent.
+struct DmaSlice {
+  i32x4 rs;
+  int k0;
+  bool full;
+};
+
 // Row-major [mn][k]: element (r, k) at byte (r * ld + k) * 2 from base.
 struct OperandK {
   static constexpr int kReads = 1;  // LDS reads per MFMA fragment
@@ -164,31 +189,43 @@ struct OperandK {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wave * 64 + i * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((r >> 2) & 3);
+      const int c = (lane & 3) ^ k_swizzle(r);
       kc[i] = c * 8;
       voff[i] = r < rows ? (uint32_t)(r * ld + c * 8) * 2u : kOOB;
     }
   }
 
-  __device__ __forceinline__ void issue(lds_t *stage, int k0, int wave) const {
+  // Descriptor of the K slice [k0, k0 + kBK) of every row.
+  __device__ __forceinline__ DmaSlice prep(int k0) const {
     const uint32_t adv = (uint32_t)k0 * 2u;
-    const i32x4 rs = rsrc_words(base + adv, remaining(nbytes, adv));
-    const bool full = k0 + kBK <= kext;
+    return DmaSlice{rsrc_words(base + adv, remaining(nbytes, adv)), k0, k0 + kBK <= kext};
+  }
+  // Load i (0..3) of this wave's share of a stage.
+  __device__ __forceinline__ void issue_one(const DmaSlice &d, lds_t *stage, int i,
+                                            int wave) const {
+    const uint32_t off = (d.full || d.k0 + kc[i] < kext) ? voff[i] : kOOB;
+    dma16(d.rs, off, stage + (wave * 64 + i * 16) * (kBK * 2));
+  }
+  __device__ __forceinline__ void issue(lds_t *stage, int k0, int wave) const {
+    const DmaSlice d = prep(k0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t off = (full || k0 + kc[i] < kext) ? voff[i] : kOOB;
-      dma16(rs, off, stage + (wave * 64 + i * 16) * (kBK * 2));
-    }
+    for (int i = 0; i < 4; ++i) issue_one(d, stage, i, wave);
   }
 
-  // Rows row0 .. row0+31, k = 16 ks + 8 (lane / 32) .. +7.
-  __device__ __forceinline__ static bf16x8 frag(const lds_t *stage, int row0, int ks, int lane) {
-    const int r = row0 + (lane & 31);
-    const int c = ks * 2 + (lane >> 5);
-    const int phys = c ^ ((r >> 2) & 3);
+  // Rows row0 .. row0+15 (one per lane % 16), k = 8 (lane / 16) .. +7.
+  __device__ __forceinline__ static bf16x8 frag(const lds_t *stage, int row0, int lane) {
+    const int r = row0 + (lane & 15);
+    const int c = lane >> 4;
+    const int phys = c ^ k_swizzle(r);
     return *(const lds_bf16x8 *)(stage + r * (kBK * 2) + phys * 16);
   }
 };
+
+// Chunk swizzle of the MN-major LDS layout: rows k and k + 8 of a stage must
+// differ so that the two 16-lane groups of one transpose read (same columns,
+// k 8 apart) fall into different banks, and rows k .. k+3 so that the four
+// k rows one read gathers do.
+__device__ __forceinline__ int mn_swizzle(int k) { return 4 * (k & 3) + 2 * ((k >> 3) & 1); }
 
 // Row-major [k][mn]: element (c, k) at byte (k * ld + c) * 2 from base.
 struct OperandMN {
@@ -210,33 +247,42 @@ struct OperandMN {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k = wave * 8 + i * 2 + (lane >> 5);
-      const int c = (lane & 31) ^ (4 * (k & 3));
+      const int c = (lane & 31) ^ mn_swizzle(k);
       kr[i] = k;
       voff[i] = c * 8 < cols ? (uint32_t)(k * ld + c * 8) * 2u : kOOB;
     }
   }
 
-  __device__ __forceinline__ void issue(lds_t *stage, int k0, int wave) const {
+  // Descriptor of the k rows [k0, k0 + kBK).
+  __device__ __forceinline__ DmaSlice prep(int k0) const {
     const uint32_t adv = (uint32_t)k0 * row_bytes;
-    const i32x4 rs = rsrc_words(base + adv, remaining(nbytes, adv));
-    const bool full = k0 + kBK <= kext;
+    return DmaSlice{rsrc_words(base + adv, remaining(nbytes, adv)), k0, k0 + kBK <= kext};
+  }
+  // Load i (0..3) of this wave's share of a stage.
+  __device__ __forceinline__ void issue_one(const DmaSlice &d, lds_t *stage, int i,
+                                            int wave) const {
+    const uint32_t off = (d.full || d.k0 + kr[i] < kext) ? voff[i] : kOOB;
+    dma16(d.rs, off, stage + (wave * 8 + i * 2) * (kTile * 2));
+  }
+  __device__ __forceinline__ void issue(lds_t *stage, int k0, int wave) const {
+    const DmaSlice d = prep(k0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t off = (full || k0 + kr[i] < kext) ? voff[i] : kOOB;
-      dma16(rs, off, stage + (wave * 8 + i * 2) * (kTile * 2));
-    }
+    for (int i = 0; i < 4; ++i) issue_one(d, stage, i, wave);
   }
 
-  // Columns mn0 .. mn0+31 (one per lane % 32), k = 16 ks + 8 (lane / 32) .. +7.
-  __device__ __forceinline__ static bf16x8 frag(const lds_t *stage, int mn0, int ks, int lane) {
+  // Columns mn0 .. mn0+15 (one per lane % 16), k = 8 (lane / 16) .. +7.  Lane
+  // j of a 16-lane group addresses 4 columns mn0 + 4 (j % 4) .. +3 of k row
+  // 8 g + 4 half + j / 4; the transpose hands lane i column mn0 + i of the
+  // four k rows.
+  __device__ __forceinline__ static bf16x8 frag(const lds_t *stage, int mn0, int lane) {
     const int g = lane >> 4, j = lane & 15;
-    const int c = (mn0 >> 3) + 2 * (g & 1) + ((j & 3) >> 1);
+    const int c = (mn0 >> 3) + ((j & 3) >> 1);
     const int sub = 8 * (j & 1);
     s16x4 h[2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int k = ks * 16 + 8 * (g >> 1) + 4 * half + (j >> 2);
-      const int phys = c ^ (4 * (k & 3));
+      const int k = 8 * g + 4 * half + (j >> 2);
+      const int phys = c ^ mn_swizzle(k);
       h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4 *)(stage + k * (kTile * 2) + phys * 16 + sub));
     }
@@ -247,20 +293,21 @@ struct OperandMN {
   }
 };
 
-// Row (within the wave's 128) of accumulator register r of block mb, for this lane.
+// Row (within the wave's 128) of accumulator register r of block mb, for this
+// lane; the column within the block is lane % 16.
 __device__ __forceinline__ int acc_row(int mb, int r, int lane) {
-  return mb * 32 + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
+  return mb * 16 + ((lane >> 4) << 2) + r;
 }
 
 struct Acc {
-  f32x16 v[4][4];  // [mb][nb]: rows mb*32.., cols nb*32.. of the wave's 128 x 128
+  f32x4 v[8][8];  // [mb][nb]: rows mb*16.., cols nb*16.. of the wave's 128 x 128
   __device__ __forceinline__ void zero() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) v[i][j][r] = 0.f;
+        for (int r = 0; r < 4; ++r) v[i][j][r] = 0.f;
   }
   // Zero, except rows >= rows_valid (wave-relative) start at -inf.  Their
   // operand rows read as zeros, so they end the K loop at exactly -inf, which
@@ -271,52 +318,62 @@ struct Acc {
       return;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < 4; ++r) {
         const float x = acc_row(i, r, lane) < rows_valid ? 0.f : -__builtin_inff();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[i][j][r] = x;
+        for (int j = 0; j < 8; ++j) v[i][j][r] = x;
       }
   }
 };
 
-struct Frags {
-  bf16x8 a[4], b[4];
+// Fragments of one K step: the wave's 8 A blocks, and 4 of its 8 B blocks.
+struct FragA {
+  bf16x8 a[8];
+};
+struct FragB {
+  bf16x8 b[4];
 };
 
-// Scheduling pattern for one half step: the 16 MFMAs alternate with the NR LDS
-// fragment reads of the other half and NV global->LDS loads, spread evenly, so
-// that neither the matrix pipe nor the LDS queue sees a long burst (issue is in
-// order per wave).
-template <int NR, int NV, int I = 0>
-__device__ __forceinline__ void interleave() {
-  if constexpr (I < 16) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    constexpr int nread = ((I + 1) * NR) / 16 - (I * NR) / 16;
-    if constexpr (nread > 0) __builtin_amdgcn_sched_group_barrier(0x100, nread, 0);  // DS reads
-    constexpr int nvmem = ((I + 1) * NV) / 16 - (I * NV) / 16;
-    if constexpr (nvmem > 0) __builtin_amdgcn_sched_group_barrier(0x020, nvmem, 0);  // loads
-    interleave<NR, NV, I + 1>();
-  }
+__device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Fragment q (0..11) of a stage in the order the first half step consumes
+// them: A block 0, B blocks 0..3, A blocks 1..7.
+template <class OA, class OB>
+__device__ __forceinline__ void load_next_one(int q, FragA &fa, FragB &fb, const lds_t *stage,
+                                              int wm, int wn, int lane) {
+  if (q == 0)
+    fa.a[0] = OA::frag(stage, wm * 128, lane);
+  else if (q < 5)
+    fb.b[q - 1] = OB::frag(stage + kOperandStageBytes, wn * 128 + (q - 1) * 16, lane);
+  else
+    fa.a[q - 4] = OA::frag(stage, wm * 128 + (q - 4) * 16, lane);
 }
 
 template <class OA, class OB>
-__device__ __forceinline__ void load_frags(Frags &f, const lds_t *stage, int ks, int wm, int wn,
-                                           int lane) {
+__device__ __forceinline__ void load_next(FragA &fa, FragB &fb, const lds_t *stage, int wm,
+                                          int wn, int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = OA::frag(stage, wm * 128 + i * 32, ks, lane);
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    f.b[j] = OB::frag(stage + kOperandStageBytes, wn * 128 + j * 32, ks, lane);
+  for (int q = 0; q < 12; ++q) load_next_one<OA, OB>(q, fa, fb, stage, wm, wn, lane);
 }
 
-__device__ __forceinline__ void mma(const Frags &f, Acc &acc) {
+// B block 4 + j of a stage.
+template <class OB>
+__device__ __forceinline__ void load_bhi_one(int j, FragB &fb, const lds_t *stage, int wn,
+                                             int lane) {
+  fb.b[j] = OB::frag(stage + kOperandStageBytes, wn * 128 + 64 + j * 16, lane);
+}
+
+// acc[mb][4 h + j] += A_mb B_(4 h + j) for the 32 blocks of half h.
+template <int H>
+__device__ __forceinline__ void mma_half(const FragA &fa, const FragB &fb, Acc &acc) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc.v[i][j], 0, 0, 0);
+    for (int j = 0; j < 4; ++j) acc.v[i][4 * H + j] = mfma16(fa.a[i], fb.b[j], acc.v[i][4 * H + j]);
 }
 
 // Issues the first kStages-1 stages of a tile's K loop (after a barrier that
@@ -332,45 +389,104 @@ __device__ __forceinline__ void pipe_prologue(const OA &A, const OB &B, lds_t *s
   }
 }
 
-// acc += A_tile * B_tile^T over nk >= 1 K-steps of 32, with the prologue
+// One K step kt that is not the last, scheduled by hand in groups of four
+// MFMAs (A block g against four B blocks); no instruction crosses a group
+// boundary, so the memory work below stays spread over the matrix work:
+//  * first half (B blocks 0..3): groups 0..3 each read one of B blocks 4..7
+//    of this stage;
+//  * publish stage kt+1: wait for own loads, barrier;
+//  * second half (B blocks 4..7): group g issues load g of stage kt+3 (A for
+//    g < 4, B after) and groups 0..5 read two fragments each of stage kt+1
+//    into `nxt` and `blo`.
+//
+// The barrier carries no memory fence of its own: the wait just before it
+// covers what it must order (stage kt+1's own loads landed, the reads of
+// stage kt-1, whose slot the loads issued after it overwrite, returned), and
+// it leaves the newest fragment reads in flight.
+template <class OA, class OB>
+__device__ __forceinline__ void pipe_step(const OA &A, const OB &B, int kt, lds_t *smem,
+                                          Acc &acc, const FragA &cur, FragA &nxt, FragB &blo,
+                                          FragB &bhi, int wave, int lane) {
+  const int wm = wave >> 1, wn = wave & 1;
+  const lds_t *cst = smem + (kt & (kStages - 1)) * kStageBytes;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc.v[g][j] = mfma16(cur.a[g], blo.b[j], acc.v[g][j]);
+    if (g < 4) load_bhi_one<OB>(g, bhi, cst, wn, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Own loads of stage kt+1 landed (kt+2 may be in flight), and every LDS read
+  // older than this half's own (all reads of stage kt-1 among them) returned;
+  // LDS reads complete in order.
+  wait_vm_lgkm<8, 4 * OB::kReads>();
+  __builtin_amdgcn_s_barrier();  // ... and everyone's; everyone is done with stage kt-1
+  __builtin_amdgcn_sched_barrier(0);
+  lds_t *st = smem + ((kt + 3) & (kStages - 1)) * kStageBytes;
+  const DmaSlice da = A.prep((kt + 3) * kBK);
+  const DmaSlice db = B.prep((kt + 3) * kBK);
+  const lds_t *nst = smem + ((kt + 1) & (kStages - 1)) * kStageBytes;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc.v[g][4 + j] = mfma16(cur.a[g], bhi.b[j], acc.v[g][4 + j]);
+    if (g < 4)
+      A.issue_one(da, st, g, wave);
+    else
+      B.issue_one(db, st + kOperandStageBytes, g - 4, wave);
+    if (g < 6) {
+      load_next_one<OA, OB>(2 * g, nxt, blo, nst, wm, wn, lane);
+      load_next_one<OA, OB>(2 * g + 1, nxt, blo, nst, wm, wn, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The last K step: no further stage to publish or load.
+template <class OB>
+__device__ __forceinline__ void pipe_last(int kt, lds_t *smem, Acc &acc, const FragA &cur,
+                                          FragB &blo, FragB &bhi, int wave, int lane) {
+  const int wn = wave & 1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) load_bhi_one<OB>(j, bhi, smem + (kt & (kStages - 1)) * kStageBytes, wn, lane);
+  mma_half<0>(cur, blo, acc);
+  mma_half<1>(cur, bhi, acc);
+}
+
+// acc += A_tile * B_tile^T over nk >= 1 K steps of 32, with the prologue
 // already issued and its loads the only vector-memory operations in flight.
-// Each step: MFMAs of the first 16-wide half (the second half's fragments
-// loading in between), publish the next stage (wait for own loads, barrier),
-// issue the stage three ahead, MFMAs of the second half (the next stage's
-// first fragments and the new loads in between).  The last step is peeled so
-// that the loop body has no branch.  Ends with all loads landed and a barrier,
-// so the caller may reuse the LDS ring afterwards.
+// The loop runs two steps per iteration so that the two A fragment sets swap
+// roles without register copies.  The step count is rounded up to an even
+// number, at least 4: the extra steps read stages past the end of K, which
+// the loads zero-fill, and add exact zeros.  The first two steps run before
+// the loop, so that every value the loop carries comes out of an MFMA: equal
+// starting values (all zeros) entering the loop would be merged into one
+// register, and the accumulators shuffled between registers on every pass.
+// Ends with all loads landed and a barrier, so the caller may reuse the LDS
+// ring afterwards.
 template <class OA, class OB>
 __device__ __forceinline__ void pipe_run(const OA &A, const OB &B, int nk, lds_t *smem, Acc &acc,
                                          int wave, int lane) {
-  constexpr int kReads = OA::kReads * 4 + OB::kReads * 4;  // LDS reads per half step
   const int wm = wave >> 1, wn = wave & 1;
+  const int n2 = nk <= 4 ? 4 : (nk + 1) & ~1;
   wait_vmcnt<16>();  // own loads of stage 0 landed; stages 1 and 2 may be in flight
   __syncthreads();
-  Frags f0, f1;
-  load_frags<OA, OB>(f0, smem, 0, wm, wn, lane);
-  for (int kt = 0; kt < nk - 1; ++kt) {
-    const lds_t *cur = smem + (kt & (kStages - 1)) * kStageBytes;
-    load_frags<OA, OB>(f1, cur, 1, wm, wn, lane);
-    mma(f0, acc);
-    interleave<kReads, 0>();
-    wait_vmcnt<8>();  // own loads of stage kt+1 landed (kt+2 may be in flight)
-    __syncthreads();  // ... and everyone's; everyone is done with stage kt-1
-    lds_t *st = smem + ((kt + 3) & (kStages - 1)) * kStageBytes;
-    A.issue(st, (kt + 3) * kBK, wave);
-    B.issue(st + kOperandStageBytes, (kt + 3) * kBK, wave);
-    load_frags<OA, OB>(f0, smem + ((kt + 1) & (kStages - 1)) * kStageBytes, 0, wm, wn, lane);
-    mma(f1, acc);
-    interleave<kReads, 8>();
+  FragA f0, f1;
+  FragB blo, bhi;
+  load_next<OA, OB>(f0, blo, smem, wm, wn, lane);
+  pipe_step(A, B, 0, smem, acc, f0, f1, blo, bhi, wave, lane);
+  pipe_step(A, B, 1, smem, acc, f1, f0, blo, bhi, wave, lane);
+  for (int kt = 2; kt < n2 - 2; kt += 2) {
+    pipe_step(A, B, kt, smem, acc, f0, f1, blo, bhi, wave, lane);
+    pipe_step(A, B, kt + 1, smem, acc, f1, f0, blo, bhi, wave, lane);
   }
-  load_frags<OA, OB>(f1, smem + ((nk - 1) & (kStages - 1)) * kStageBytes, 1, wm, wn, lane);
-  mma(f0, acc);
-  mma(f1, acc);
+  pipe_step(A, B, n2 - 2, smem, acc, f0, f1, blo, bhi, wave, lane);
+  pipe_last<OB>(n2 - 1, smem, acc, f1, blo, bhi, wave, lane);
   wait_vmcnt<0>();  // loads past the end still write LDS: let them land
   __syncthreads();
 }
 
-// acc += A_tile * B_tile^T over nk K-steps of 32.  Starts and ends with a
+// acc += A_tile * B_tile^T over nk K steps of 32.  Starts and ends with a
 // barrier, so the caller may use the LDS area before and after.
 template <class OA, class OB>
 __device__ __forceinline__ void tile_mainloop(const OA &A, const OB &B, int nk, lds_t *smem,
