@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(kThreads)
 
   OperandK B;
   B.init(p.hidden + (size_t)t0 * p.D, p.D, min(kTile, p.T - t0), p.D, wave, lane);
-  const int nk = (p.D + kBK - 1) / kBK;
+  const int nk = (p.D + kKS - 1) / kKS;
 
   int lab[8];
   float mrun[8], srun[8], zl[8];
@@ -351,7 +351,7 @@ __global__ void __launch_bounds__(kThreads)
     OperandK A, B;
     A.init(p.weight + (size_t)v0 * p.D, p.D, min(kTile, p.V - v0), p.D, wave, lane);
     B.init(p.hidden + (size_t)t0 * p.D, p.D, min(kTile, p.T - t0), p.D, wave, lane);
-    tile_mainloop(A, B, (p.D + kBK - 1) / kBK, smem, acc, wave, lane);
+    tile_mainloop(A, B, (p.D + kKS - 1) / kKS, smem, acc, wave, lane);
   }
 
 #pragma unroll
@@ -478,7 +478,7 @@ __global__ void __launch_bounds__(kThreads)
          min(kend, p.vcount) - kbeg, wave, lane);
   Acc acc;
   acc.zero();
-  tile_mainloop(A, B, (kend - kbeg + kBK - 1) / kBK, smem, acc, wave, lane);
+  tile_mainloop(A, B, (kend - kbeg + kKS - 1) / kKS, smem, acc, wave, lane);
 
   // rows [tm*256, tm*256 + 256) of split s, all inside the R x D slice
   const float *tile = p.acc + ((size_t)s * p.R + (size_t)tm * kTile) * p.D;
@@ -516,7 +516,7 @@ __global__ void __launch_bounds__(kThreads)
   B.init(p.hidden + (size_t)p.rb0 * p.D + h0, p.D, min(kTile, p.D - h0), p.rcount, wave, lane);
   Acc acc;
   acc.zero();
-  tile_mainloop(A, B, (p.rcount + kBK - 1) / kBK, smem, acc, wave, lane);
+  tile_mainloop(A, B, (p.rcount + kKS - 1) / kKS, smem, acc, wave, lane);
 
   // rows [v0, min(V, v0 + 256)) of dW
   const uint32_t rows = (uint32_t)min(kTile, p.V - v0);

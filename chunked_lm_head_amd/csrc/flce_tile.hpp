@@ -53,10 +53,11 @@ typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) f32x2 lds_f32x2;
 
 constexpr int kTile = 256;                                   // macro tile (rows = cols)
-constexpr int kBK = 32;                                      // K per pipeline stage
-constexpr int kStages = 4;                                   // LDS ring depth
+constexpr int kKS = 32;                                      // K per MFMA step
+constexpr int kBK = 64;                                      // K per pipeline stage (2 steps)
+constexpr int kStages = 2;                                   // LDS ring depth
 constexpr int kThreads = 256;                                // 4 wave64s
-constexpr int kOperandStageBytes = kTile * kBK * 2;          // 16 KiB
+constexpr int kOperandStageBytes = kTile * kBK * 2;          // 32 KiB
 constexpr int kStageBytes = 2 * kOperandStageBytes;          // A + B
 constexpr int kPipeBytes = kStages * kStageBytes;            // 128 KiB
 constexpr uint32_t kOOB = 0x80000000u;                       // offset past every descriptor
@@ -155,13 +156,13 @@ __device__ __forceinline__ void grouped_tile(int L, int tiles_m, int tiles_n, in
 // Operands.  Each wave issues 4 DMA instructions per operand per stage.
 // ---------------------------------------------------------------------------
 
-// Chunk swizzle of the K-major LDS layout (rows of four 16-byte chunks): a
-// fragment read takes chunk c of 16 consecutive rows in each 16-lane group;
-// folding row bits 1 and 2 into the chunk index spreads them over all banks
-// (measured conflict-free with the LDS bank-conflict counter at every 1 KiB
-// offset of the ring, where folding bits 2 and 3 costs four extra cycles per
-// read).
-__device__ __forceinline__ int k_swizzle(int r) { return (r >> 1) & 3; }
+// Chunk swizzle of the K-major LDS layout (rows of eight 16-byte chunks, one
+// 128-byte line of global memory each): a fragment read takes chunk c of 16
+// consecutive rows in each 16-lane group; folding the low three row bits into
+// the chunk index spreads them over all banks (measured conflict-free with
+// the LDS bank-conflict counter at every 2 KiB offset, for both K halves of a
+// stage, where an unswizzled layout costs twelve extra cycles per read).
+__device__ __forceinline__ int k_swizzle(int r) { return r & 7; }
 
 // One stage's K slice of an operand: its buffer descriptor (scalar), first k,
 // and whether the whole slice lies inside the valid K extent.
@@ -172,13 +173,15 @@ struct DmaSlice {
 };
 
 // Row-major [mn][k]: element (r, k) at byte (r * ld + k) * 2 from base.
+// A stage holds 256 rows of 64 k (128 bytes); each wave loads 64 rows, one
+// full row per 8 lanes, in 8 loads of 8 rows.
 struct OperandK {
   static constexpr int kReads = 1;  // LDS reads per MFMA fragment
   const char *base;  // tile origin (row 0, k 0)
   uint32_t nbytes;   // valid bytes from base
   int kext;          // valid K extent (multiple of 8)
-  uint32_t voff[4];  // per lane: row/chunk offset within a stage, kOOB for rows past the tile
-  int kc[4];         // per lane: k offset of its chunk within a stage
+  int kc;            // per lane: k offset of its chunk within a stage (the same in every load)
+  uint32_t voff[8];  // per lane and load: row/chunk offset, kOOB for rows past the tile
 
   __device__ __forceinline__ void init(const uint16_t *base_, int ld, int rows, int kext_,
                                        int wave, int lane) {
@@ -186,11 +189,12 @@ struct OperandK {
     rows = rows < 0 ? 0 : rows;
     kext = kext_ < 0 ? 0 : kext_;
     nbytes = (rows > 0 && kext > 0) ? (uint32_t)((rows - 1) * ld + kext) * 2u : 0u;
+    // rows of one load start at a multiple of 8, so the swizzle is lane-only
+    const int c = (lane & 7) ^ k_swizzle(lane >> 3);
+    kc = c * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wave * 64 + i * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ k_swizzle(r);
-      kc[i] = c * 8;
+    for (int i = 0; i < 8; ++i) {
+      const int r = wave * 64 + i * 8 + (lane >> 3);
       voff[i] = r < rows ? (uint32_t)(r * ld + c * 8) * 2u : kOOB;
     }
   }
@@ -200,22 +204,22 @@ struct OperandK {
     const uint32_t adv = (uint32_t)k0 * 2u;
     return DmaSlice{rsrc_words(base + adv, remaining(nbytes, adv)), k0, k0 + kBK <= kext};
   }
-  // Load i (0..3) of this wave's share of a stage.
+  // Load i (0..7) of this wave's share of a stage.
   __device__ __forceinline__ void issue_one(const DmaSlice &d, lds_t *stage, int i,
                                             int wave) const {
-    const uint32_t off = (d.full || d.k0 + kc[i] < kext) ? voff[i] : kOOB;
-    dma16(d.rs, off, stage + (wave * 64 + i * 16) * (kBK * 2));
+    const uint32_t off = (d.full || d.k0 + kc < kext) ? voff[i] : kOOB;
+    dma16(d.rs, off, stage + (wave * 64 + i * 8) * (kBK * 2));
   }
   __device__ __forceinline__ void issue(lds_t *stage, int k0, int wave) const {
     const DmaSlice d = prep(k0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) issue_one(d, stage, i, wave);
+    for (int i = 0; i < 8; ++i) issue_one(d, stage, i, wave);
   }
 
-  // Rows row0 .. row0+15 (one per lane % 16), k = 8 (lane / 16) .. +7.
-  __device__ __forceinline__ static bf16x8 frag(const lds_t *stage, int row0, int lane) {
+  // Rows row0 .. row0+15 (one per lane % 16), k = 32 kk + 8 (lane / 16) .. +7.
+  __device__ __forceinline__ static bf16x8 frag(const lds_t *stage, int row0, int kk, int lane) {
     const int r = row0 + (lane & 15);
-    const int c = lane >> 4;
+    const int c = 4 * kk + (lane >> 4);
     const int phys = c ^ k_swizzle(r);
     return *(const lds_bf16x8 *)(stage + r * (kBK * 2) + phys * 16);
   }
@@ -228,14 +232,16 @@ struct OperandK {
 __device__ __forceinline__ int mn_swizzle(int k) { return 4 * (k & 3) + 2 * ((k >> 3) & 1); }
 
 // Row-major [k][mn]: element (c, k) at byte (k * ld + c) * 2 from base.
+// A stage holds 64 k rows of 256 columns (512 bytes); each wave loads 16 of
+// them, two per load.
 struct OperandMN {
   static constexpr int kReads = 2;  // LDS reads per MFMA fragment
   const char *base;   // tile origin (k 0, column 0)
   uint32_t nbytes;    // valid bytes from base
   uint32_t row_bytes; // ld * 2
   int kext;           // valid K extent
-  uint32_t voff[4];   // per lane: k-row/chunk offset within a stage, kOOB past the columns
-  int kr[4];          // per lane: k row of its chunk within a stage
+  int kr0;            // per lane: k row of its chunk in load 0 (load i: kr0 + 2 i)
+  uint32_t voff[8];   // per lane and load: k-row/chunk offset, kOOB past the columns
 
   __device__ __forceinline__ void init(const uint16_t *base_, int ld, int cols, int kext_,
                                        int wave, int lane) {
@@ -244,11 +250,11 @@ struct OperandMN {
     kext = kext_ < 0 ? 0 : kext_;
     row_bytes = (uint32_t)ld * 2u;
     nbytes = (cols > 0 && kext > 0) ? (uint32_t)((kext - 1) * ld + cols) * 2u : 0u;
+    kr0 = wave * 16 + (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = wave * 8 + i * 2 + (lane >> 5);
+    for (int i = 0; i < 8; ++i) {
+      const int k = kr0 + 2 * i;
       const int c = (lane & 31) ^ mn_swizzle(k);
-      kr[i] = k;
       voff[i] = c * 8 < cols ? (uint32_t)(k * ld + c * 8) * 2u : kOOB;
     }
   }
@@ -258,30 +264,30 @@ struct OperandMN {
     const uint32_t adv = (uint32_t)k0 * row_bytes;
     return DmaSlice{rsrc_words(base + adv, remaining(nbytes, adv)), k0, k0 + kBK <= kext};
   }
-  // Load i (0..3) of this wave's share of a stage.
+  // Load i (0..7) of this wave's share of a stage.
   __device__ __forceinline__ void issue_one(const DmaSlice &d, lds_t *stage, int i,
                                             int wave) const {
-    const uint32_t off = (d.full || d.k0 + kr[i] < kext) ? voff[i] : kOOB;
-    dma16(d.rs, off, stage + (wave * 8 + i * 2) * (kTile * 2));
+    const uint32_t off = (d.full || d.k0 + kr0 + 2 * i < kext) ? voff[i] : kOOB;
+    dma16(d.rs, off, stage + (wave * 16 + i * 2) * (kTile * 2));
   }
   __device__ __forceinline__ void issue(lds_t *stage, int k0, int wave) const {
     const DmaSlice d = prep(k0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) issue_one(d, stage, i, wave);
+    for (int i = 0; i < 8; ++i) issue_one(d, stage, i, wave);
   }
 
-  // Columns mn0 .. mn0+15 (one per lane % 16), k = 8 (lane / 16) .. +7.  Lane
-  // j of a 16-lane group addresses 4 columns mn0 + 4 (j % 4) .. +3 of k row
-  // 8 g + 4 half + j / 4; the transpose hands lane i column mn0 + i of the
-  // four k rows.
-  __device__ __forceinline__ static bf16x8 frag(const lds_t *stage, int mn0, int lane) {
+  // Columns mn0 .. mn0+15 (one per lane % 16), k = 32 kk + 8 (lane / 16) ..
+  // +7.  Lane j of a 16-lane group addresses 4 columns mn0 + 4 (j % 4) .. +3
+  // of k row 32 kk + 8 g + 4 half + j / 4; the transpose hands lane i column
+  // mn0 + i of the four k rows.
+  __device__ __forceinline__ static bf16x8 frag(const lds_t *stage, int mn0, int kk, int lane) {
     const int g = lane >> 4, j = lane & 15;
     const int c = (mn0 >> 3) + ((j & 3) >> 1);
     const int sub = 8 * (j & 1);
     s16x4 h[2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int k = 8 * g + 4 * half + (j >> 2);
+      const int k = 32 * kk + 8 * g + 4 * half + (j >> 2);
       const int phys = c ^ mn_swizzle(k);
       h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4 *)(stage + k * (kTile * 2) + phys * 16 + sub));
@@ -340,31 +346,31 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Fragment q (0..11) of a stage in the order the first half step consumes
-// them: A block 0, B blocks 0..3, A blocks 1..7.
+// Fragment q (0..11) of K step kk of a stage, in the order the first half
+// step consumes them: A block 0, B blocks 0..3, A blocks 1..7.
 template <class OA, class OB>
 __device__ __forceinline__ void load_next_one(int q, FragA &fa, FragB &fb, const lds_t *stage,
-                                              int wm, int wn, int lane) {
+                                              int kk, int wm, int wn, int lane) {
   if (q == 0)
-    fa.a[0] = OA::frag(stage, wm * 128, lane);
+    fa.a[0] = OA::frag(stage, wm * 128, kk, lane);
   else if (q < 5)
-    fb.b[q - 1] = OB::frag(stage + kOperandStageBytes, wn * 128 + (q - 1) * 16, lane);
+    fb.b[q - 1] = OB::frag(stage + kOperandStageBytes, wn * 128 + (q - 1) * 16, kk, lane);
   else
-    fa.a[q - 4] = OA::frag(stage, wm * 128 + (q - 4) * 16, lane);
+    fa.a[q - 4] = OA::frag(stage, wm * 128 + (q - 4) * 16, kk, lane);
 }
 
 template <class OA, class OB>
-__device__ __forceinline__ void load_next(FragA &fa, FragB &fb, const lds_t *stage, int wm,
-                                          int wn, int lane) {
+__device__ __forceinline__ void load_next(FragA &fa, FragB &fb, const lds_t *stage, int kk,
+                                          int wm, int wn, int lane) {
 #pragma unroll
-  for (int q = 0; q < 12; ++q) load_next_one<OA, OB>(q, fa, fb, stage, wm, wn, lane);
+  for (int q = 0; q < 12; ++q) load_next_one<OA, OB>(q, fa, fb, stage, kk, wm, wn, lane);
 }
 
-// B block 4 + j of a stage.
+// B block 4 + j of K step kk of a stage.
 template <class OB>
-__device__ __forceinline__ void load_bhi_one(int j, FragB &fb, const lds_t *stage, int wn,
-                                             int lane) {
-  fb.b[j] = OB::frag(stage + kOperandStageBytes, wn * 128 + 64 + j * 16, lane);
+__device__ __forceinline__ void load_bhi_one(int j, FragB &fb, const lds_t *stage, int kk,
+                                             int wn, int lane) {
+  fb.b[j] = OB::frag(stage + kOperandStageBytes, wn * 128 + 64 + j * 16, kk, lane);
 }
 
 // acc[mb][4 h + j] += A_mb B_(4 h + j) for the 32 blocks of half h.
@@ -376,67 +382,76 @@ __device__ __forceinline__ void mma_half(const FragA &fa, const FragB &fb, Acc &
     for (int j = 0; j < 4; ++j) acc.v[i][4 * H + j] = mfma16(fa.a[i], fb.b[j], acc.v[i][4 * H + j]);
 }
 
-// Issues the first kStages-1 stages of a tile's K loop (after a barrier that
-// frees the LDS ring, with no other vector-memory operation in flight).
-// Stages past the end of K are issued too, as loads from an empty range that
-// zero-fill ring slots nobody reads; the counts in pipe_run rely on it.
+// Issues both stages of a tile's K loop (after a barrier that frees the LDS
+// ring, with no other vector-memory operation in flight).  Stages past the
+// end of K are issued too, as loads from an empty range that zero-fill ring
+// slots; the counts in pipe_run rely on it.
 template <class OA, class OB>
 __device__ __forceinline__ void pipe_prologue(const OA &A, const OB &B, lds_t *smem, int wave) {
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) {
+  for (int s = 0; s < kStages; ++s) {
     A.issue(smem + s * kStageBytes, s * kBK, wave);
     B.issue(smem + s * kStageBytes + kOperandStageBytes, s * kBK, wave);
   }
 }
 
-// One K step kt that is not the last, scheduled by hand in groups of four
-// MFMAs (A block g against four B blocks); no instruction crosses a group
-// boundary, so the memory work below stays spread over the matrix work:
+__device__ __forceinline__ lds_t *stage_of(lds_t *smem, int kt) {
+  return smem + ((kt >> 1) & (kStages - 1)) * kStageBytes;
+}
+
+// One K step kt (32 wide) that is not the last, scheduled by hand in groups
+// of four MFMAs (A block g against four B blocks); no instruction crosses a
+// group boundary, so the memory work stays spread over the matrix work:
 //  * first half (B blocks 0..3): groups 0..3 each read one of B blocks 4..7
-//    of this stage;
-//  * publish stage kt+1: wait for own loads, barrier;
-//  * second half (B blocks 4..7): group g issues load g of stage kt+3 (A for
-//    g < 4, B after) and groups 0..5 read two fragments each of stage kt+1
-//    into `nxt` and `blo`.
+//    of this step;
+//  * on the second step of a stage only (kPublish): wait until the next
+//    stage has landed, barrier, and refill this stage's slot with the stage
+//    after next over the second half, two loads per group;
+//  * second half (B blocks 4..7): groups 0..5 read two fragments each of
+//    step kt+1 into `nxt` and `blo`.
+// The ring holds the stage being multiplied and the next one, so each
+// barrier covers a stage (two K steps) while every load has two K steps to
+// land.
 //
 // The barrier carries no memory fence of its own: the wait just before it
-// covers what it must order (stage kt+1's own loads landed, the reads of
-// stage kt-1, whose slot the loads issued after it overwrite, returned), and
-// it leaves the newest fragment reads in flight.
-template <class OA, class OB>
+// covers what it must order (the next stage's loads landed, every read of
+// this stage, whose slot the loads issued after it overwrite, returned).
+template <bool kPublish, class OA, class OB>
 __device__ __forceinline__ void pipe_step(const OA &A, const OB &B, int kt, lds_t *smem,
                                           Acc &acc, const FragA &cur, FragA &nxt, FragB &blo,
                                           FragB &bhi, int wave, int lane) {
   const int wm = wave >> 1, wn = wave & 1;
-  const lds_t *cst = smem + (kt & (kStages - 1)) * kStageBytes;
+  lds_t *cst = stage_of(smem, kt);
 #pragma unroll
   for (int g = 0; g < 8; ++g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc.v[g][j] = mfma16(cur.a[g], blo.b[j], acc.v[g][j]);
-    if (g < 4) load_bhi_one<OB>(g, bhi, cst, wn, lane);
+    if (g < 4) load_bhi_one<OB>(g, bhi, cst, kt & 1, wn, lane);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // Own loads of stage kt+1 landed (kt+2 may be in flight), and every LDS read
-  // older than this half's own (all reads of stage kt-1 among them) returned;
-  // LDS reads complete in order.
-  wait_vm_lgkm<8, 4 * OB::kReads>();
-  __builtin_amdgcn_s_barrier();  // ... and everyone's; everyone is done with stage kt-1
-  __builtin_amdgcn_sched_barrier(0);
-  lds_t *st = smem + ((kt + 3) & (kStages - 1)) * kStageBytes;
-  const DmaSlice da = A.prep((kt + 3) * kBK);
-  const DmaSlice db = B.prep((kt + 3) * kBK);
-  const lds_t *nst = smem + ((kt + 1) & (kStages - 1)) * kStageBytes;
+  DmaSlice da, db;
+  if constexpr (kPublish) {
+    // All loads landed (nothing newer is in flight) and every LDS read of this
+    // wave returned, the B block reads of this step among them.
+    wait_vm_lgkm<0, 0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const int k0 = ((kt >> 1) + kStages) * kBK;
+    da = A.prep(k0);
+    db = B.prep(k0);
+  }
+  const lds_t *nst = stage_of(smem, kt + 1);
 #pragma unroll
   for (int g = 0; g < 8; ++g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc.v[g][4 + j] = mfma16(cur.a[g], bhi.b[j], acc.v[g][4 + j]);
-    if (g < 4)
-      A.issue_one(da, st, g, wave);
-    else
-      B.issue_one(db, st + kOperandStageBytes, g - 4, wave);
+    if constexpr (kPublish) {
+      A.issue_one(da, cst, g, wave);
+      B.issue_one(db, cst + kOperandStageBytes, g, wave);
+    }
     if (g < 6) {
-      load_next_one<OA, OB>(2 * g, nxt, blo, nst, wm, wn, lane);
-      load_next_one<OA, OB>(2 * g + 1, nxt, blo, nst, wm, wn, lane);
+      load_next_one<OA, OB>(2 * g, nxt, blo, nst, (kt + 1) & 1, wm, wn, lane);
+      load_next_one<OA, OB>(2 * g + 1, nxt, blo, nst, (kt + 1) & 1, wm, wn, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -448,39 +463,39 @@ __device__ __forceinline__ void pipe_last(int kt, lds_t *smem, Acc &acc, const F
                                           FragB &blo, FragB &bhi, int wave, int lane) {
   const int wn = wave & 1;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) load_bhi_one<OB>(j, bhi, smem + (kt & (kStages - 1)) * kStageBytes, wn, lane);
+  for (int j = 0; j < 4; ++j) load_bhi_one<OB>(j, bhi, stage_of(smem, kt), kt & 1, wn, lane);
   mma_half<0>(cur, blo, acc);
   mma_half<1>(cur, bhi, acc);
 }
 
 // acc += A_tile * B_tile^T over nk >= 1 K steps of 32, with the prologue
 // already issued and its loads the only vector-memory operations in flight.
-// The loop runs two steps per iteration so that the two A fragment sets swap
-// roles without register copies.  The step count is rounded up to an even
-// number, at least 4: the extra steps read stages past the end of K, which
-// the loads zero-fill, and add exact zeros.  The first two steps run before
-// the loop, so that every value the loop carries comes out of an MFMA: equal
-// starting values (all zeros) entering the loop would be merged into one
-// register, and the accumulators shuffled between registers on every pass.
-// Ends with all loads landed and a barrier, so the caller may reuse the LDS
-// ring afterwards.
+// The loop runs one stage (two steps, the second publishing) per iteration,
+// so that the two A fragment sets swap roles without register copies.  The
+// step count is rounded up to whole stages, at least 2: the extra steps read
+// k past the end, which the loads zero-fill, and add exact zeros.  The first
+// stage runs before the loop, so that every value the loop carries comes out
+// of an MFMA: equal starting values (all zeros) entering the loop would be
+// merged into one register, and the accumulators shuffled between registers
+// on every pass.  Ends with all loads landed and a barrier, so the caller may
+// reuse the LDS ring afterwards.
 template <class OA, class OB>
 __device__ __forceinline__ void pipe_run(const OA &A, const OB &B, int nk, lds_t *smem, Acc &acc,
                                          int wave, int lane) {
   const int wm = wave >> 1, wn = wave & 1;
   const int n2 = nk <= 4 ? 4 : (nk + 1) & ~1;
-  wait_vmcnt<16>();  // own loads of stage 0 landed; stages 1 and 2 may be in flight
+  wait_vmcnt<8 + 8>();  // own loads of stage 0 landed; stage 1's 16 may be in flight
   __syncthreads();
   FragA f0, f1;
   FragB blo, bhi;
-  load_next<OA, OB>(f0, blo, smem, wm, wn, lane);
-  pipe_step(A, B, 0, smem, acc, f0, f1, blo, bhi, wave, lane);
-  pipe_step(A, B, 1, smem, acc, f1, f0, blo, bhi, wave, lane);
+  load_next<OA, OB>(f0, blo, smem, 0, wm, wn, lane);
+  pipe_step<false>(A, B, 0, smem, acc, f0, f1, blo, bhi, wave, lane);
+  pipe_step<true>(A, B, 1, smem, acc, f1, f0, blo, bhi, wave, lane);
   for (int kt = 2; kt < n2 - 2; kt += 2) {
-    pipe_step(A, B, kt, smem, acc, f0, f1, blo, bhi, wave, lane);
-    pipe_step(A, B, kt + 1, smem, acc, f1, f0, blo, bhi, wave, lane);
+    pipe_step<false>(A, B, kt, smem, acc, f0, f1, blo, bhi, wave, lane);
+    pipe_step<true>(A, B, kt + 1, smem, acc, f1, f0, blo, bhi, wave, lane);
   }
-  pipe_step(A, B, n2 - 2, smem, acc, f0, f1, blo, bhi, wave, lane);
+  pipe_step<false>(A, B, n2 - 2, smem, acc, f0, f1, blo, bhi, wave, lane);
   pipe_last<OB>(n2 - 1, smem, acc, f1, blo, bhi, wave, lane);
   wait_vmcnt<0>();  // loads past the end still write LDS: let them land
   __syncthreads();
