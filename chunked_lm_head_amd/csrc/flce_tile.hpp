@@ -399,38 +399,49 @@ __device__ __forceinline__ lds_t *stage_of(lds_t *smem, int kt) {
   return smem + ((kt >> 1) & (kStages - 1)) * kStageBytes;
 }
 
+// How a K step takes part in refilling the ring.
+enum StepLoads {
+  kNoLoads,   // first step of a tile: the prologue filled both slots
+  kPublish,   // second step of a stage: barrier, then the first 8 loads of the refill
+  kFinish,    // first step of a later stage: the last 8 loads of the refill
+};
+
 // One K step kt (32 wide) that is not the last, scheduled by hand in groups
 // of four MFMAs (A block g against four B blocks); no instruction crosses a
 // group boundary, so the memory work stays spread over the matrix work:
 //  * first half (B blocks 0..3): groups 0..3 each read one of B blocks 4..7
-//    of this step;
-//  * on the second step of a stage only (kPublish): wait until the next
-//    stage has landed, barrier, and refill this stage's slot with the stage
-//    after next over the second half, two loads per group;
+//    of this step; on kFinish steps each group also issues one load (B);
+//  * on kPublish steps: wait until the next stage has landed, barrier; this
+//    stage's slot is then refilled with the stage after next, one load (A)
+//    per group of the second half and one per group of the next step's
+//    first half, so that the load unit (about 64 bytes per clock per CU,
+//    half of which a full-rate stage needs) is never handed a burst;
 //  * second half (B blocks 4..7): groups 0..5 read two fragments each of
 //    step kt+1 into `nxt` and `blo`.
 // The ring holds the stage being multiplied and the next one, so each
-// barrier covers a stage (two K steps) while every load has two K steps to
-// land.
+// barrier covers a stage (two K steps); the last load of a refill still has
+// a full K step to land.
 //
 // The barrier carries no memory fence of its own: the wait just before it
 // covers what it must order (the next stage's loads landed, every read of
 // this stage, whose slot the loads issued after it overwrite, returned).
-template <bool kPublish, class OA, class OB>
+template <StepLoads kLoads, class OA, class OB>
 __device__ __forceinline__ void pipe_step(const OA &A, const OB &B, int kt, lds_t *smem,
                                           Acc &acc, const FragA &cur, FragA &nxt, FragB &blo,
-                                          FragB &bhi, int wave, int lane) {
+                                          FragB &bhi, DmaSlice &da, DmaSlice &db, int wave,
+                                          int lane) {
   const int wm = wave >> 1, wn = wave & 1;
   lds_t *cst = stage_of(smem, kt);
+  lds_t *fill = stage_of(smem, kt - 1);  // the slot a kFinish step refills
 #pragma unroll
   for (int g = 0; g < 8; ++g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc.v[g][j] = mfma16(cur.a[g], blo.b[j], acc.v[g][j]);
     if (g < 4) load_bhi_one<OB>(g, bhi, cst, kt & 1, wn, lane);
+    if constexpr (kLoads == kFinish) B.issue_one(db, fill + kOperandStageBytes, g, wave);
     __builtin_amdgcn_sched_barrier(0);
   }
-  DmaSlice da, db;
-  if constexpr (kPublish) {
+  if constexpr (kLoads == kPublish) {
     // All loads landed (nothing newer is in flight) and every LDS read of this
     // wave returned, the B block reads of this step among them.
     wait_vm_lgkm<0, 0>();
@@ -445,10 +456,7 @@ __device__ __forceinline__ void pipe_step(const OA &A, const OB &B, int kt, lds_
   for (int g = 0; g < 8; ++g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc.v[g][4 + j] = mfma16(cur.a[g], bhi.b[j], acc.v[g][4 + j]);
-    if constexpr (kPublish) {
-      A.issue_one(da, cst, g, wave);
-      B.issue_one(db, cst + kOperandStageBytes, g, wave);
-    }
+    if constexpr (kLoads == kPublish) A.issue_one(da, cst, g, wave);
     if (g < 6) {
       load_next_one<OA, OB>(2 * g, nxt, blo, nst, (kt + 1) & 1, wm, wn, lane);
       load_next_one<OA, OB>(2 * g + 1, nxt, blo, nst, (kt + 1) & 1, wm, wn, lane);
@@ -488,14 +496,15 @@ __device__ __forceinline__ void pipe_run(const OA &A, const OB &B, int nk, lds_t
   __syncthreads();
   FragA f0, f1;
   FragB blo, bhi;
+  DmaSlice da, db;
   load_next<OA, OB>(f0, blo, smem, 0, wm, wn, lane);
-  pipe_step<false>(A, B, 0, smem, acc, f0, f1, blo, bhi, wave, lane);
-  pipe_step<true>(A, B, 1, smem, acc, f1, f0, blo, bhi, wave, lane);
+  pipe_step<kNoLoads>(A, B, 0, smem, acc, f0, f1, blo, bhi, da, db, wave, lane);
+  pipe_step<kPublish>(A, B, 1, smem, acc, f1, f0, blo, bhi, da, db, wave, lane);
   for (int kt = 2; kt < n2 - 2; kt += 2) {
-    pipe_step<false>(A, B, kt, smem, acc, f0, f1, blo, bhi, wave, lane);
-    pipe_step<true>(A, B, kt + 1, smem, acc, f1, f0, blo, bhi, wave, lane);
+    pipe_step<kFinish>(A, B, kt, smem, acc, f0, f1, blo, bhi, da, db, wave, lane);
+    pipe_step<kPublish>(A, B, kt + 1, smem, acc, f1, f0, blo, bhi, da, db, wave, lane);
   }
-  pipe_step<false>(A, B, n2 - 2, smem, acc, f0, f1, blo, bhi, wave, lane);
+  pipe_step<kFinish>(A, B, n2 - 2, smem, acc, f0, f1, blo, bhi, da, db, wave, lane);
   pipe_last<OB>(n2 - 1, smem, acc, f1, blo, bhi, wave, lane);
   wait_vmcnt<0>();  // loads past the end still write LDS: let them land
   __syncthreads();
