@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--cpu-sample-vocab", type=int, default=65536)
     ap.add_argument("--gemm-ceiling", action="store_true",
                     help="only time the vendor GEMM (torch.mm -> hipBLASLt) at this path's shapes")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only run the sustained-MFMA probe (random operands, no memory traffic)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for HBM counters)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -100,6 +102,9 @@ def main():
 
     from chunked_lm_head_amd import flce, synth
 
+    if args.mfma_ceiling:
+        mfma_ceiling()
+        return
     if args.gemm_ceiling:
         gemm_ceiling(synth.WORKLOADS[args.workload])
         return
@@ -208,6 +213,23 @@ def main():
         line["cpu_baseline"] = cpu_baseline(x, min(args.cpu_sample_tokens, T),
                                            args.cpu_sample_vocab)
     print(json.dumps(line), flush=True)
+
+
+def mfma_ceiling() -> None:
+    """Runs chunked_lm_head_amd/mfma_ceiling (built with the library) in a child process and
+    reports its sustained bf16 rates as fractions of the 2.5 PFLOP/s data-sheet peak."""
+    import subprocess
+
+    exe = os.path.join(ROOT, "chunked_lm_head_amd", "mfma_ceiling")
+    if not os.path.exists(exe):
+        raise SystemExit(f"{exe} is not built; run __graft_entry__.build() first")
+    proc = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    if proc.returncode != 0:
+        raise SystemExit(f"mfma_ceiling failed ({proc.returncode}): {proc.stderr.strip()}")
+    rec = json.loads(proc.stdout.strip().splitlines()[-1])["mfma_ceiling"]
+    for k in ("v_mfma_f32_32x32x16_bf16", "v_mfma_f32_16x16x32_bf16"):
+        rec[k.replace("v_mfma_f32_", "frac_")] = round(rec[k] / PEAK_BF16, 4)
+    print(json.dumps({"mfma_ceiling": rec}), flush=True)
 
 
 def gemm_ceiling(w) -> None:

@@ -11,6 +11,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libflce.so")
+CEILING_SRC = os.path.join(CSRC, "mfma_ceiling.hip")
+CEILING_BIN = os.path.join(PKG, "mfma_ceiling")  # measurement program, not part of the library
 SOURCES = [os.path.join(CSRC, "flce_api.hip")]
 DEPENDS = SOURCES + [os.path.join(CSRC, f) for f in ("flce_tile.hpp", "flce_kernels.hpp")] + [
     os.path.join(INCLUDE, "flce.h")]
@@ -48,7 +50,22 @@ def build_library(verbose: bool = False) -> str:
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, LIB)
+    build_ceiling_probe(verbose)
     return LIB
+
+
+def build_ceiling_probe(verbose: bool = False) -> str:
+    """Compile the sustained-MFMA probe that bench.py --mfma-ceiling runs."""
+    flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
+    tmp = CEILING_BIN + ".tmp"
+    cmd = [hipcc(), *flags, CEILING_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {CEILING_SRC} ({proc.returncode}):\n{proc.stderr}")
+    os.replace(tmp, CEILING_BIN)
+    return CEILING_BIN
 
 
 if __name__ == "__main__":

@@ -374,7 +374,7 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
       h.V = (int)V;
       h.vc0 = (int)vc0;
       h.vcount = (int)vcount;
-      h.Kc = (int)p.Vc;
+      h.Kc = (int)std::min<int64_t>(p.Vc, cdiv(vcount, kBK) * kBK);  // G is zero past vcount
       h.R = (int)p.R;
       h.tiles_m = (int)(p.R / kTile);
       h.tiles_n = tiles_h;
