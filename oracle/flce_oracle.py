@@ -26,6 +26,13 @@ What it computes (a plain, slow, obviously correct definition in float64):
   oracle decodes the same bf16 bits exactly into float64 (bf16 -> fp32 is a
   16-bit shift and fp32 is a subset of fp64), so it sees the GPU's inputs.
 
+* Same Unsloth section, the compiled chunked call and the list under it: the
+  call takes ``logit_scale_multiply``, ``logit_scale_divide``,
+  ``logit_softcapping`` and ``temperature``, and the page says softcapping and
+  temperature scaling are supported.  The page gives the names only; the
+  oracle applies them to each logit in that order (see ``LogitTransform``)
+  before the log-softmax, and the backward takes the chain rule through them.
+
 Readings where the pages are silent (each one is listed with its reason in the
 design notes):
 
@@ -35,6 +42,10 @@ design notes):
   0 and the gradients are 0 (PyTorch would give NaN).
 * a label outside ``[0, V)`` that is not ``ignore_index`` is a caller error:
   the oracle raises.
+* logit transforms: ``z' = z * multiply`` (if multiply != 0), ``/ divide`` (if
+  divide != 0), ``cap * tanh(z' / cap)`` (if cap != 0), ``/ temperature``, in
+  that order; 0 means "not applied" for the first three, temperature must be
+  positive and the others non-negative.
 
 Large inputs are processed in row blocks of complete vocabulary rows so that
 memory stays bounded; a block is a schedule detail, not part of the method.
@@ -80,6 +91,50 @@ def valid_mask(labels: np.ndarray, V: int, ignore_index: int = IGNORE_INDEX) -> 
     return valid
 
 
+@dataclasses.dataclass(frozen=True)
+class LogitTransform:
+    """Per-logit transform of the chunked call's keyword arguments (0: not applied)."""
+    scale_multiply: float = 0.0
+    scale_divide: float = 0.0
+    softcap: float = 0.0
+    temperature: float = 1.0
+
+    def check(self) -> None:
+        if not self.temperature > 0.0:
+            raise ValueError("temperature must be positive")
+        for name in ("scale_multiply", "scale_divide", "softcap"):
+            if not getattr(self, name) >= 0.0:
+                raise ValueError(f"{name} must be non-negative")
+
+    def apply(self, z: np.ndarray):
+        """(z', dz'/dz) elementwise, float64."""
+        self.check()
+        x = np.asarray(z, dtype=np.float64)
+        d = np.ones_like(x)
+        if self.scale_multiply != 0.0:
+            x = x * self.scale_multiply
+            d = d * self.scale_multiply
+        if self.scale_divide != 0.0:
+            x = x / self.scale_divide
+            d = d / self.scale_divide
+        if self.softcap != 0.0:
+            t = np.tanh(x / self.softcap)
+            x = self.softcap * t
+            d = d * (1.0 - t * t)
+        if self.temperature != 1.0:
+            x = x / self.temperature
+            d = d / self.temperature
+        return x, d
+
+
+def _logits(h: np.ndarray, w: np.ndarray, transform: Optional[LogitTransform]):
+    """Transformed logit rows and their derivative (None when untransformed)."""
+    z = h @ w.T
+    if transform is None:
+        return z, None
+    return transform.apply(z)
+
+
 def logsumexp_rows(z: np.ndarray) -> np.ndarray:
     """Textbook max-shifted log-sum-exp over the last axis (float64)."""
     m = z.max(axis=1)
@@ -95,8 +150,9 @@ class Forward:
 
 
 def forward(hidden, weight, labels, ignore_index: int = IGNORE_INDEX,
-            mode: str = "nll") -> Forward:
-    """Per-token NLL (``mode="nll"``) or log p(label) (``mode="logprob"``)."""
+            mode: str = "nll", transform: Optional[LogitTransform] = None) -> Forward:
+    """Per-token NLL (``mode="nll"``) or log p(label) (``mode="logprob"``) of the
+    (optionally transformed) logits."""
     if mode not in ("nll", "logprob"):
         raise ValueError(mode)
     h = _as_f64(hidden)
@@ -109,7 +165,7 @@ def forward(hidden, weight, labels, ignore_index: int = IGNORE_INDEX,
     step = _rows_per_block(V, T)
     for r0 in range(0, T, step):
         r1 = min(T, r0 + step)
-        z = h[r0:r1] @ w.T                      # full-vocabulary logit rows
+        z, _ = _logits(h[r0:r1], w, transform)  # full-vocabulary logit rows
         lse[r0:r1] = logsumexp_rows(z)
         rows = np.nonzero(valid[r0:r1])[0]
         zy[r0 + rows] = z[rows, labels[r0 + rows]]
@@ -140,17 +196,21 @@ def token_scale(labels, V: int, ignore_index: int = IGNORE_INDEX, mode: str = "n
     return np.where(valid, g, 0.0)
 
 
-def grad_logits(z: np.ndarray, lse: np.ndarray, labels: np.ndarray, c: np.ndarray) -> np.ndarray:
-    """G = c_t (softmax(z_t) - onehot(y_t)) for a block of rows."""
+def grad_logits(z: np.ndarray, lse: np.ndarray, labels: np.ndarray, c: np.ndarray,
+                dz: Optional[np.ndarray] = None) -> np.ndarray:
+    """G = c_t (softmax(z_t) - onehot(y_t)) for a block of rows; with a logit
+    transform, z are the transformed logits and the chain rule multiplies by
+    dz = dz'/dz (the gradient with respect to the raw logits)."""
     g = np.exp(z - lse[:, None])
     rows = np.nonzero(c != 0.0)[0]
     g[rows, labels[rows]] -= 1.0
-    return g * c[:, None]
+    g = g * c[:, None]
+    return g if dz is None else g * dz
 
 
 def backward(hidden, weight, labels, ignore_index: int = IGNORE_INDEX, mode: str = "nll",
              grad_out: Optional[np.ndarray] = None, grad_mean: Optional[float] = None,
-             lse: Optional[np.ndarray] = None):
+             lse: Optional[np.ndarray] = None, transform: Optional[LogitTransform] = None):
     """(dH [T, H], dW [V, H]) in float64 for the loss the forward defines."""
     h = _as_f64(hidden)
     w = _as_f64(weight)
@@ -162,37 +222,39 @@ def backward(hidden, weight, labels, ignore_index: int = IGNORE_INDEX, mode: str
     step = _rows_per_block(V, T)
     for r0 in range(0, T, step):
         r1 = min(T, r0 + step)
-        z = h[r0:r1] @ w.T
+        z, dz = _logits(h[r0:r1], w, transform)
         l = logsumexp_rows(z) if lse is None else np.asarray(lse[r0:r1], dtype=np.float64)
-        g = grad_logits(z, l, labels[r0:r1], c[r0:r1])
+        g = grad_logits(z, l, labels[r0:r1], c[r0:r1], dz)
         dh[r0:r1] = g @ w
         dw += g.T @ h[r0:r1]
     return dh, dw
 
 
 def forward_rows(hidden, weight, labels, rows: Sequence[int], ignore_index: int = IGNORE_INDEX,
-                 mode: str = "nll"):
+                 mode: str = "nll", transform: Optional[LogitTransform] = None):
     """(out, lse) of the selected tokens only; each row needs its own logits only."""
     rows = np.asarray(rows, dtype=np.int64)
-    f = forward(np.asarray(hidden)[rows], weight, np.asarray(labels)[rows], ignore_index, mode)
+    f = forward(np.asarray(hidden)[rows], weight, np.asarray(labels)[rows], ignore_index, mode,
+                transform)
     return f.out, f.lse
 
 
 def grad_hidden_rows(hidden, weight, labels, rows: Sequence[int], c_rows: np.ndarray,
-                     ignore_index: int = IGNORE_INDEX) -> np.ndarray:
+                     ignore_index: int = IGNORE_INDEX,
+                     transform: Optional[LogitTransform] = None) -> np.ndarray:
     """dH rows of the selected tokens given their scales c_t (a row needs only its logits)."""
     rows = np.asarray(rows, dtype=np.int64)
     h = _as_f64(np.asarray(hidden)[rows])
     w = _as_f64(weight)
     lab = np.asarray(labels, dtype=np.int64)[rows]
     valid_mask(lab, w.shape[0], ignore_index)
-    z = h @ w.T
-    g = grad_logits(z, logsumexp_rows(z), lab, np.asarray(c_rows, dtype=np.float64))
+    z, dz = _logits(h, w, transform)
+    g = grad_logits(z, logsumexp_rows(z), lab, np.asarray(c_rows, dtype=np.float64), dz)
     return g @ w
 
 
 def grad_weight_rows(hidden, weight, labels, vocab_rows: Sequence[int], c: np.ndarray,
-                     lse: np.ndarray) -> np.ndarray:
+                     lse: np.ndarray, transform: Optional[LogitTransform] = None) -> np.ndarray:
     """dW rows of the selected vocabulary entries: dW_v = sum_t G_tv H_t.
 
     Needs lse for every token (from ``forward``); only the selected columns of
@@ -203,10 +265,12 @@ def grad_weight_rows(hidden, weight, labels, vocab_rows: Sequence[int], c: np.nd
     wv = _as_f64(np.asarray(weight)[vr])
     labels = np.asarray(labels, dtype=np.int64)
     c = np.asarray(c, dtype=np.float64)
-    z = h @ wv.T                                   # [T, len(vr)]
+    z, dz = _logits(h, wv, transform)              # [T, len(vr)]
     g = np.exp(z - np.asarray(lse, dtype=np.float64)[:, None])
     g -= (labels[:, None] == vr[None, :])
     g *= c[:, None]
+    if dz is not None:
+        g *= dz
     return g.T @ h
 
 

@@ -294,6 +294,142 @@ def check_out_of_range_label_raises(o):
     raise AssertionError("out-of-range label was accepted")
 
 
+# --- logit transforms (Unsloth page, section "Chunking der abgeflachten Sequenzlaenge": the
+# chunked call's logit_scale_multiply / logit_scale_divide / logit_softcapping / temperature) ---
+
+
+def check_transform_linear(o):
+    """Without softcap the transform is one positive scale s = mul / div / temperature, so it
+    must equal the untransformed oracle on s W (exact in bf16 for powers of two), with
+    dH unchanged and dW scaled by s (chain rule through W' = s W)."""
+    hb, wb, labels = _rand_case(7, 8, 13, seed=71, w_std=0.6, ignore=(3,))
+    g = np.linspace(-1.0, 2.0, 7)
+    w64 = o.decode_bf16(wb)
+    for tf, s in [(o.LogitTransform(temperature=2.0), 0.5),
+                  (o.LogitTransform(scale_multiply=4.0, scale_divide=2.0), 2.0),
+                  (o.LogitTransform(scale_multiply=0.5, temperature=0.25), 2.0),
+                  (o.LogitTransform(scale_divide=8.0), 0.125)]:
+        ws = bf16_exact(w64 * s)
+        for mode in ("nll", "logprob"):
+            a = o.forward(hb, wb, labels, IGN, mode, transform=tf)
+            b = o.forward(hb, ws, labels, IGN, mode)
+            assert np.allclose(a.out, b.out, rtol=1e-13, atol=1e-13), (tf, a.out, b.out)
+            assert np.allclose(a.lse, b.lse, rtol=1e-13, atol=1e-13)
+            dha, dwa = o.backward(hb, wb, labels, IGN, mode, grad_out=g, transform=tf)
+            dhb, dwb = o.backward(hb, ws, labels, IGN, mode, grad_out=g)
+            assert np.allclose(dha, dhb, rtol=1e-12, atol=1e-14), np.abs(dha - dhb).max()
+            assert np.allclose(dwa, s * dwb, rtol=1e-12, atol=1e-14), np.abs(dwa - s * dwb).max()
+    # a scale that is not a power of two, on float64 inputs
+    h64 = o.decode_bf16(hb)
+    a = o.forward(h64, w64, labels, IGN, "nll", transform=o.LogitTransform(scale_multiply=3.0))
+    b = o.forward(h64, 3.0 * w64, labels, IGN, "nll")
+    assert np.allclose(a.out, b.out, rtol=1e-12, atol=1e-12)
+
+
+def check_softcap_saturation(o):
+    """Logits far beyond the cap saturate tanh to exactly +-1 in float64, so every transformed
+    logit is +-cap / temperature and lse = ln(k e^c + (V - k) e^-c) with c = cap / temperature
+    and k the number of positive logits: a closed form that also fixes the order (scaling
+    before the cap, temperature after it)."""
+    T, H, V = 4, 2, 9
+    h = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0], [-1.0, 0.5]])
+    w = np.array([[3e3 * (1 if (v % 3) else -1), 2e3 * (1 if v % 2 else -1)] for v in range(V)])
+    labels = np.array([0, 1, 4, 7])
+    z = h @ w.T
+    assert np.all(np.abs(z) > 400.0)
+    for cap, temp, mul in [(10.0, 1.0, 0.0), (10.0, 2.0, 0.0), (5.0, 0.5, 4.0), (30.0, 3.0, 0.5)]:
+        tf = o.LogitTransform(scale_multiply=mul, softcap=cap, temperature=temp)
+        f = o.forward(h, w, labels, IGN, "nll", transform=tf)
+        c = cap / temp
+        for t in range(T):
+            k = int((z[t] > 0).sum())
+            lse = math.log(k * math.exp(c) + (V - k) * math.exp(-c))
+            zy = c if z[t, labels[t]] > 0 else -c
+            assert abs(f.lse[t] - lse) < 1e-12, (tf, t, f.lse[t], lse)
+            assert abs(f.out[t] - (lse - zy)) < 1e-12
+    # a tiny scale before the cap keeps the logits far from it: no saturation at all
+    tf = o.LogitTransform(scale_multiply=1e-6, softcap=10.0)
+    f = o.forward(h, w, labels, IGN, "nll", transform=tf)
+    g = o.forward(h, w * 1e-6, labels, IGN, "nll")
+    assert np.allclose(f.out, g.out, rtol=1e-6, atol=1e-9)
+
+
+def check_softcap_limits(o):
+    """A cap far above every logit changes nothing; the softcap is odd in the logits."""
+    hb, wb, labels = _rand_case(6, 8, 11, seed=81, w_std=0.6)
+    a = o.forward(hb, wb, labels, IGN, "nll", transform=o.LogitTransform(softcap=1e9))
+    b = o.forward(hb, wb, labels, IGN, "nll")
+    assert np.allclose(a.out, b.out, rtol=1e-12, atol=1e-12)
+    h64, w64 = o.decode_bf16(hb), o.decode_bf16(wb)
+    tf = o.LogitTransform(softcap=1.5, temperature=0.7)
+    zp, dp = tf.apply(h64 @ w64.T)
+    zm, dm = tf.apply(h64 @ (-w64).T)
+    assert np.allclose(zp, -zm, rtol=0, atol=1e-15) and np.allclose(dp, dm, rtol=0, atol=1e-15)
+    assert np.all(np.abs(zp) < 1.5 / 0.7)
+
+
+def _tloss(o, h, w, labels, mode, g, tf):
+    f = o.forward(h, w, labels, IGN, mode, transform=tf)
+    return float(np.dot(f.out, g)) if g is not None else f.mean
+
+
+def check_transform_finite_differences(o):
+    """Central differences of the transformed forward against the backward's chain rule."""
+    rng = np.random.default_rng(91)
+    T, H, V = 4, 3, 6
+    h = rng.standard_normal((T, H)) * 1.5
+    w = rng.standard_normal((V, H)) * 1.2
+    labels = np.array([2, 0, IGN, 5])
+    for tf, mode, g in [
+            (o.LogitTransform(softcap=1.5), "nll", None),
+            (o.LogitTransform(scale_multiply=2.0, softcap=2.0, temperature=0.8), "nll",
+             rng.standard_normal(T)),
+            (o.LogitTransform(scale_divide=3.0, temperature=1.7), "logprob", rng.standard_normal(T)),
+            (o.LogitTransform(scale_multiply=0.7, scale_divide=0.9, softcap=0.6, temperature=1.3),
+             "logprob", rng.standard_normal(T))]:
+        if g is None:
+            dh, dw = o.backward(h, w, labels, IGN, mode, grad_mean=1.0, transform=tf)
+        else:
+            dh, dw = o.backward(h, w, labels, IGN, mode, grad_out=g, transform=tf)
+        eps = 1e-6
+        for arr, grad in ((h, dh), (w, dw)):
+            num = np.zeros_like(arr)
+            for idx in np.ndindex(arr.shape):
+                keep = arr[idx]
+                arr[idx] = keep + eps
+                lp = _tloss(o, h, w, labels, mode, g, tf)
+                arr[idx] = keep - eps
+                lm = _tloss(o, h, w, labels, mode, g, tf)
+                arr[idx] = keep
+                num[idx] = (lp - lm) / (2 * eps)
+            assert np.allclose(grad, num, rtol=1e-6, atol=1e-8), (tf, np.abs(grad - num).max())
+
+
+def check_transform_rows_and_args(o):
+    """Row helpers agree with the full computation under a transform; invalid values raise."""
+    hb, wb, labels = _rand_case(8, 8, 10, seed=95, w_std=0.6, ignore=(6,))
+    tf = o.LogitTransform(scale_multiply=1.5, softcap=2.0, temperature=0.9)
+    g = np.linspace(-1.0, 1.0, 8)
+    f = o.forward(hb, wb, labels, IGN, "nll", transform=tf)
+    dh, dw = o.backward(hb, wb, labels, IGN, "nll", grad_out=g, transform=tf)
+    rows = [0, 3, 7]
+    out_r, lse_r = o.forward_rows(hb, wb, labels, rows, IGN, "nll", transform=tf)
+    assert np.allclose(out_r, f.out[rows], rtol=1e-13, atol=1e-13)
+    assert np.allclose(lse_r, f.lse[rows], rtol=1e-13, atol=1e-13)
+    c = o.token_scale(labels, 10, IGN, "nll", grad_out=g)
+    dhr = o.grad_hidden_rows(hb, wb, labels, rows, c[rows], IGN, transform=tf)
+    assert np.allclose(dhr, dh[rows], rtol=1e-12, atol=1e-14)
+    dwr = o.grad_weight_rows(hb, wb, labels, [1, 4, 9], c, f.lse, transform=tf)
+    assert np.allclose(dwr, dw[[1, 4, 9]], rtol=1e-12, atol=1e-14)
+    for bad in (dict(temperature=0.0), dict(temperature=-1.0), dict(softcap=-1.0),
+                dict(scale_multiply=-2.0), dict(scale_divide=-0.5)):
+        try:
+            o.forward(hb, wb, labels, IGN, "nll", transform=o.LogitTransform(**bad))
+        except ValueError:
+            continue
+        raise AssertionError(f"invalid transform {bad} was accepted")
+
+
 ALL_CHECKS = [
     check_zero_weight,
     check_two_class,
@@ -307,4 +443,9 @@ ALL_CHECKS = [
     check_token_permutation,
     check_row_helpers,
     check_out_of_range_label_raises,
+    check_transform_linear,
+    check_softcap_saturation,
+    check_softcap_limits,
+    check_transform_finite_differences,
+    check_transform_rows_and_args,
 ]

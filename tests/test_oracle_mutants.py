@@ -29,6 +29,16 @@ MUTANTS = {
                           "f32 = (b.astype(np.uint32) << np.uint32(15)).view(np.float32)"),
     "dh_uses_softmax_only": ("dh[r0:r1] = g @ w", "dh[r0:r1] = np.exp(z - l[:, None]) @ w"),
     "dw_transposed_rows": ("dw += g.T @ h[r0:r1]", "dw += (g.T @ h[r0:r1])[::-1]"),
+    # logit transforms
+    "softcap_no_chain_rule": ("d = d * (1.0 - t * t)", "d = d * 1.0"),
+    "softcap_without_division": ("t = np.tanh(x / self.softcap)", "t = np.tanh(x)"),
+    "temperature_multiplies": ("            x = x / self.temperature\n",
+                               "            x = x * self.temperature\n"),
+    "temperature_before_cap": ("            t = np.tanh(x / self.softcap)\n            x = self.softcap * t\n",
+                               "            t = np.tanh(x / self.temperature / self.softcap)\n"
+                               "            x = self.softcap * t * self.temperature\n"),
+    "divide_multiplies": ("            x = x / self.scale_divide\n", "            x = x * self.scale_divide\n"),
+    "weight_rows_drop_chain": ("    if dz is not None:\n        g *= dz\n", ""),
 }
 
 
