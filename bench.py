@@ -43,12 +43,20 @@ def parse():
                     help="only run the sustained-MFMA probe (random operands, no memory traffic)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for HBM counters)")
+    ap.add_argument("--logit-scale-multiply", type=float, default=0.0,
+                    help="logit transform: multiply each logit (0 = off)")
+    ap.add_argument("--logit-scale-divide", type=float, default=0.0,
+                    help="logit transform: divide each logit (0 = off)")
+    ap.add_argument("--logit-softcapping", type=float, default=0.0,
+                    help="logit transform: cap * tanh(z / cap) (0 = off)")
+    ap.add_argument("--temperature", type=float, default=1.0,
+                    help="logit transform: divide by the temperature, last")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch from rocprofv3 counters (optional)")
     return ap.parse_args()
 
 
-def cpu_baseline(x, n_tokens: int, n_vocab: int) -> dict:
+def cpu_baseline(x, n_tokens: int, n_vocab: int, transform=None) -> dict:
     """The oracle, untouched, on a bounded sample: the first n_tokens tokens against the
     first n_vocab vocabulary rows (labels folded into that range).  Its work is linear in
     the vocabulary, so the rate is scaled by n_vocab / V to full-vocabulary tokens/s."""
@@ -69,8 +77,9 @@ def cpu_baseline(x, n_tokens: int, n_vocab: int) -> dict:
     used = y != -100
     y[used] %= n_vocab
     t0 = time.perf_counter()
-    f = flce_oracle.forward(h, wt, y)
-    flce_oracle.backward(h, wt, y, lse=f.lse, grad_mean=1.0)
+    tr = flce_oracle.LogitTransform(**transform) if transform else None
+    f = flce_oracle.forward(h, wt, y, transform=tr)
+    flce_oracle.backward(h, wt, y, lse=f.lse, grad_mean=1.0, transform=tr)
     dt = time.perf_counter() - t0
     return {"value": round(n_tokens / dt * n_vocab / V, 3), "unit": "tokens/s",
             "cores": int(cores), "kind": "oracle",
@@ -111,6 +120,12 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     chunk_rows = args.chunk_rows or w.chunk_rows
+    xf_vals = dict(scale_multiply=args.logit_scale_multiply, scale_divide=args.logit_scale_divide,
+                   softcap=args.logit_softcapping, temperature=args.temperature)
+    has_xf = xf_vals != dict(scale_multiply=0.0, scale_divide=0.0, softcap=0.0, temperature=1.0)
+    xf = dict(logit_scale_multiply=args.logit_scale_multiply,
+              logit_scale_divide=args.logit_scale_divide,
+              logit_softcapping=args.logit_softcapping, temperature=args.temperature)
     t_gen = time.perf_counter()
     x = synth.make_inputs(w)
     t_gen = time.perf_counter() - t_gen
@@ -135,12 +150,12 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        flce.forward(h, W, y, chunk_rows=chunk_rows, mode=w.mode, workspace=ws, out=out,
-                     lse=lse, mean=mean)
+        flce.forward(h, W, y, chunk_rows=chunk_rows, mode=w.mode, transform=xf, workspace=ws,
+                     out=out, lse=lse, mean=mean)
         if ev is not None:
             ev[1].record()
-        flce.backward(h, W, y, lse, chunk_rows=chunk_rows, mode=w.mode, grad_hidden=dh,
-                      grad_weight=dw, workspace=ws, **gkw)
+        flce.backward(h, W, y, lse, chunk_rows=chunk_rows, mode=w.mode, transform=xf,
+                      grad_hidden=dh, grad_weight=dw, workspace=ws, **gkw)
         if ev is not None:
             ev[2].record()
 
@@ -166,7 +181,8 @@ def main():
     fwd_flops = 2.0 * T * V * D
 
     traffic = None
-    if os.path.exists(args.traffic_json):
+    # the counters were taken without a softcap (the capped forward is another instantiation)
+    if os.path.exists(args.traffic_json) and args.logit_softcapping == 0.0:
         try:
             tj = json.load(open(args.traffic_json))
             rec = tj.get(args.workload, {}).get("fwd_lse_kernel")
@@ -190,7 +206,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "tokens": T, "hidden": D, "vocab": V,
                    "chunk_rows": chunk_rows, "mode": w.mode, "reduction": w.reduction,
-                   "ignored_tokens": w.ignore_count},
+                   "ignored_tokens": w.ignore_count,
+                   **({"logit_transform": xf_vals} if has_xf else {})},
         "mfma_frac_of_step": round(step_flops / (ms / 1e3) / PEAK_BF16, 4),
         "fwd_ms": round(fwd_avg, 4),
         "bwd_ms": round(bwd_avg, 4),
@@ -211,7 +228,7 @@ def main():
           f"(fwd {fwd_avg:.3f}, bwd {bwd_avg:.3f})", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(x, min(args.cpu_sample_tokens, T),
-                                           args.cpu_sample_vocab)
+                                           args.cpu_sample_vocab, xf_vals if has_xf else None)
     print(json.dumps(line), flush=True)
 
 

@@ -19,6 +19,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "flce.h"
 #include "flce_kernels.hpp"
@@ -176,6 +177,40 @@ flce_status launched(const char *what) {
     if (s_ != FLCE_OK) return s_;        \
   } while (0)
 
+// Folds the logit transform into the kernels' parameters.  Without a cap the
+// transform is the single scale (multiply / divide) / temperature; with one,
+// the kernels apply cap * tanh(z * scale / cap) / temperature per logit.
+flce_status make_xform(const flce_logit_transform *t, Xform &x, bool &cap) {
+  x.zscale = 1.f;
+  x.cap = 0.f;
+  x.inv_cap = 0.f;
+  x.inv_temp = 1.f;
+  cap = false;
+  if (!t) return FLCE_OK;
+  const float mul = t->scale_multiply, div = t->scale_divide, sc = t->softcap,
+              temp = t->temperature;
+  if (!std::isfinite(mul) || !std::isfinite(div) || !std::isfinite(sc) ||
+      !std::isfinite(temp) || mul < 0.f || div < 0.f || sc < 0.f || !(temp > 0.f))
+    return fail(FLCE_ERR_ARG,
+                "logit transform (multiply %g, divide %g, softcap %g, temperature %g): the "
+                "first three must be finite and >= 0, temperature finite and > 0",
+                mul, div, sc, temp);
+  const double s1 = (mul != 0.f ? (double)mul : 1.0) / (div != 0.f ? (double)div : 1.0);
+  const double inv_temp = 1.0 / (double)temp;
+  cap = sc != 0.f;
+  const double zscale = cap ? s1 : s1 * inv_temp;
+  const double inv_cap = cap ? 1.0 / (double)sc : 0.0;
+  const double lim = 3.0e38, tiny = 1.0e-37;
+  if (!(zscale <= lim && zscale >= tiny) || !(inv_temp <= lim && inv_temp >= tiny) ||
+      !(inv_cap <= lim) || (cap && inv_cap < tiny))
+    return fail(FLCE_ERR_ARG, "logit transform factors are out of the fp32 range");
+  x.zscale = (float)zscale;
+  x.cap = sc;
+  x.inv_cap = (float)inv_cap;
+  x.inv_temp = cap ? (float)inv_temp : 1.f;
+  return FLCE_OK;
+}
+
 flce_status fill(float *dst, int64_t n, float v, hipStream_t s) {
   if (n <= 0) return FLCE_OK;
   const int64_t blocks = std::min<int64_t>(cdiv(n, 256), 4096);
@@ -221,13 +256,17 @@ const char *flce_last_error(void) { return g_last_error; }
 
 flce_status flce_forward(const void *hidden, const void *weight, const int64_t *labels,
                          int64_t T, int64_t D, int64_t V, int64_t ignore_index,
-                         int64_t chunk_rows, int mode, float *out, float *lse, float *mean_out,
+                         int64_t chunk_rows, int mode, const flce_logit_transform *transform,
+                         float *out, float *lse, float *mean_out,
                          void *workspace, size_t workspace_bytes, void *stream) {
   g_last_error[0] = 0;
   Plan p;
   FLCE_TRY(make_plan(T, D, V, chunk_rows, p));
   if (mode != FLCE_MODE_NLL && mode != FLCE_MODE_LOGPROB)
     return fail(FLCE_ERR_ARG, "mode %d is neither NLL (0) nor LOGPROB (1)", mode);
+  Xform xf;
+  bool cap;
+  FLCE_TRY(make_xform(transform, xf, cap));
   if (T > 0) {
     if (!hidden || !weight || !labels || !out || !lse || !workspace)
       return fail(FLCE_ERR_ARG, "a required pointer is NULL");
@@ -256,10 +295,14 @@ flce_status flce_forward(const void *hidden, const void *weight, const int64_t *
   a.n_vt = (int)p.n_vt;
   a.splits = (int)p.splits;
   a.T_pad = (int)p.T_pad;
+  a.xf = xf;
   a.part_m = (float *)(ws + p.off_pm);
   a.part_s = (float *)(ws + p.off_ps);
   a.zlab = (float *)(ws + p.off_zl);
-  fwd_lse_kernel<<<(unsigned)(p.n_tt * p.splits), kThreads, 0, s>>>(a);
+  if (cap)
+    fwd_lse_kernel<true><<<(unsigned)(p.n_tt * p.splits), kThreads, 0, s>>>(a);
+  else
+    fwd_lse_kernel<false><<<(unsigned)(p.n_tt * p.splits), kThreads, 0, s>>>(a);
   FLCE_TRY(launched("fwd_lse"));
 
   FwdCombineParams c;
@@ -289,14 +332,18 @@ flce_status flce_forward(const void *hidden, const void *weight, const int64_t *
 flce_status flce_backward(const void *hidden, const void *weight, const int64_t *labels,
                           const float *lse, int64_t T, int64_t D, int64_t V,
                           int64_t ignore_index, int64_t chunk_rows, int mode,
-                          const float *grad_out, const float *grad_mean, void *grad_hidden,
-                          float *grad_weight, int accumulate_grad_weight, void *workspace,
-                          size_t workspace_bytes, void *stream) {
+                          const flce_logit_transform *transform, const float *grad_out,
+                          const float *grad_mean, void *grad_hidden, float *grad_weight,
+                          int accumulate_grad_weight, void *workspace, size_t workspace_bytes,
+                          void *stream) {
   g_last_error[0] = 0;
   Plan p;
   FLCE_TRY(make_plan(T, D, V, chunk_rows, p));
   if (mode != FLCE_MODE_NLL && mode != FLCE_MODE_LOGPROB)
     return fail(FLCE_ERR_ARG, "mode %d is neither NLL (0) nor LOGPROB (1)", mode);
+  Xform xf;
+  bool cap;
+  FLCE_TRY(make_xform(transform, xf, cap));
   if ((grad_out == nullptr) == (grad_mean == nullptr))
     return fail(FLCE_ERR_ARG, "exactly one of grad_out and grad_mean must be given");
   if (!grad_weight) return fail(FLCE_ERR_ARG, "grad_weight is NULL");
@@ -361,9 +408,13 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
       g.vc0 = (int)vc0;
       g.tiles_m = (int)(p.Vc / kTile);
       g.tiles_n = (int)(p.R / kTile);
+      g.xf = xf;
       g.G = G;
       g.Gp = (int)p.Vc;
-      bwd_grad_kernel<<<(unsigned)(g.tiles_m * g.tiles_n), kThreads, 0, s>>>(g);
+      if (cap)
+        bwd_grad_kernel<true><<<(unsigned)(g.tiles_m * g.tiles_n), kThreads, 0, s>>>(g);
+      else
+        bwd_grad_kernel<false><<<(unsigned)(g.tiles_m * g.tiles_n), kThreads, 0, s>>>(g);
       FLCE_TRY(launched("bwd_grad"));
 
       BwdDhParams h;

@@ -55,6 +55,34 @@ __device__ __forceinline__ int label_reg(int rel, int lane) {
   return (rel >> 4) * 4 + (rel & 3);
 }
 
+// Per-logit transform before the log-softmax (the chunked call's
+// logit_scale_multiply / logit_scale_divide / logit_softcapping / temperature
+// on the Unsloth GRPO page, section "Chunking der abgeflachten
+// Sequenzlaenge"), in the order multiply, divide, cap * tanh(. / cap),
+// divide by temperature.  Without a cap the whole transform is one positive
+// scale, folded into the base-2 prescale of the exponentials; with a cap
+// (kCap kernels) it is applied per logit.  Every factor is positive, so the
+// transform is increasing and the running maximum stays a maximum.
+struct Xform {
+  float zscale;    // no cap: the whole transform (z' = z * zscale); cap: multiply / divide
+  float cap;       // cap kernels only
+  float inv_cap;
+  float inv_temp;
+};
+
+// tanh through the hardware base-2 exponential: 1 - 2 / (1 + e^(2u)); exact
+// limits +-1 for large |u|, absolute error about 1e-7 near 0.
+__device__ __forceinline__ float tanh_exp2(float u) {
+  const float e = fast_exp2(u * (2.f * kLog2e));
+  return 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e);
+}
+
+// Capped transform of one raw logit; -inf (rows past the vocabulary) stays -inf.
+__device__ __forceinline__ float xform_cap(float z, const Xform &x, float &t) {
+  t = tanh_exp2(z * x.zscale * x.inv_cap);
+  return z == -kInf ? -kInf : x.cap * t * x.inv_temp;
+}
+
 // Merges two (max, sum of 2^(x - max)) pairs of the base-2 log-sum-exp.
 __device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2) {
   const float M = fmaxf(m, m2);
@@ -75,6 +103,7 @@ struct FwdLseParams {
   int64_t ignore_index;
   int T, D, V;
   int n_tt, n_vt, splits, T_pad;
+  Xform xf;                 // logit transform (z below is the transformed logit)
   float *part_m;            // [splits, T_pad] running max of z*log2(e)
   float *part_s;            // [splits, T_pad] sum of 2^(z*log2(e) - max)
   float *zlab;              // [T_pad] logit of the label
@@ -82,6 +111,7 @@ struct FwdLseParams {
 
 constexpr int kLdsFwd = kPipeBytes;  // the partial-merge exchange reuses the ring
 
+template <bool kCap>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(1, 1))) fwd_lse_kernel(FwdLseParams p) {
   __shared__ __attribute__((aligned(16))) char smem_raw[kLdsFwd];
@@ -116,6 +146,7 @@ __global__ void __launch_bounds__(kThreads)
     zl[nb] = 0.f;
   }
   unsigned have = 0;  // bit nb: this lane captured the label logit of token column nb
+  const float ks = p.xf.zscale * kLog2e;  // base-2 prescale of the uncapped transform
 
   // The next vocabulary tile's first stages are issued before the current
   // tile's epilogue, which touches neither LDS nor memory.
@@ -153,22 +184,34 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int r = 0; r < 4; ++r) zmax = fmaxf(zmax, acc_read(acc.v[mb][nb][r]));
       const float mold = mrun[nb];
-      const float mnew = fmaxf(mold, zmax * kLog2e);
+      float t;
+      const float mnew =
+          fmaxf(mold, kCap ? xform_cap(zmax, p.xf, t) * kLog2e : zmax * ks);  // increasing
       if (mnew != -kInf) {
         float s = 0.f;
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            s += fast_exp2(__builtin_fmaf(acc_read(acc.v[mb][nb][r]), kLog2e, -mnew));
+          for (int r = 0; r < 4; ++r) {
+            const float z = acc_read(acc.v[mb][nb][r]);
+            if constexpr (kCap)
+              s += fast_exp2(__builtin_fmaf(xform_cap(z, p.xf, t), kLog2e, -mnew));
+            else
+              s += fast_exp2(__builtin_fmaf(z, ks, -mnew));
+          }
         srun[nb] = (mold == -kInf ? 0.f : srun[nb] * fast_exp2(mold - mnew)) + s;
         mrun[nb] = mnew;
       }
     }
   }
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb)
-    if (have & (1u << nb)) p.zlab[t0 + wn * 128 + nb * 16 + (lane & 15)] = zl[nb];
+  for (int nb = 0; nb < 8; ++nb) {
+    if (have & (1u << nb)) {
+      float t;
+      p.zlab[t0 + wn * 128 + nb * 16 + (lane & 15)] =
+          kCap ? xform_cap(zl[nb], p.xf, t) : zl[nb] * p.xf.zscale;
+    }
+  }
 
   // Merge the four lanes holding one token (l, l ^ 16, l ^ 32, l ^ 48), then
   // the two waves (wm).
@@ -325,6 +368,7 @@ struct BwdGradParams {
   int T, D, V;
   int rb0, vc0;          // first token / vocabulary row of this block
   int tiles_m, tiles_n;  // vocabulary tiles of the chunk, token tiles of the row block
+  Xform xf;              // logit transform; G is the gradient with respect to the raw logits
   uint16_t *G;           // [R, Gp] bf16, row = token - rb0, col = vocab - vc0
   int Gp;
 };
@@ -332,6 +376,7 @@ struct BwdGradParams {
 constexpr int kGPitch = kTile * 2 + 16;                 // bytes per LDS row of the G tile
 constexpr int kLdsGrad = (kTile * kGPitch > kPipeBytes) ? kTile * kGPitch : kPipeBytes;
 
+template <bool kCap>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(1, 1))) bwd_grad_kernel(BwdGradParams p) {
   __shared__ __attribute__((aligned(16))) char smem_raw[kLdsGrad];
@@ -364,18 +409,33 @@ __global__ void __launch_bounds__(kThreads)
     if (c != 0.f) y = (int)p.labels[t];  // c != 0 implies 0 <= y < V
     const int lr = label_reg(y - vw, lane);
     const bool any_label = __builtin_amdgcn_ballot_w64(lr >= 0) != 0;
+    // uncapped: G = c s (P - onehot), P = 2^(z s log2 e - l2), s the whole scale
+    const float cs = c * p.xf.zscale, ks = p.xf.zscale * kLog2e;
+    // capped: G = c (P - onehot) dz'/dz, dz'/dz = scale (1 - t^2) / temperature
+    const float dscale = p.xf.zscale * p.xf.inv_temp;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
-      float g[4];
+      float g[4], d[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float z = acc_read(acc.v[mb][nb][e]);
-        g[e] = c * fast_exp2(__builtin_fmaf(z, kLog2e, -l2));
+        if constexpr (kCap) {
+          float tt;
+          const float zt = xform_cap(z, p.xf, tt);
+          g[e] = fast_exp2(__builtin_fmaf(zt, kLog2e, -l2));
+          d[e] = c * dscale * (1.f - tt * tt);
+        } else {
+          g[e] = cs * fast_exp2(__builtin_fmaf(z, ks, -l2));
+        }
       }
       if (any_label) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (lr == mb * 4 + e) g[e] -= c;
+          if (lr == mb * 4 + e) g[e] -= kCap ? 1.f : cs;
+      }
+      if constexpr (kCap) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) g[e] *= d[e];
       }
       u32x2 w;
       w[0] = pack_bf16(g[0], g[1]);

@@ -32,6 +32,12 @@ EXPORTS = ("flce_workspace_bytes", "flce_forward", "flce_backward", "flce_descri
            "flce_status_string", "flce_last_error")
 
 
+class LogitTransform(ctypes.Structure):
+    """``flce_logit_transform``: multiply, divide, softcap, temperature (0 = skipped)."""
+    _fields_ = [("scale_multiply", ctypes.c_float), ("scale_divide", ctypes.c_float),
+                ("softcap", ctypes.c_float), ("temperature", ctypes.c_float)]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
@@ -39,11 +45,12 @@ def _load() -> ctypes.CDLL:
     i64, vp, f32p, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t
     lib.flce_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.flce_workspace_bytes.restype = sz
-    lib.flce_forward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int,
+    xp = ctypes.POINTER(LogitTransform)
+    lib.flce_forward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, xp,
                                  f32p, f32p, f32p, vp, sz, vp]
     lib.flce_forward.restype = ctypes.c_int
     lib.flce_backward.argtypes = [vp, vp, vp, f32p, i64, i64, i64, i64, i64, ctypes.c_int,
-                                  f32p, f32p, vp, f32p, ctypes.c_int, vp, sz, vp]
+                                  xp, f32p, f32p, vp, f32p, ctypes.c_int, vp, sz, vp]
     lib.flce_backward.restype = ctypes.c_int
     lib.flce_describe_plan.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
     lib.flce_describe_plan.restype = ctypes.c_int
@@ -75,6 +82,20 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def make_transform(logit_scale_multiply: float = 0.0, logit_scale_divide: float = 0.0,
+                   logit_softcapping: float = 0.0, temperature: float = 1.0):
+    """The C struct for these values, or None (no transform) for the defaults.
+
+    The library applies, per raw logit z: z * multiply (if nonzero), / divide
+    (if nonzero), softcap * tanh(. / softcap) (if nonzero), / temperature, and
+    checks the values (FLCE_ERR_ARG when out of range)."""
+    vals = (float(logit_scale_multiply), float(logit_scale_divide), float(logit_softcapping),
+            float(temperature))
+    if vals == (0.0, 0.0, 0.0, 1.0):
+        return None
+    return ctypes.byref(LogitTransform(*vals))
 
 
 def workspace_bytes(T: int, D: int, V: int, chunk_rows: int = 256) -> int:
@@ -117,9 +138,12 @@ def alloc_workspace(T: int, D: int, V: int, chunk_rows: int, device) -> torch.Te
 
 def forward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor, *,
             ignore_index: int = -100, chunk_rows: int = 256, mode: str = "nll",
+            transform: Optional[dict] = None,
             workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
             lse: Optional[torch.Tensor] = None, mean: Optional[torch.Tensor] = None):
-    """(out [T], lse [T], mean []) fp32: per-token NLL or log-prob, lse, mean over used tokens."""
+    """(out [T], lse [T], mean []) fp32: per-token NLL or log-prob, lse, mean over used tokens.
+
+    ``transform`` holds keyword arguments of :func:`make_transform`."""
     _validate(hidden, weight, labels)
     T, D = hidden.shape
     V = weight.shape[0]
@@ -130,7 +154,8 @@ def forward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor, *,
     if workspace is None:
         workspace = alloc_workspace(T, D, V, chunk_rows, dev)
     _check(lib.flce_forward(_ptr(hidden), _ptr(weight), _ptr(labels), T, D, V, ignore_index,
-                            chunk_rows, _MODES[mode], _ptr(out), _ptr(lse), _ptr(mean),
+                            chunk_rows, _MODES[mode], make_transform(**(transform or {})),
+                            _ptr(out), _ptr(lse), _ptr(mean),
                             _ptr(workspace), workspace.numel(), _stream(dev)))
     return out, lse, mean
 
@@ -138,7 +163,7 @@ def forward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor, *,
 def backward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor,
              lse: torch.Tensor, *, grad_out: Optional[torch.Tensor] = None,
              grad_mean: Optional[torch.Tensor] = None, ignore_index: int = -100,
-             chunk_rows: int = 256, mode: str = "nll",
+             chunk_rows: int = 256, mode: str = "nll", transform: Optional[dict] = None,
              grad_hidden: Optional[torch.Tensor] = None,
              grad_weight: Optional[torch.Tensor] = None, accumulate: bool = False,
              workspace: Optional[torch.Tensor] = None):
@@ -161,7 +186,8 @@ def backward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor,
     if workspace is None:
         workspace = alloc_workspace(T, D, V, chunk_rows, dev)
     _check(lib.flce_backward(_ptr(hidden), _ptr(weight), _ptr(labels), _ptr(lse), T, D, V,
-                             ignore_index, chunk_rows, _MODES[mode], _ptr(grad_out),
+                             ignore_index, chunk_rows, _MODES[mode],
+                             make_transform(**(transform or {})), _ptr(grad_out),
                              _ptr(grad_mean), _ptr(grad_hidden), _ptr(grad_weight),
                              1 if accumulate else 0, _ptr(workspace), workspace.numel(),
                              _stream(dev)))
@@ -172,32 +198,49 @@ class _ChunkedLinearCE(torch.autograd.Function):
     """Mean NLL (``reduction="mean"``) or per-token NLL / log-prob (``"none"``)."""
 
     @staticmethod
-    def forward(ctx, hidden, weight, labels, ignore_index, chunk_rows, mode, reduction):
+    def forward(ctx, hidden, weight, labels, ignore_index, chunk_rows, mode, reduction,
+                transform):
         out, lse, mean = forward(hidden, weight, labels, ignore_index=ignore_index,
-                                 chunk_rows=chunk_rows, mode=mode)
+                                 chunk_rows=chunk_rows, mode=mode, transform=transform)
         ctx.save_for_backward(hidden, weight, labels, lse)
-        ctx.cfg = (ignore_index, chunk_rows, mode, reduction)
+        ctx.cfg = (ignore_index, chunk_rows, mode, reduction, transform)
         return mean if reduction == "mean" else out
 
     @staticmethod
     def backward(ctx, grad):
         hidden, weight, labels, lse = ctx.saved_tensors
-        ignore_index, chunk_rows, mode, reduction = ctx.cfg
+        ignore_index, chunk_rows, mode, reduction, transform = ctx.cfg
         g = grad.float().contiguous()
         kw = dict(grad_mean=g.reshape(())) if reduction == "mean" else dict(grad_out=g)
         dh, dw = backward(hidden, weight, labels, lse, ignore_index=ignore_index,
-                          chunk_rows=chunk_rows, mode=mode, **kw)
-        return dh, dw.to(weight.dtype), None, None, None, None, None
+                          chunk_rows=chunk_rows, mode=mode, transform=transform, **kw)
+        return dh, dw.to(weight.dtype), None, None, None, None, None, None
+
+
+def _transform_kwargs(logit_scale_multiply, logit_scale_divide, logit_softcapping, temperature):
+    return dict(logit_scale_multiply=logit_scale_multiply, logit_scale_divide=logit_scale_divide,
+                logit_softcapping=logit_softcapping, temperature=temperature)
 
 
 def chunked_linear_cross_entropy(hidden, weight, labels, *, ignore_index=-100, chunk_rows=256,
-                                 reduction="mean"):
-    """Autograd-aware chunked NLL of ``hidden @ weight.T`` against ``labels``."""
+                                 reduction="mean", logit_scale_multiply=0.0,
+                                 logit_scale_divide=0.0, logit_softcapping=0.0,
+                                 temperature=1.0):
+    """Autograd-aware chunked NLL of ``hidden @ weight.T`` against ``labels``.
+
+    The logit transform arguments follow the chunked call of the Unsloth GRPO
+    page (section "Chunking der abgeflachten Sequenzlaenge"); 0 skips a step."""
+    xf = _transform_kwargs(logit_scale_multiply, logit_scale_divide, logit_softcapping,
+                           temperature)
     return _ChunkedLinearCE.apply(hidden, weight, labels, ignore_index, chunk_rows, "nll",
-                                  reduction)
+                                  reduction, xf)
 
 
-def selective_log_softmax(hidden, weight, labels, *, ignore_index=-100, chunk_rows=256):
+def selective_log_softmax(hidden, weight, labels, *, ignore_index=-100, chunk_rows=256,
+                          logit_scale_multiply=0.0, logit_scale_divide=0.0,
+                          logit_softcapping=0.0, temperature=1.0):
     """Autograd-aware per-token log p(label) without materialising the logits."""
+    xf = _transform_kwargs(logit_scale_multiply, logit_scale_divide, logit_softcapping,
+                           temperature)
     return _ChunkedLinearCE.apply(hidden, weight, labels, ignore_index, chunk_rows, "logprob",
-                                  "none")
+                                  "none", xf)

@@ -46,6 +46,8 @@
  *    and are left out of the mean's denominator.
  *  - Results are deterministic: repeated calls with the same inputs give the
  *    same bits (no floating-point atomics).
+ *  - The one host pointer is the optional logit transform (read during the
+ *    call, not retained).
  */
 #ifndef FLCE_H
 #define FLCE_H
@@ -67,6 +69,30 @@ typedef enum flce_status {
 } flce_status;
 
 enum { FLCE_MODE_NLL = 0, FLCE_MODE_LOGPROB = 1 };
+
+/*
+ * Optional per-logit transform applied before the log-softmax: the chunked
+ * call on the Unsloth GRPO page (section "Chunking der abgeflachten
+ * Sequenzlaenge") takes logit_scale_multiply, logit_scale_divide,
+ * logit_softcapping and temperature, and the page says softcapping and
+ * temperature scaling are supported; it prints no formula.  This library
+ * applies them in that order to each raw logit z:
+ *     z' = z * scale_multiply                 (skipped when scale_multiply == 0)
+ *     z' = z' / scale_divide                  (skipped when scale_divide == 0)
+ *     z' = softcap * tanh(z' / softcap)       (skipped when softcap == 0)
+ *     z' = z' / temperature
+ * and every output (lse, NLL, log p) refers to z'.  The backward takes the
+ * chain rule through the transform.  scale_multiply, scale_divide and softcap
+ * must be >= 0 and finite, temperature > 0 and finite; otherwise the call
+ * fails with FLCE_ERR_ARG.  A NULL pointer means no transform.  Passed by
+ * host pointer; forward and backward must be given the same values.
+ */
+typedef struct flce_logit_transform {
+  float scale_multiply;
+  float scale_divide;
+  float softcap;
+  float temperature;
+} flce_logit_transform;
 
 /*
  * Bytes of device workspace that flce_forward and flce_backward need for this
@@ -92,7 +118,7 @@ size_t flce_workspace_bytes(int64_t T, int64_t D, int64_t V, int64_t chunk_rows)
  */
 flce_status flce_forward(const void *hidden, const void *weight, const int64_t *labels,
                          int64_t T, int64_t D, int64_t V, int64_t ignore_index,
-                         int64_t chunk_rows, int mode,
+                         int64_t chunk_rows, int mode, const flce_logit_transform *transform,
                          float *out, float *lse, float *mean_out,
                          void *workspace, size_t workspace_bytes, void *stream);
 
@@ -101,18 +127,21 @@ flce_status flce_forward(const void *hidden, const void *weight, const int64_t *
  *   grad_hidden [T x D] bf16  = G W,
  *   grad_weight [V x D] fp32  = G^T H      (added to the existing contents if
  *                                           accumulate_grad_weight != 0),
- * with G_tv = c_t (softmax(z_t)_v - [v == y_t]) and
+ * with G_tv = c_t (softmax(z'_t)_v - [v == y_t]) dz'_tv/dz_tv (z' = z without a
+ * transform) and
  *   c_t = s * grad_out[t]            if grad_out != NULL (dL/d out_t),
  *   c_t = s * (*grad_mean) / N_valid if grad_out == NULL (dL/d mean; device scalar),
  * s = +1 for FLCE_MODE_NLL and -1 for FLCE_MODE_LOGPROB, c_t = 0 for ignored
  * (and out-of-range) labels, N_valid = number of tokens whose label is not
  * ignore_index (c_t = 0 for all t if N_valid == 0).  Exactly one of grad_out
  * and grad_mean must be non-NULL.  lse must be the forward's output for the
- * same inputs.  T == 0 is valid: grad_weight is zeroed unless accumulating.
+ * same inputs and transform.  T == 0 is valid: grad_weight is zeroed unless
+ * accumulating.
  */
 flce_status flce_backward(const void *hidden, const void *weight, const int64_t *labels,
                           const float *lse, int64_t T, int64_t D, int64_t V,
                           int64_t ignore_index, int64_t chunk_rows, int mode,
+                          const flce_logit_transform *transform,
                           const float *grad_out, const float *grad_mean,
                           void *grad_hidden, float *grad_weight, int accumulate_grad_weight,
                           void *workspace, size_t workspace_bytes, void *stream);

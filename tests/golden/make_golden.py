@@ -9,6 +9,12 @@ float64 oracle computes, over ALL tokens and the FULL vocabulary:
 The samples include the first and last tokens and vocabulary rows, tile
 boundaries, the ragged tail, ignored tokens and labels of sampled tokens.
 
+Variants with a logit transform (the chunked call's multiply / divide /
+softcap / temperature keywords on the Unsloth GRPO page) reuse a workload's
+inputs; the transform's values are stored in the file beside the results.  The
+softcap variant caps at about four standard deviations of these logits, so the
+tanh is far from linear over the top of each row.
+
 Usage:  python tests/golden/make_golden.py [workload ...]
 """
 from __future__ import annotations
@@ -27,6 +33,12 @@ from chunked_lm_head_amd import synth  # noqa: E402  (inputs only)
 from oracle import flce_oracle as o  # noqa: E402
 
 FULL = ("single_chunk", "qwen3_8b_sft", "grpo_logprob", "long_context")
+# name -> (workload, transform)
+VARIANTS = {
+    "qwen3_8b_sft_softcap": ("qwen3_8b_sft", dict(softcap=5.0, temperature=0.7)),
+    "single_chunk_scaled": ("single_chunk",
+                            dict(scale_multiply=1.5, scale_divide=1.2, temperature=0.8)),
+}
 
 
 def sample_tokens(w: synth.Workload, labels: np.ndarray, rng) -> np.ndarray:
@@ -53,28 +65,34 @@ def sample_vocab(w: synth.Workload, labels: np.ndarray, tokens: np.ndarray, rng)
 
 
 def make(name: str) -> str:
-    w = synth.WORKLOADS[name]
+    base, xf = VARIANTS.get(name, (name, {}))
+    w = synth.WORKLOADS[base]
+    tr = o.LogitTransform(**xf) if xf else None
     t0 = time.time()
     x = synth.make_inputs(w)
     rng = np.random.default_rng(w.seed + 77)
-    f = o.forward(x.hidden, x.weight, x.labels, synth.IGNORE_INDEX, w.mode)
+    f = o.forward(x.hidden, x.weight, x.labels, synth.IGNORE_INDEX, w.mode, transform=tr)
     tokens = sample_tokens(w, x.labels, rng)
     vocab = sample_vocab(w, x.labels, tokens, rng)
     if w.reduction == "mean":
         c = o.token_scale(x.labels, w.V, synth.IGNORE_INDEX, w.mode, grad_mean=1.0)
     else:
         c = o.token_scale(x.labels, w.V, synth.IGNORE_INDEX, w.mode, grad_out=x.grad_out)
-    dh = o.grad_hidden_rows(x.hidden, x.weight, x.labels, tokens, c[tokens], synth.IGNORE_INDEX)
-    dw = o.grad_weight_rows(x.hidden, x.weight, x.labels, vocab, c, f.lse)
+    dh = o.grad_hidden_rows(x.hidden, x.weight, x.labels, tokens, c[tokens], synth.IGNORE_INDEX,
+                            transform=tr)
+    dw = o.grad_weight_rows(x.hidden, x.weight, x.labels, vocab, c, f.lse, transform=tr)
+    tv = o.LogitTransform(**xf)
     path = os.path.join(HERE, f"{name}.npz")
     np.savez(path, tokens=tokens, out=f.out[tokens], lse=f.lse[tokens], mean=np.float64(f.mean),
              n_valid=np.int64(f.n_valid), vocab=vocab, dh=dh.astype(np.float32),
              dw=dw.astype(np.float32), dw_norm_rows=np.linalg.norm(dw, axis=1),
-             seed=np.int64(w.seed))
+             seed=np.int64(w.seed), workload=np.str_(base),
+             transform=np.array([tv.scale_multiply, tv.scale_divide, tv.softcap,
+                                 tv.temperature], dtype=np.float64))
     print(f"{name}: {time.time() - t0:.0f} s -> {path}", flush=True)
     return path
 
 
 if __name__ == "__main__":
-    for n in (sys.argv[1:] or FULL):
+    for n in (sys.argv[1:] or FULL + tuple(VARIANTS)):
         make(n)

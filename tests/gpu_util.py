@@ -18,8 +18,20 @@ def bf16_tensor(bits: np.ndarray, dev) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
+def binding_transform(tr) -> dict:
+    """Keyword arguments of the binding for a transform given as
+    (multiply, divide, softcap, temperature) or an object with those fields."""
+    if tr is None:
+        return {}
+    if not isinstance(tr, (tuple, list, np.ndarray)):
+        tr = (tr.scale_multiply, tr.scale_divide, tr.softcap, tr.temperature)
+    m, d, c, t = (float(v) for v in tr)
+    return dict(logit_scale_multiply=m, logit_scale_divide=d, logit_softcapping=c,
+                temperature=t)
+
+
 def run(x: synth.Inputs, *, chunk_rows=None, mode=None, grad_out=None, grad_mean=1.0,
-        labels=None, weight_bits=None, accumulate_into=None):
+        labels=None, weight_bits=None, accumulate_into=None, transform=None):
     """Forward + backward through the library; returns numpy arrays."""
     from chunked_lm_head_amd import flce
 
@@ -30,7 +42,8 @@ def run(x: synth.Inputs, *, chunk_rows=None, mode=None, grad_out=None, grad_mean
     h = bf16_tensor(x.hidden, dev)
     W = bf16_tensor(x.weight if weight_bits is None else weight_bits, dev)
     y = torch.from_numpy(x.labels if labels is None else labels).to(dev)
-    out, lse, mean = flce.forward(h, W, y, chunk_rows=chunk_rows, mode=mode)
+    xf = binding_transform(transform)
+    out, lse, mean = flce.forward(h, W, y, chunk_rows=chunk_rows, mode=mode, transform=xf)
     g = x.grad_out if grad_out is None else grad_out
     kw = {}
     if g is not None:
@@ -40,7 +53,8 @@ def run(x: synth.Inputs, *, chunk_rows=None, mode=None, grad_out=None, grad_mean
     gw = None
     if accumulate_into is not None:
         gw = torch.from_numpy(accumulate_into.astype(np.float32)).to(dev)
-    dh, dw = flce.backward(h, W, y, lse, chunk_rows=chunk_rows, mode=mode, grad_weight=gw,
+    dh, dw = flce.backward(h, W, y, lse, chunk_rows=chunk_rows, mode=mode, transform=xf,
+                           grad_weight=gw,
                            accumulate=accumulate_into is not None, **kw)
     torch.cuda.synchronize()
     return dict(out=out.cpu().numpy(), lse=lse.cpu().numpy(), mean=float(mean.cpu()),

@@ -47,11 +47,11 @@ def test_shape_checks(flce):
 
 def _fwd(flce, **over):
     args = dict(hidden=16, weight=16, labels=8, T=4, D=64, V=100, ign=-100, cr=16, mode=0,
-                out=4, lse=4, mean=0, ws=16, wsb=1 << 30, stream=0)
+                xf=None, out=4, lse=4, mean=0, ws=16, wsb=1 << 30, stream=0)
     args.update(over)
     return flce.lib.flce_forward(args["hidden"], args["weight"], args["labels"], args["T"],
                                  args["D"], args["V"], args["ign"], args["cr"], args["mode"],
-                                 args["out"], args["lse"], args["mean"] or None, args["ws"],
+                                 args["xf"], args["out"], args["lse"], args["mean"] or None, args["ws"],
                                  args["wsb"], args["stream"] or None)
 
 
@@ -68,13 +68,42 @@ def test_forward_rejects_before_launch(flce):
 def test_backward_rejects_before_launch(flce):
     b = flce.lib.flce_backward
     # neither grad given
-    assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, None, None, 16, 16, 0, 16, 1 << 30, None) == 1
+    assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, None, None, None, 16, 16, 0, 16, 1 << 30, None) == 1
     # both given
-    assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, 4, 4, 16, 16, 0, 16, 1 << 30, None) == 1
+    assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, None, 4, 4, 16, 16, 0, 16, 1 << 30, None) == 1
     # grad_weight missing
-    assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, 4, None, 16, None, 0, 16, 1 << 30, None) == 1
+    assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, None, 4, None, 16, None, 0, 16, 1 << 30, None) == 1
     # tiny workspace
-    assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, 4, None, 16, 16, 0, 16, 8, None) == 3
+    assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, None, 4, None, 16, 16, 0, 16, 8, None) == 3
+
+
+BAD_TRANSFORMS = [
+    (-1.0, 0.0, 0.0, 1.0),            # negative multiply
+    (0.0, -2.0, 0.0, 1.0),            # negative divide
+    (0.0, 0.0, -30.0, 1.0),           # negative softcap
+    (0.0, 0.0, 0.0, 0.0),             # zero temperature
+    (0.0, 0.0, 0.0, -1.0),            # negative temperature
+    (float("nan"), 0.0, 0.0, 1.0),
+    (0.0, 0.0, float("inf"), 1.0),
+    (0.0, 0.0, 0.0, float("inf")),
+    (1e30, 1e-30, 0.0, 1.0),          # combined scale overflows fp32
+    (0.0, 0.0, 1e-39, 1.0),           # 1 / softcap overflows fp32
+]
+
+
+@pytest.mark.parametrize("vals", BAD_TRANSFORMS)
+def test_invalid_logit_transform_rejected(flce, vals):
+    xf = ctypes.byref(flce.LogitTransform(*vals))
+    assert _fwd(flce, xf=xf) == 1
+    assert b"transform" in flce.lib.flce_last_error()
+    b = flce.lib.flce_backward
+    assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, xf, 4, None, 16, 16, 0, 16, 1 << 30,
+             None) == 1
+
+
+def test_identity_transform_is_none(flce):
+    assert flce.make_transform() is None
+    assert flce.make_transform(temperature=0.7) is not None
 
 
 def test_workspace_bound_independent_of_tokens_times_vocab(flce):
