@@ -44,6 +44,7 @@ constexpr int64_t kMaxTV = (int64_t)1 << 30;  // T and V each
 constexpr int64_t kRowBlockMax = 8192;
 constexpr int64_t kFwdTargetWG = 2048;
 constexpr int64_t kDhTargetWG = 512;
+constexpr int64_t kCUs = 256;  // compute units of an MI355X (8 XCDs of 32)
 constexpr int64_t kDhPartialCap = (int64_t)128 << 20;  // bytes of split-K partial sums
 constexpr int64_t kI32Bytes = ((int64_t)1 << 31) - 1;
 
@@ -406,15 +407,18 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
       g.V = (int)V;
       g.rb0 = (int)rb0;
       g.vc0 = (int)vc0;
-      g.tiles_m = (int)(p.Vc / kTile);
-      g.tiles_n = (int)(p.R / kTile);
+      g.n_vt = (int)cdiv(vcount, kTile);
+      g.tiles_n = (int)cdiv(rcount, kTile);
+      // about one workgroup per CU, each walking n_vt / vsplits vocabulary tiles
+      g.vsplits = (int)std::min<int64_t>(g.n_vt, std::max<int64_t>(1, cdiv(kCUs, g.tiles_n)));
       g.xf = xf;
       g.G = G;
       g.Gp = (int)p.Vc;
+      const unsigned grid = (unsigned)(g.tiles_n * g.vsplits);
       if (cap)
-        bwd_grad_kernel<true><<<(unsigned)(g.tiles_m * g.tiles_n), kThreads, 0, s>>>(g);
+        bwd_grad_kernel<true><<<grid, kThreads, 0, s>>>(g);
       else
-        bwd_grad_kernel<false><<<(unsigned)(g.tiles_m * g.tiles_n), kThreads, 0, s>>>(g);
+        bwd_grad_kernel<false><<<grid, kThreads, 0, s>>>(g);
       FLCE_TRY(launched("bwd_grad"));
 
       BwdDhParams h;

@@ -367,92 +367,112 @@ struct BwdGradParams {
   int64_t ignore_index;
   int T, D, V;
   int rb0, vc0;          // first token / vocabulary row of this block
-  int tiles_m, tiles_n;  // vocabulary tiles of the chunk, token tiles of the row block
+  int n_vt;              // vocabulary tiles of the chunk that hold rows < V
+  int tiles_n, vsplits;  // token tiles of the row block; vocabulary ranges per token tile
   Xform xf;              // logit transform; G is the gradient with respect to the raw logits
   uint16_t *G;           // [R, Gp] bf16, row = token - rb0, col = vocab - vc0
   int Gp;
 };
 
-constexpr int kGPitch = kTile * 2 + 16;                 // bytes per LDS row of the G tile
-constexpr int kLdsGrad = (kTile * kGPitch > kPipeBytes) ? kTile * kGPitch : kPipeBytes;
-
+// G tiles of one row block and vocabulary chunk.  A workgroup keeps one
+// token tile (the B operand, H rows) and walks a contiguous range of the
+// chunk's vocabulary tiles, as the forward does: the next tile's first stages
+// are issued before the current tile's epilogue, which writes its G values
+// straight from registers (8 bytes per lane: four consecutive vocabulary
+// entries of one token), so the load ring stays busy across tiles.  Token
+// tiles past T and vocabulary tiles past V are skipped: no consumer reads
+// those G rows, and the columns of a partial tile past V come out as exact
+// zeros (their logits are -inf).
 template <bool kCap>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(1, 1))) bwd_grad_kernel(BwdGradParams p) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[kLdsGrad];
+  __shared__ __attribute__((aligned(16))) char smem_raw[kPipeBytes];
   lds_t *smem = (lds_t *)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  int tm, tn;
-  grouped_tile(xcd_contiguous(blockIdx.x, gridDim.x), p.tiles_m, p.tiles_n, 8, tm, tn);
-  const int v0 = p.vc0 + tm * kTile;
+  int tn, sp;
+  grouped_tile(xcd_contiguous(blockIdx.x, gridDim.x), p.tiles_n, p.vsplits, 8, tn, sp);
+  const int vt0 = (int)((int64_t)sp * p.n_vt / p.vsplits);
+  const int vt1 = (int)((int64_t)(sp + 1) * p.n_vt / p.vsplits);
   const int t0 = p.rb0 + tn * kTile;
+  if (t0 >= p.T || vt0 >= vt1) return;
 
-  const int vw = v0 + wm * 128;
-  Acc acc;
-  acc.init_rows(p.V - vw, lane);  // rows past the vocabulary end at -inf, i.e. G = 0
-  if (v0 < p.V && t0 < p.T) {
-    OperandK A, B;
-    A.init(p.weight + (size_t)v0 * p.D, p.D, min(kTile, p.V - v0), p.D, wave, lane);
-    B.init(p.hidden + (size_t)t0 * p.D, p.D, min(kTile, p.T - t0), p.D, wave, lane);
-    tile_mainloop(A, B, (p.D + kKS - 1) / kKS, smem, acc, wave, lane);
-  }
-
+  // Per-token values of this lane's 8 token columns, loaded before any DMA.
+  float cc[8], l2[8];
+  int yy[8];
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {
-    const int tl = wn * 128 + nb * 16 + (lane & 15);  // token within the tile
-    const int t = t0 + tl;                            // < rb0 + R <= T_pad
-    const float c = p.c[t];
-    const float l2 = p.lse2[t];
-    int y = -1;
-    if (c != 0.f) y = (int)p.labels[t];  // c != 0 implies 0 <= y < V
-    const int lr = label_reg(y - vw, lane);
-    const bool any_label = __builtin_amdgcn_ballot_w64(lr >= 0) != 0;
-    // uncapped: G = c s (P - onehot), P = 2^(z s log2 e - l2), s the whole scale
-    const float cs = c * p.xf.zscale, ks = p.xf.zscale * kLog2e;
-    // capped: G = c (P - onehot) dz'/dz, dz'/dz = scale (1 - t^2) / temperature
-    const float dscale = p.xf.zscale * p.xf.inv_temp;
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      float g[4], d[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float z = acc_read(acc.v[mb][nb][e]);
-        if constexpr (kCap) {
-          float tt;
-          const float zt = xform_cap(z, p.xf, tt);
-          g[e] = fast_exp2(__builtin_fmaf(zt, kLog2e, -l2));
-          d[e] = c * dscale * (1.f - tt * tt);
-        } else {
-          g[e] = cs * fast_exp2(__builtin_fmaf(z, ks, -l2));
-        }
-      }
-      if (any_label) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (lr == mb * 4 + e) g[e] -= kCap ? 1.f : cs;
-      }
-      if constexpr (kCap) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) g[e] *= d[e];
-      }
-      u32x2 w;
-      w[0] = pack_bf16(g[0], g[1]);
-      w[1] = pack_bf16(g[2], g[3]);
-      const int vl = wm * 128 + acc_row(mb, 0, lane);  // 4 consecutive vocabulary rows
-      *(lds_u32x2 *)(smem + tl * kGPitch + vl * 2) = w;
-    }
+    const int t = t0 + wn * 128 + nb * 16 + (lane & 15);  // < rb0 + R <= T_pad
+    cc[nb] = p.c[t];
+    l2[nb] = p.lse2[t];
+    yy[nb] = -1;
+    if (cc[nb] != 0.f) yy[nb] = (int)p.labels[t];  // c != 0 implies 0 <= y < V
   }
+  // uncapped: G = c s (P - onehot), P = 2^(z s log2 e - l2), s the whole scale
+  const float ks = p.xf.zscale * kLog2e;
+  // capped: G = c (P - onehot) dz'/dz, dz'/dz = scale (1 - t^2) / temperature
+  const float dscale = p.xf.zscale * p.xf.inv_temp;
+
+  OperandK B;
+  B.init(p.hidden + (size_t)t0 * p.D, p.D, min(kTile, p.T - t0), p.D, wave, lane);
+  const int nk = (p.D + kKS - 1) / kKS;
+  OperandK A;
+  int v0 = p.vc0 + vt0 * kTile;
+  A.init(p.weight + (size_t)v0 * p.D, p.D, min(kTile, p.V - v0), p.D, wave, lane);
+  wait_vmcnt<0>();
   __syncthreads();
-  // LDS [token][vocab] -> G rows, 16 bytes per lane, 512 contiguous bytes per 32 lanes.
-  uint16_t *gbase = p.G + (size_t)(tn * kTile) * p.Gp + tm * kTile;
-#pragma unroll 4
-  for (int i = 0; i < 32; ++i) {
-    const int q = i * kThreads + tid;
-    const int row = q >> 5, col16 = q & 31;
-    const u32x4 v = *(const lds_u32x4 *)(smem + row * kGPitch + col16 * 16);
-    *(u32x4 *)(gbase + (size_t)row * p.Gp + col16 * 8) = v;
+  pipe_prologue(A, B, smem, wave);
+  Acc acc;
+  for (int vt = vt0; vt < vt1; ++vt) {
+    v0 = p.vc0 + vt * kTile;
+    const int vw = v0 + wm * 128;    // first vocabulary row of this wave's half
+    acc.init_rows(p.V - vw, lane);  // rows past the vocabulary end at -inf, i.e. G = 0
+    pipe_run(A, B, nk, smem, acc, wave, lane);
+    if (vt + 1 < vt1) {
+      A.init(p.weight + (size_t)(v0 + kTile) * p.D, p.D, min(kTile, p.V - v0 - kTile), p.D,
+             wave, lane);
+      pipe_prologue(A, B, smem, wave);
+    }
+    uint16_t *gcol = p.G + (vw - p.vc0);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const int tl = t0 - p.rb0 + wn * 128 + nb * 16 + (lane & 15);  // row of G
+      const float c = cc[nb];
+      const int lr = label_reg(yy[nb] - vw, lane);
+      const bool any_label = __builtin_amdgcn_ballot_w64(lr >= 0) != 0;
+      const float cs = c * p.xf.zscale;
+      uint16_t *grow = gcol + (size_t)tl * p.Gp;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        float g[4], d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float z = acc_read(acc.v[mb][nb][e]);
+          if constexpr (kCap) {
+            float tt;
+            const float zt = xform_cap(z, p.xf, tt);
+            g[e] = fast_exp2(__builtin_fmaf(zt, kLog2e, -l2[nb]));
+            d[e] = c * dscale * (1.f - tt * tt);
+          } else {
+            g[e] = cs * fast_exp2(__builtin_fmaf(z, ks, -l2[nb]));
+          }
+        }
+        if (any_label) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (lr == mb * 4 + e) g[e] -= kCap ? 1.f : cs;
+        }
+        if constexpr (kCap) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) g[e] *= d[e];
+        }
+        u32x2 w;
+        w[0] = pack_bf16(g[0], g[1]);
+        w[1] = pack_bf16(g[2], g[3]);
+        *(u32x2 *)(grow + acc_row(mb, 0, lane)) = w;  // 4 consecutive vocabulary rows
+      }
+    }
   }
 }
 
