@@ -479,31 +479,38 @@ __global__ void __launch_bounds__(kThreads)
 // Writes (or adds) a wave's 128 x 128 fp32 accumulator block to row-major
 // memory through a buffer descriptor; lanes whose column lies past `cols`
 // and rows past the descriptor's range are dropped by the hardware.  When
-// adding, the 16 old values of four 16 x 16 blocks are loaded together before
-// any is consumed, so their latencies overlap.
+// adding, the old values of two 16-column blocks (64 per lane) are loaded
+// together before any is consumed: after the K loop the fragment registers
+// are free, and four round trips per tile instead of sixteen keep the
+// epilogue short.
+template <int kNb>
+__device__ __forceinline__ void add_acc_cols(const Acc &acc, __amdgpu_buffer_rsrc_t rs, int ld,
+                                             int row0, int col0, int cols, int nb0, int lane) {
+  uint32_t off[kNb][32];
+  float old[kNb][32];
+#pragma unroll
+  for (int j = 0; j < kNb; ++j) {
+    const int col = col0 + (nb0 + j) * 16 + (lane & 15);
+    const bool col_ok = col < cols;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      off[j][q] = col_ok ? (uint32_t)((row0 + acc_row(q >> 2, q & 3, lane)) * ld + col) * 4u : kOOB;
+      old[j][q] = load_f32(rs, off[j][q]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kNb; ++j)
+#pragma unroll
+    for (int q = 0; q < 32; ++q)
+      store_f32(rs, off[j][q], acc_read(acc.v[q >> 2][nb0 + j][q & 3]) + old[j][q]);
+}
+
 __device__ __forceinline__ void store_acc_block(const Acc &acc, __amdgpu_buffer_rsrc_t rs,
                                                 int ld, int row0, int col0, int cols,
                                                 bool accumulate, int lane) {
   if (accumulate) {
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const int col = col0 + nb * 16 + (lane & 15);
-      const bool col_ok = col < cols;
-#pragma unroll
-      for (int m4 = 0; m4 < 8; m4 += 4) {
-        uint32_t off[16];
-        float old[16];
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int row = row0 + acc_row(m4 + (q >> 2), q & 3, lane);
-          off[q] = col_ok ? (uint32_t)(row * ld + col) * 4u : kOOB;
-          old[q] = load_f32(rs, off[q]);
-        }
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-          store_f32(rs, off[q], acc_read(acc.v[m4 + (q >> 2)][nb][q & 3]) + old[q]);
-      }
-    }
+    for (int nb = 0; nb < 8; nb += 2) add_acc_cols<2>(acc, rs, ld, row0, col0, cols, nb, lane);
   } else {
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
