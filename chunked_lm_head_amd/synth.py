@@ -174,3 +174,76 @@ def make_inputs(w: Workload, *, zero_weight: bool = False) -> Inputs:
             pos = np.arange(w.T) % w.seq_len
             grad[pos < w.prompt_len] = 0.0
     return Inputs(w, hidden, weight, labels, grad)
+
+
+# ---------------------------------------------------------------------------
+# Distillation: a student head and a teacher head over the same vocabulary.
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class DistillWorkload:
+    """Student and teacher hidden states / lm_heads over one vocabulary."""
+
+    name: str
+    T: int                 # flattened tokens
+    Hs: int                # student hidden size
+    Ht: int                # teacher hidden size
+    V: int                 # shared vocabulary
+    chunk_rows: int        # rows per logit chunk (bounds live logit memory)
+    ws_std: float          # student lm_head entries ~ N(0, ws_std^2)
+    wt_std: float          # teacher lm_head entries ~ N(0, wt_std^2)
+    ignore_count: int      # tokens left out of the loss (mask = IGNORE_INDEX)
+    seed: int
+    reduction: str = "mean"  # "mean" (scalar loss) or "none" (per-token upstream grad)
+
+
+DISTILL_WORKLOADS = {
+    "distill_tiny": DistillWorkload("distill_tiny", T=67, Hs=128, Ht=192, V=1000, chunk_rows=16,
+                                    ws_std=1.0 / math.sqrt(128), wt_std=1.0 / math.sqrt(192),
+                                    ignore_count=_ignored(67, 0.10), seed=2001),
+    # student at the Qwen3-8B lm_head shape, a wider teacher over the same vocabulary
+    "distill_qwen3": DistillWorkload("distill_qwen3", T=16384, Hs=4096, Ht=5120, V=151936,
+                                     chunk_rows=256, ws_std=0.02, wt_std=0.02,
+                                     ignore_count=_ignored(16384, 0.05), seed=2002),
+}
+
+
+def distill_custom(name: str, T: int, Hs: int, Ht: int, V: int, *, chunk_rows: int = 256,
+                   ws_std: Optional[float] = None, wt_std: Optional[float] = None,
+                   ignore_frac: float = 0.0, reduction: str = "mean",
+                   seed: int = 7) -> DistillWorkload:
+    """A distillation workload of arbitrary shape with the same recipe (for tests)."""
+    return DistillWorkload(name, T=T, Hs=Hs, Ht=Ht, V=V, chunk_rows=chunk_rows,
+                           ws_std=1.0 / math.sqrt(Hs) if ws_std is None else ws_std,
+                           wt_std=1.0 / math.sqrt(Ht) if wt_std is None else wt_std,
+                           ignore_count=_ignored(T, ignore_frac), seed=seed,
+                           reduction=reduction)
+
+
+@dataclasses.dataclass
+class DistillInputs:
+    workload: DistillWorkload
+    s_hidden: np.ndarray          # uint16 bf16 bits [T, Hs]
+    s_weight: np.ndarray          # uint16 bf16 bits [V, Hs]
+    t_hidden: np.ndarray          # uint16 bf16 bits [T, Ht]
+    t_weight: np.ndarray          # uint16 bf16 bits [V, Ht]
+    labels: np.ndarray            # int64 [T]: IGNORE_INDEX for left-out tokens, else 0
+    grad_out: Optional[np.ndarray]  # float32 [T] upstream dL/d kl, or None (mean)
+
+
+def make_distill_inputs(w: DistillWorkload) -> DistillInputs:
+    """Draw the inputs of distillation workload ``w`` (hidden ~ N(0, 1))."""
+    root = np.random.SeedSequence(w.seed)
+    s_sh, s_sw, s_th, s_tw, s_ign, s_grad = root.spawn(6)
+    s_hidden = normal_bf16_matrix(s_sh, w.T, w.Hs, 1.0)
+    s_weight = normal_bf16_matrix(s_sw, w.V, w.Hs, w.ws_std)
+    t_hidden = normal_bf16_matrix(s_th, w.T, w.Ht, 1.0)
+    t_weight = normal_bf16_matrix(s_tw, w.V, w.Ht, w.wt_std)
+    labels = np.zeros(w.T, dtype=np.int64)
+    if w.ignore_count:
+        idx = np.random.default_rng(s_ign).permutation(w.T)[: w.ignore_count]
+        labels[idx] = IGNORE_INDEX
+    grad = None
+    if w.reduction == "none":
+        grad = np.random.default_rng(s_grad).standard_normal(w.T, dtype=np.float32)
+    return DistillInputs(w, s_hidden, s_weight, t_hidden, t_weight, labels, grad)

@@ -1,0 +1,65 @@
+"""The distillation oracle against its pins, and mutants of it that some pin must catch."""
+import os
+import sys
+import types
+import warnings
+
+import pytest
+
+import distill_pins as pins
+from oracle import distill_oracle as d
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "distill_oracle.py")
+
+
+@pytest.mark.parametrize("check", pins.ALL_CHECKS, ids=lambda f: f.__name__)
+def test_distill_pin(check):
+    check(d)
+
+
+MUTANTS = {
+    "reverse_kl": ("kl[r0:r1] = (np.exp(log_pt) * (log_pt - log_ps)).sum(axis=1)",
+                   "kl[r0:r1] = (np.exp(log_ps) * (log_ps - log_pt)).sum(axis=1)"),
+    "cross_entropy_not_kl": ("kl[r0:r1] = (np.exp(log_pt) * (log_pt - log_ps)).sum(axis=1)",
+                             "kl[r0:r1] = (np.exp(log_pt) * (-log_ps)).sum(axis=1)"),
+    "grad_sign": ("g = (np.exp(_log_softmax(zs)) - np.exp(_log_softmax(zt))) * c[:, None]",
+                  "g = (np.exp(_log_softmax(zt)) - np.exp(_log_softmax(zs))) * c[:, None]"),
+    "teacher_untransformed": ("        zt, _ = _rows(ht, wt, transform, r0, r1)\n        lse_s",
+                              "        zt, _ = _rows(ht, wt, None, r0, r1)\n        lse_s"),
+    "mean_over_all_tokens": ("mean = float(kl[valid].sum() / n_valid) if n_valid else 0.0",
+                             "mean = float(kl.sum() / T)"),
+    "masked_tokens_get_grad": ("    return np.where(valid, g, 0.0)", "    return g"),
+    "no_chain_rule": ("return g if dzs is None else g * dzs", "return g"),
+    "weight_rows_no_teacher": ("g = np.exp(zs - np.asarray(lse_s)[:, None]) - np.exp(zt - np.asarray(lse_t)[:, None])",
+                               "g = np.exp(zs - np.asarray(lse_s)[:, None])"),
+    "lse_swapped": ("        log_pt = zt - lse_t[r0:r1, None]", "        log_pt = zt - lse_s[r0:r1, None]"),
+}
+
+
+def _mutant(name):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site not found once: {old!r}"
+    modname = f"distill_oracle_mutant_{name}"
+    mod = types.ModuleType(modname)
+    sys.modules[modname] = mod          # dataclasses look the module up by name
+    try:
+        exec(compile(src.replace(old, new), SRC, "exec"), mod.__dict__)
+    finally:
+        del sys.modules[modname]
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_distill_mutant_is_caught(name):
+    mod = _mutant(name)
+    caught = []
+    for check in pins.ALL_CHECKS:
+        with warnings.catch_warnings():
+            warnings.simplefilter("ignore")
+            try:
+                check(mod)
+            except (AssertionError, ValueError, FloatingPointError, IndexError):
+                caught.append(check.__name__)
+    assert caught, f"mutant {name} passed every pin"
