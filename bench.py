@@ -118,6 +118,9 @@ def main():
         gemm_ceiling(synth.WORKLOADS[args.workload])
         return
 
+    if args.workload in synth.DISTILL_WORKLOADS:
+        distill_main(args)
+        return
     w = synth.WORKLOADS[args.workload]
     chunk_rows = args.chunk_rows or w.chunk_rows
     xf_vals = dict(scale_multiply=args.logit_scale_multiply, scale_divide=args.logit_scale_divide,
@@ -230,6 +233,107 @@ def main():
         line["cpu_baseline"] = cpu_baseline(x, min(args.cpu_sample_tokens, T),
                                            args.cpu_sample_vocab, xf_vals if has_xf else None)
     print(json.dumps(line), flush=True)
+
+
+def distill_main(args) -> None:
+    """One step = one flce_distill call with the mean's gradients: both heads'
+    log-sum-exps, then per block the teacher's probabilities and the student's
+    gradient, dH and dW.  Work: teacher 2 x 2TVDt, student 4 x 2TVDs FLOPs."""
+    import numpy as np
+    import torch
+
+    from chunked_lm_head_amd import flce, synth
+
+    w = synth.DISTILL_WORKLOADS[args.workload]
+    chunk_rows = args.chunk_rows or w.chunk_rows
+    xf = dict(logit_scale_multiply=args.logit_scale_multiply,
+              logit_scale_divide=args.logit_scale_divide,
+              logit_softcapping=args.logit_softcapping, temperature=args.temperature)
+    t_gen = time.perf_counter()
+    x = synth.make_distill_inputs(w)
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    sh, sw, th, tw = bf16(x.s_hidden), bf16(x.s_weight), bf16(x.t_hidden), bf16(x.t_weight)
+    y = torch.from_numpy(x.labels).to(dev)
+    T, Ds, Dt, V = w.T, w.Hs, w.Ht, w.V
+    ws = torch.empty(flce.distill_workspace_bytes(T, Ds, Dt, V, chunk_rows), dtype=torch.uint8,
+                     device=dev)
+    kl = torch.empty(T, dtype=torch.float32, device=dev)
+    mean = torch.empty((), dtype=torch.float32, device=dev)
+    dh = torch.empty((T, Ds), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((V, Ds), dtype=torch.float32, device=dev)
+    one = torch.ones((), dtype=torch.float32, device=dev)
+
+    def step():
+        flce.distill(sh, sw, th, tw, y, chunk_rows=chunk_rows, transform=xf, grad_mean=one,
+                     grad_hidden=dh, grad_weight=dw, workspace=ws, kl=kl, mean=mean)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    flops = 4.0 * T * V * Dt + 8.0 * T * V * Ds
+    achieved = flops / (ms / 1e3)
+    line = {
+        "metric": "distillation fwd+bwd tokens/s (student and teacher LM heads)",
+        "value": round(T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "student_hidden": Ds,
+                   "teacher_hidden": Dt, "vocab": V, "chunk_rows": chunk_rows,
+                   "masked_tokens": w.ignore_count, "loss": "mean KL(teacher || student)"},
+        "workspace_bytes": int(ws.numel()),
+        "roofline": {
+            "kernel": "whole flce_distill call (2 lse passes, teacher and student block passes, "
+                      "dH, dW)",
+            "bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": PEAK_BF16 / 1e12,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4), "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+        },
+    }
+    print(f"[bench] {args.workload}: inputs drawn in {t_gen:.1f} s; step {ms:.3f} ms",
+          file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = distill_cpu_baseline(x, min(args.cpu_sample_tokens, T),
+                                                    args.cpu_sample_vocab)
+    print(json.dumps(line), flush=True)
+
+
+def distill_cpu_baseline(x, n_tokens: int, n_vocab: int) -> dict:
+    """The distillation oracle, untouched, on the first n_tokens tokens against the first
+    n_vocab vocabulary rows of both heads; the rate is scaled by n_vocab / V."""
+    from oracle import distill_oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    V = x.s_weight.shape[0]
+    n_vocab = min(n_vocab, V)
+    args = (x.s_hidden[:n_tokens], x.s_weight[:n_vocab], x.t_hidden[:n_tokens],
+            x.t_weight[:n_vocab], x.labels[:n_tokens])
+    t0 = time.perf_counter()
+    distill_oracle.forward(*args)
+    distill_oracle.backward(*args, grad_mean=1.0)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_tokens / dt * n_vocab / V, 3), "unit": "tokens/s",
+            "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n_tokens} tokens x first {n_vocab} of {V} vocabulary rows of "
+                      f"both heads, float64 numpy forward + backward in {dt:.1f} s; rate scaled "
+                      f"by {n_vocab}/{V}"}
 
 
 def mfma_ceiling() -> None:

@@ -22,7 +22,7 @@
 #include <cmath>
 
 #include "flce.h"
-#include "flce_kernels.hpp"
+#include "flce_distill.hpp"
 
 namespace {
 
@@ -74,6 +74,39 @@ flce_status check_shape(int64_t T, int64_t D, int64_t V, int64_t chunk_rows) {
   return FLCE_OK;
 }
 
+// Row block R (tokens) and vocabulary chunk (tiles) of a staged block of
+// elem_bytes bytes per (token, vocabulary) element, bounded by the fp32 logits
+// of one chunk of chunk_rows rows, chunk_rows * V * 4 bytes (at least one tile);
+// the widest array of the block must stay below 2 GiB (32-bit tile addressing),
+// as must the lm_head rows of one chunk (D bf16 values each).
+void block_shape(int64_t n_tt, int64_t n_vt, int64_t D, int64_t V, int64_t chunk_rows,
+                 int64_t elem_bytes, int64_t widest_bytes, int64_t &R, int64_t &tiles_per_chunk,
+                 int64_t &n_vc) {
+  if (chunk_rows > kMaxTV) chunk_rows = kMaxTV;
+  const int64_t cap = std::max<int64_t>(chunk_rows * V * 4 / elem_bytes, (int64_t)kTile * kTile);
+  const int64_t vc_lim = std::max<int64_t>(kTile, (kI32Bytes / (2 * D)) / kTile * kTile);
+  R = std::min<int64_t>(kRowBlockMax, n_tt * kTile);
+  int64_t n_rb = cdiv(n_tt * kTile, R);
+  R = cdiv(n_tt, n_rb) * kTile;
+  int64_t vc_max = cap / R / kTile * kTile;
+  if (vc_max < kTile) {
+    R = std::max<int64_t>(kTile, cap / kTile / kTile * kTile);
+    n_rb = cdiv(n_tt * kTile, R);
+    R = cdiv(n_tt, n_rb) * kTile;
+    vc_max = kTile;
+  }
+  vc_max = std::min(vc_max, vc_lim);
+  vc_max = std::min(vc_max,
+                    std::max<int64_t>(kTile, (kI32Bytes / (widest_bytes * R)) / kTile * kTile));
+  // Chunks of a multiple of 16 vocabulary tiles keep the dW grid (chunk tiles x
+  // 16 hidden tiles at D = 4096) a multiple of the 256 CUs.
+  tiles_per_chunk = vc_max / kTile;
+  if (tiles_per_chunk >= 16 && (tiles_per_chunk / 16 * 16) * 20 >= tiles_per_chunk * 17)
+    tiles_per_chunk = tiles_per_chunk / 16 * 16;
+  tiles_per_chunk = std::min(tiles_per_chunk, n_vt);
+  n_vc = cdiv(n_vt, tiles_per_chunk);
+}
+
 flce_status make_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows, Plan &p) {
   flce_status st = check_shape(T, D, V, chunk_rows);
   if (st != FLCE_OK) return st;
@@ -89,30 +122,9 @@ flce_status make_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows, Plan 
   p.splits = std::min<int64_t>(std::max<int64_t>(cdiv(kFwdTargetWG, p.n_tt), 1), p.n_vt);
   p.n_cblk = cdiv(Tn, 256);
 
-  // Backward blocking.  cap = bf16 gradient values allowed = chunk_rows*V*4 / 2.
-  if (chunk_rows > kMaxTV) chunk_rows = kMaxTV;
-  const int64_t cap = std::max<int64_t>(chunk_rows * V * 2, (int64_t)kTile * kTile);
-  // 32-bit tile addressing: any operand spanned by one tile stays below 2 GiB.
-  const int64_t vc_lim = std::max<int64_t>(kTile, (kI32Bytes / (2 * D)) / kTile * kTile);
-  int64_t R = std::min<int64_t>(kRowBlockMax, p.n_tt * kTile);
-  int64_t n_rb = cdiv(p.n_tt * kTile, R);
-  R = cdiv(p.n_tt, n_rb) * kTile;
-  int64_t vc_max = cap / R / kTile * kTile;
-  if (vc_max < kTile) {
-    R = std::max<int64_t>(kTile, cap / kTile / kTile * kTile);
-    n_rb = cdiv(p.n_tt * kTile, R);
-    R = cdiv(p.n_tt, n_rb) * kTile;
-    vc_max = kTile;
-  }
-  vc_max = std::min(vc_max, vc_lim);
-  vc_max = std::min(vc_max, std::max<int64_t>(kTile, (kI32Bytes / (2 * R)) / kTile * kTile));
-  // Chunks of a multiple of 16 vocabulary tiles keep the dW grid (chunk tiles x
-  // 16 hidden tiles at D = 4096) a multiple of the 256 CUs.
-  int64_t tiles_per_chunk = vc_max / kTile;
-  if (tiles_per_chunk >= 16 && (tiles_per_chunk / 16 * 16) * 20 >= tiles_per_chunk * 17)
-    tiles_per_chunk = tiles_per_chunk / 16 * 16;
-  tiles_per_chunk = std::min(tiles_per_chunk, p.n_vt);
-  const int64_t n_vc = cdiv(p.n_vt, tiles_per_chunk);
+  // Backward blocking: bf16 gradient values, 2 bytes each.
+  int64_t R, n_vc, tiles_per_chunk;
+  block_shape(p.n_tt, p.n_vt, D, V, chunk_rows, 2, 2, R, tiles_per_chunk, n_vc);
   p.R = R;
   p.n_rb = cdiv(p.n_tt * kTile, R);
   p.Tb = p.n_rb * R;
@@ -144,6 +156,92 @@ flce_status make_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows, Plan 
 }
 
 bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+// Schedule of the distillation call: the forward layout for the two
+// log-sum-exps, and blocks of R rows x Vc vocabulary entries holding the
+// teacher's fp32 probabilities and the student's bf16 gradient (6 bytes per
+// element) within the fp32 logits of one chunk of chunk_rows rows.
+struct DistillPlan {
+  int64_t T, Ds, Dt, V, chunk_rows;
+  int64_t n_tt, n_vt, splits, T_pad, n_cblk;
+  int64_t R, n_rb, Tb, Vc, n_vc, vsplits, dh_splits;
+  size_t off_pm, off_ps, off_zl, off_bs, off_bc;
+  size_t off_lse_s, off_lse_t, off_l2s, off_l2t, off_c, off_A, off_B;
+  size_t off_P, off_G, off_pa, off_pb, off_dh;
+  size_t total;
+};
+
+flce_status make_distill_plan(int64_t T, int64_t Ds, int64_t Dt, int64_t V, int64_t chunk_rows,
+                              DistillPlan &p) {
+  flce_status st = check_shape(T, Ds, V, chunk_rows);
+  if (st != FLCE_OK) return st;
+  st = check_shape(T, Dt, V, chunk_rows);
+  if (st != FLCE_OK) return st;
+  memset(&p, 0, sizeof(p));
+  p.T = T;
+  p.Ds = Ds;
+  p.Dt = Dt;
+  p.V = V;
+  p.chunk_rows = chunk_rows;
+  const int64_t Tn = std::max<int64_t>(T, 1);
+  p.n_tt = cdiv(Tn, kTile);
+  p.n_vt = cdiv(V, kTile);
+  p.T_pad = p.n_tt * kTile;
+  p.splits = std::min<int64_t>(std::max<int64_t>(cdiv(kFwdTargetWG, p.n_tt), 1), p.n_vt);
+  p.n_cblk = cdiv(Tn, 256);
+  int64_t R, tiles_per_chunk, n_vc;
+  block_shape(p.n_tt, p.n_vt, std::max(Ds, Dt), V, chunk_rows, 6, 4, R, tiles_per_chunk, n_vc);
+  // Prefer chunks of a multiple of 16 vocabulary tiles (whole-wave dW grids and
+  // tile launches): halve the row block while that makes room for them.
+  const int64_t cap = std::max<int64_t>(std::min<int64_t>(chunk_rows, kMaxTV) * V * 4 / 6,
+                                        (int64_t)kTile * kTile);
+  const int64_t vc_lim = std::max<int64_t>(kTile, (kI32Bytes / (2 * std::max(Ds, Dt))) / kTile * kTile);
+  while (tiles_per_chunk < 16 && tiles_per_chunk < p.n_vt && R >= 4 * kTile) {
+    const int64_t half = R / 2 / kTile * kTile;
+    int64_t vc = std::min<int64_t>(cap / half / kTile * kTile, vc_lim);
+    vc = std::min<int64_t>(vc, (kI32Bytes / (4 * half)) / kTile * kTile);
+    int64_t tiles = std::min<int64_t>(vc / kTile, p.n_vt);
+    if (tiles >= 16) tiles = tiles / 16 * 16;
+    if (tiles <= tiles_per_chunk) break;
+    R = half;
+    tiles_per_chunk = tiles;
+    n_vc = cdiv(p.n_vt, tiles);
+  }
+  p.R = R;
+  p.n_rb = cdiv(p.n_tt * kTile, R);
+  p.Tb = p.n_rb * R;
+  p.Vc = tiles_per_chunk * kTile;
+  p.n_vc = n_vc;
+  p.vsplits = std::min<int64_t>(tiles_per_chunk, std::max<int64_t>(1, cdiv(kCUs, R / kTile)));
+  // dH: one workgroup per output tile once the tiles fill the chip (split-K
+  // would add a read-modify-write of the partial sums per chunk).
+  const int64_t dh_tiles = (R / kTile) * cdiv(Ds, kTile);
+  int64_t sp = std::max<int64_t>(1, cdiv(kCUs, dh_tiles));
+  sp = std::min(sp, std::max<int64_t>(1, kDhPartialCap / (R * Ds * 4)));
+  sp = std::min(sp, cdiv(p.Vc, kBK));
+  p.dh_splits = sp;
+
+  size_t off = 0;
+  p.off_pm = off;    off = align256(off + (size_t)p.splits * p.T_pad * 4);
+  p.off_ps = off;    off = align256(off + (size_t)p.splits * p.T_pad * 4);
+  p.off_zl = off;    off = align256(off + (size_t)p.T_pad * 4);
+  p.off_bs = off;    off = align256(off + (size_t)p.n_cblk * 8);
+  p.off_bc = off;    off = align256(off + (size_t)p.n_cblk * 4);
+  p.off_lse_s = off; off = align256(off + (size_t)p.Tb * 4);
+  p.off_lse_t = off; off = align256(off + (size_t)p.Tb * 4);
+  p.off_l2s = off;   off = align256(off + (size_t)p.Tb * 4);
+  p.off_l2t = off;   off = align256(off + (size_t)p.Tb * 4);
+  p.off_c = off;     off = align256(off + (size_t)p.Tb * 4);
+  p.off_A = off;     off = align256(off + (size_t)p.Tb * 4);
+  p.off_B = off;     off = align256(off + (size_t)p.Tb * 4);
+  p.off_P = off;     off = align256(off + (size_t)p.R * p.Vc * 4);
+  p.off_G = off;     off = align256(off + (size_t)p.R * p.Vc * 2);
+  p.off_pa = off;    off = align256(off + (size_t)p.n_vc * p.vsplits * p.R * 4);
+  p.off_pb = off;    off = align256(off + (size_t)p.n_vc * p.vsplits * p.R * 4);
+  p.off_dh = off;    off = align256(off + (size_t)p.dh_splits * p.R * p.Ds * 4);
+  p.total = off;
+  return FLCE_OK;
+}
 
 flce_status check_device() {
   static int cache[64];  // 0 unknown, 1 ok, 2 unsupported
@@ -210,6 +308,64 @@ flce_status make_xform(const flce_logit_transform *t, Xform &x, bool &cap) {
   x.inv_cap = (float)inv_cap;
   x.inv_temp = cap ? (float)inv_temp : 1.f;
   return FLCE_OK;
+}
+
+// dH partial sums and the dW update of one (row block, vocabulary chunk) from
+// its bf16 gradient block G [R, Gp] (token rows, vocabulary columns).
+flce_status launch_dh_dw(const uint16_t *G, int Gp, const void *weight, const void *hidden,
+                         int64_t D, int64_t V, int64_t R, int64_t rb0, int64_t rcount,
+                         int64_t vc0, int64_t vcount, int64_t dh_splits, float *dhacc,
+                         float *grad_weight, bool acc_dh, bool acc_dw, hipStream_t s) {
+  const int tiles_h = (int)cdiv(D, kTile);
+  BwdDhParams h;
+  h.G = G;
+  h.weight = (const uint16_t *)weight;
+  h.Gp = Gp;
+  h.D = (int)D;
+  h.V = (int)V;
+  h.vc0 = (int)vc0;
+  h.vcount = (int)vcount;
+  h.Kc = (int)std::min<int64_t>(Gp, cdiv(vcount, kBK) * kBK);  // G is zero past vcount
+  h.R = (int)R;
+  h.tiles_m = (int)(R / kTile);
+  h.tiles_n = tiles_h;
+  h.splits = (int)dh_splits;
+  h.acc = dhacc;
+  h.accumulate = acc_dh ? 1 : 0;
+  bwd_dh_kernel<<<(unsigned)(h.tiles_m * h.tiles_n * h.splits), kThreads, 0, s>>>(h);
+  FLCE_TRY(launched("bwd_dh"));
+
+  BwdDwParams w;
+  w.G = G;
+  w.hidden = (const uint16_t *)hidden;
+  w.Gp = Gp;
+  w.D = (int)D;
+  w.V = (int)V;
+  w.rb0 = (int)rb0;
+  w.rcount = (int)rcount;
+  w.vc0 = (int)vc0;
+  w.tiles_m = Gp / kTile;
+  w.tiles_n = tiles_h;
+  w.dW = grad_weight;
+  w.accumulate = acc_dw ? 1 : 0;
+  bwd_dw_kernel<<<(unsigned)(w.tiles_m * w.tiles_n), kThreads, 0, s>>>(w);
+  return launched("bwd_dw");
+}
+
+// dH rows of a row block: sum of the split-K partials, rounded to bf16.
+flce_status launch_dh_out(const float *dhacc, void *grad_hidden, int64_t D, int64_t R,
+                          int64_t dh_splits, int64_t rb0, int64_t rcount, hipStream_t s) {
+  BwdDhOutParams o;
+  o.acc = dhacc;
+  o.dH = (uint16_t *)grad_hidden;
+  o.D = (int)D;
+  o.R = (int)R;
+  o.splits = (int)dh_splits;
+  o.rb0 = (int)rb0;
+  o.rcount = (int)rcount;
+  const int64_t work = rcount * (D / 8);
+  bwd_dh_out_kernel<<<(unsigned)std::min<int64_t>(cdiv(work, 256), 8192), 256, 0, s>>>(o);
+  return launched("bwd_dh_out");
 }
 
 flce_status fill(float *dst, int64_t n, float v, hipStream_t s) {
@@ -385,7 +541,6 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
   bwd_prep_kernel<<<1, 1024, 0, s>>>(pr);
   FLCE_TRY(launched("bwd_prep"));
 
-  const int tiles_h = (int)cdiv(D, kTile);
   for (int64_t rb = 0; rb < p.n_rb; ++rb) {
     const int64_t rb0 = rb * p.R;
     const int64_t rcount = std::min<int64_t>(p.R, T - rb0);
@@ -421,51 +576,201 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
         bwd_grad_kernel<false><<<grid, kThreads, 0, s>>>(g);
       FLCE_TRY(launched("bwd_grad"));
 
-      BwdDhParams h;
-      h.G = G;
-      h.weight = (const uint16_t *)weight;
-      h.Gp = (int)p.Vc;
-      h.D = (int)D;
-      h.V = (int)V;
-      h.vc0 = (int)vc0;
-      h.vcount = (int)vcount;
-      h.Kc = (int)std::min<int64_t>(p.Vc, cdiv(vcount, kBK) * kBK);  // G is zero past vcount
-      h.R = (int)p.R;
-      h.tiles_m = (int)(p.R / kTile);
-      h.tiles_n = tiles_h;
-      h.splits = (int)p.dh_splits;
-      h.acc = dhacc;
-      h.accumulate = vc > 0;
-      bwd_dh_kernel<<<(unsigned)(h.tiles_m * h.tiles_n * h.splits), kThreads, 0, s>>>(h);
-      FLCE_TRY(launched("bwd_dh"));
-
-      BwdDwParams w;
-      w.G = G;
-      w.hidden = (const uint16_t *)hidden;
-      w.Gp = (int)p.Vc;
-      w.D = (int)D;
-      w.V = (int)V;
-      w.rb0 = (int)rb0;
-      w.rcount = (int)rcount;
-      w.vc0 = (int)vc0;
-      w.tiles_m = (int)(p.Vc / kTile);
-      w.tiles_n = tiles_h;
-      w.dW = grad_weight;
-      w.accumulate = (accumulate_grad_weight || rb > 0) ? 1 : 0;
-      bwd_dw_kernel<<<(unsigned)(w.tiles_m * w.tiles_n), kThreads, 0, s>>>(w);
-      FLCE_TRY(launched("bwd_dw"));
+      FLCE_TRY(launch_dh_dw(G, (int)p.Vc, weight, hidden, D, V, p.R, rb0, rcount, vc0, vcount,
+                            p.dh_splits, dhacc, grad_weight, vc > 0,
+                            accumulate_grad_weight || rb > 0, s));
     }
-    BwdDhOutParams o;
-    o.acc = dhacc;
-    o.dH = (uint16_t *)grad_hidden;
-    o.D = (int)D;
-    o.R = (int)p.R;
-    o.splits = (int)p.dh_splits;
-    o.rb0 = (int)rb0;
-    o.rcount = (int)rcount;
-    const int64_t work = rcount * (D / 8);
-    bwd_dh_out_kernel<<<(unsigned)std::min<int64_t>(cdiv(work, 256), 8192), 256, 0, s>>>(o);
-    FLCE_TRY(launched("bwd_dh_out"));
+    FLCE_TRY(launch_dh_out(dhacc, grad_hidden, D, p.R, p.dh_splits, rb0, rcount, s));
+  }
+  return FLCE_OK;
+}
+
+size_t flce_distill_workspace_bytes(int64_t T, int64_t Ds, int64_t Dt, int64_t V,
+                                    int64_t chunk_rows) {
+  DistillPlan p;
+  if (make_distill_plan(T, Ds, Dt, V, chunk_rows, p) != FLCE_OK) return 0;
+  return p.total;
+}
+
+flce_status flce_distill(const void *student_hidden, const void *student_weight, int64_t Ds,
+                         const void *teacher_hidden, const void *teacher_weight, int64_t Dt,
+                         const int64_t *labels, int64_t ignore_index, int64_t T, int64_t V,
+                         int64_t chunk_rows, const flce_logit_transform *transform,
+                         float *kl_out, float *mean_out, const float *grad_out,
+                         const float *grad_mean, void *grad_student_hidden,
+                         float *grad_student_weight, int accumulate_grad_weight,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+  g_last_error[0] = 0;
+  DistillPlan p;
+  FLCE_TRY(make_distill_plan(T, Ds, Dt, V, chunk_rows, p));
+  Xform xf;
+  bool cap;
+  FLCE_TRY(make_xform(transform, xf, cap));
+  if (grad_out && grad_mean)
+    return fail(FLCE_ERR_ARG, "give at most one of grad_out and grad_mean");
+  const bool grads = grad_out || grad_mean;
+  if (grads && !grad_student_weight)
+    return fail(FLCE_ERR_ARG, "a gradient was requested but grad_student_weight is NULL");
+  if (grad_student_weight && !aligned(grad_student_weight, 16))
+    return fail(FLCE_ERR_ARG, "grad_student_weight not 16-byte aligned");
+  if (T > 0) {
+    if (!student_hidden || !student_weight || !teacher_hidden || !teacher_weight || !workspace ||
+        (grads && !grad_student_hidden))
+      return fail(FLCE_ERR_ARG, "a required pointer is NULL");
+    if (!aligned(student_hidden, 16) || !aligned(student_weight, 16) ||
+        !aligned(teacher_hidden, 16) || !aligned(teacher_weight, 16) ||
+        !aligned(workspace, 16) || (labels && !aligned(labels, 8)) ||
+        (kl_out && !aligned(kl_out, 4)) || (mean_out && !aligned(mean_out, 4)) ||
+        (grad_out && !aligned(grad_out, 4)) || (grad_mean && !aligned(grad_mean, 4)) ||
+        (grads && !aligned(grad_student_hidden, 16)))
+      return fail(FLCE_ERR_ARG, "misaligned pointer");
+    if (workspace_bytes < p.total)
+      return fail(FLCE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
+                  p.total);
+  }
+  FLCE_TRY(check_device());
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) {
+    if (mean_out) FLCE_TRY(fill(mean_out, 1, 0.f, s));
+    if (grads && !accumulate_grad_weight) FLCE_TRY(fill(grad_student_weight, V * Ds, 0.f, s));
+    return FLCE_OK;
+  }
+
+  char *ws = (char *)workspace;
+  float *lse_s = (float *)(ws + p.off_lse_s), *lse_t = (float *)(ws + p.off_lse_t);
+  float *l2s = (float *)(ws + p.off_l2s), *l2t = (float *)(ws + p.off_l2t);
+  float *cbuf = (float *)(ws + p.off_c);
+  float *Abuf = (float *)(ws + p.off_A), *Bbuf = (float *)(ws + p.off_B);
+  float *Pbuf = (float *)(ws + p.off_P);
+  uint16_t *G = (uint16_t *)(ws + p.off_G);
+  float *part_a = (float *)(ws + p.off_pa), *part_b = (float *)(ws + p.off_pb);
+  float *dhacc = (float *)(ws + p.off_dh);
+
+  // Log-sum-exp of each head: the fused forward kernel without labels.
+  for (int head = 0; head < 2; ++head) {
+    FwdLseParams a;
+    a.hidden = (const uint16_t *)(head ? student_hidden : teacher_hidden);
+    a.weight = (const uint16_t *)(head ? student_weight : teacher_weight);
+    a.labels = nullptr;
+    a.ignore_index = ignore_index;
+    a.T = (int)T;
+    a.D = (int)(head ? Ds : Dt);
+    a.V = (int)V;
+    a.n_tt = (int)p.n_tt;
+    a.n_vt = (int)p.n_vt;
+    a.splits = (int)p.splits;
+    a.T_pad = (int)p.T_pad;
+    a.xf = xf;
+    a.part_m = (float *)(ws + p.off_pm);
+    a.part_s = (float *)(ws + p.off_ps);
+    a.zlab = (float *)(ws + p.off_zl);
+    if (cap)
+      fwd_lse_kernel<true><<<(unsigned)(p.n_tt * p.splits), kThreads, 0, s>>>(a);
+    else
+      fwd_lse_kernel<false><<<(unsigned)(p.n_tt * p.splits), kThreads, 0, s>>>(a);
+    FLCE_TRY(launched("fwd_lse"));
+    DstLseParams l;
+    l.part_m = a.part_m;
+    l.part_s = a.part_s;
+    l.T = (int)T;
+    l.splits = (int)p.splits;
+    l.T_pad = (int)p.T_pad;
+    l.n = (int)p.Tb;
+    l.lse = head ? lse_s : lse_t;
+    l.lse2 = head ? l2s : l2t;
+    dst_lse_kernel<<<(unsigned)cdiv(p.Tb, 256), 256, 0, s>>>(l);
+    FLCE_TRY(launched("dst_lse"));
+  }
+
+  DstPrepParams pr;
+  pr.labels = labels;
+  pr.grad_out = grad_out;
+  pr.grad_mean = grad_mean;
+  pr.ignore_index = ignore_index;
+  pr.T = grads ? (int)T : 0;  // no gradient: c = 0 everywhere
+  pr.n = (int)p.Tb;
+  pr.c = cbuf;
+  dst_prep_kernel<<<1, 1024, 0, s>>>(pr);
+  FLCE_TRY(launched("dst_prep"));
+
+  for (int64_t rb = 0; rb < p.n_rb; ++rb) {
+    const int64_t rb0 = rb * p.R;
+    const int64_t rcount = std::min<int64_t>(p.R, T - rb0);
+    if (rcount <= 0) break;
+    const int64_t tiles_n = cdiv(rcount, kTile);
+    for (int64_t vc = 0; vc < p.n_vc; ++vc) {
+      const int64_t vc0 = vc * p.Vc;
+      const int64_t vcount = std::min<int64_t>(p.Vc, V - vc0);
+      DstTileParams d;
+      d.lse2 = l2t;
+      d.c = cbuf;
+      d.T = (int)T;
+      d.V = (int)V;
+      d.rb0 = (int)rb0;
+      d.vc0 = (int)vc0;
+      d.n_vt = (int)cdiv(vcount, kTile);
+      d.tiles_n = (int)tiles_n;
+      d.vsplits = (int)p.vsplits;
+      d.R = (int)p.R;
+      d.xf = xf;
+      d.P = Pbuf;
+      d.Pp = (int)p.Vc;
+      d.G = G;
+      d.Gp = (int)p.Vc;
+      const unsigned grid = (unsigned)(tiles_n * p.vsplits);
+      // teacher: p_t block and partial sums of A
+      d.hidden = (const uint16_t *)teacher_hidden;
+      d.weight = (const uint16_t *)teacher_weight;
+      d.D = (int)Dt;
+      d.part = part_a + (size_t)vc * p.vsplits * p.R;
+      if (cap)
+        dst_tile_kernel<true, true><<<grid, kThreads, 0, s>>>(d);
+      else
+        dst_tile_kernel<true, false><<<grid, kThreads, 0, s>>>(d);
+      FLCE_TRY(launched("dst_tile teacher"));
+      // student: partial sums of B and the gradient block
+      d.hidden = (const uint16_t *)student_hidden;
+      d.weight = (const uint16_t *)student_weight;
+      d.D = (int)Ds;
+      d.lse2 = l2s;
+      d.part = part_b + (size_t)vc * p.vsplits * p.R;
+      if (cap)
+        dst_tile_kernel<false, true><<<grid, kThreads, 0, s>>>(d);
+      else
+        dst_tile_kernel<false, false><<<grid, kThreads, 0, s>>>(d);
+      FLCE_TRY(launched("dst_tile student"));
+      if (grads)
+        FLCE_TRY(launch_dh_dw(G, (int)p.Vc, student_weight, student_hidden, Ds, V, p.R, rb0,
+                              rcount, vc0, vcount, p.dh_splits, dhacc, grad_student_weight,
+                              vc > 0, accumulate_grad_weight || rb > 0, s));
+    }
+    const int nparts = (int)(p.n_vc * p.vsplits);
+    dst_reduce_kernel<<<(unsigned)cdiv(rcount, 64), 256, 0, s>>>(part_a, nparts, (int)p.R,
+                                                                 (int)rb0, (int)rcount, Abuf);
+    FLCE_TRY(launched("dst_reduce"));
+    dst_reduce_kernel<<<(unsigned)cdiv(rcount, 64), 256, 0, s>>>(part_b, nparts, (int)p.R,
+                                                                 (int)rb0, (int)rcount, Bbuf);
+    FLCE_TRY(launched("dst_reduce"));
+    if (grads)
+      FLCE_TRY(launch_dh_out(dhacc, grad_student_hidden, Ds, p.R, p.dh_splits, rb0, rcount, s));
+  }
+
+  DstCombineParams c;
+  c.A = Abuf;
+  c.B = Bbuf;
+  c.lse_s = lse_s;
+  c.lse_t = lse_t;
+  c.labels = labels;
+  c.ignore_index = ignore_index;
+  c.T = (int)T;
+  c.kl = kl_out;
+  c.blk_sum = (double *)(ws + p.off_bs);
+  c.blk_cnt = (int *)(ws + p.off_bc);
+  dst_combine_kernel<<<(unsigned)p.n_cblk, 256, 0, s>>>(c);
+  FLCE_TRY(launched("dst_combine"));
+  if (mean_out) {
+    fwd_mean_kernel<<<1, 256, 0, s>>>(c.blk_sum, c.blk_cnt, (int)p.n_cblk, mean_out);
+    FLCE_TRY(launched("fwd_mean"));
   }
   return FLCE_OK;
 }

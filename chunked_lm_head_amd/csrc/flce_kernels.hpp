@@ -99,7 +99,7 @@ __device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2
 struct FwdLseParams {
   const uint16_t *hidden;   // [T, D] bf16
   const uint16_t *weight;   // [V, D] bf16
-  const int64_t *labels;    // [T]
+  const int64_t *labels;    // [T], or null: no label logits (zlab is not written)
   int64_t ignore_index;
   int T, D, V;
   int n_tt, n_vt, splits, T_pad;
@@ -136,7 +136,7 @@ __global__ void __launch_bounds__(kThreads)
   for (int nb = 0; nb < 8; ++nb) {
     const int t = t0 + wn * 128 + nb * 16 + (lane & 15);
     int y = -1;
-    if (t < p.T) {
+    if (p.labels && t < p.T) {  // no labels: log-sum-exp only
       const int64_t yy = p.labels[t];
       if (yy != p.ignore_index && yy >= 0 && yy < p.V) y = (int)yy;
     }

@@ -29,7 +29,8 @@ _MODES = {"nll": MODE_NLL, "logprob": MODE_LOGPROB}
 STATUS = {0: "FLCE_OK", 1: "FLCE_ERR_ARG", 2: "FLCE_ERR_SHAPE", 3: "FLCE_ERR_WORKSPACE",
           4: "FLCE_ERR_UNSUPPORTED", 5: "FLCE_ERR_HIP"}
 EXPORTS = ("flce_workspace_bytes", "flce_forward", "flce_backward", "flce_describe_plan",
-           "flce_status_string", "flce_last_error")
+           "flce_status_string", "flce_last_error", "flce_distill_workspace_bytes",
+           "flce_distill")
 
 
 class LogitTransform(ctypes.Structure):
@@ -52,6 +53,11 @@ def _load() -> ctypes.CDLL:
     lib.flce_backward.argtypes = [vp, vp, vp, f32p, i64, i64, i64, i64, i64, ctypes.c_int,
                                   xp, f32p, f32p, vp, f32p, ctypes.c_int, vp, sz, vp]
     lib.flce_backward.restype = ctypes.c_int
+    lib.flce_distill_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.flce_distill_workspace_bytes.restype = sz
+    lib.flce_distill.argtypes = [vp, vp, i64, vp, vp, i64, vp, i64, i64, i64, i64, xp,
+                                 f32p, f32p, f32p, f32p, vp, f32p, ctypes.c_int, vp, sz, vp]
+    lib.flce_distill.restype = ctypes.c_int
     lib.flce_describe_plan.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
     lib.flce_describe_plan.restype = ctypes.c_int
     lib.flce_status_string.argtypes = [ctypes.c_int]
@@ -244,3 +250,119 @@ def selective_log_softmax(hidden, weight, labels, *, ignore_index=-100, chunk_ro
                            temperature)
     return _ChunkedLinearCE.apply(hidden, weight, labels, ignore_index, chunk_rows, "logprob",
                                   "none", xf)
+
+
+# ---------------------------------------------------------------------------
+# Distillation (student and teacher heads over one vocabulary)
+# ---------------------------------------------------------------------------
+
+def distill_workspace_bytes(T: int, Ds: int, Dt: int, V: int, chunk_rows: int = 256) -> int:
+    n = lib.flce_distill_workspace_bytes(T, Ds, Dt, V, chunk_rows)
+    if n == 0:
+        raise ValueError(f"invalid shape T={T} Ds={Ds} Dt={Dt} V={V} chunk_rows={chunk_rows}")
+    return n
+
+
+def distill(student_hidden, student_weight, teacher_hidden, teacher_weight,
+            labels: Optional[torch.Tensor] = None, *, ignore_index: int = -100,
+            chunk_rows: int = 256, transform: Optional[dict] = None,
+            grad_out: Optional[torch.Tensor] = None, grad_mean: Optional[torch.Tensor] = None,
+            grad_hidden: Optional[torch.Tensor] = None,
+            grad_weight: Optional[torch.Tensor] = None, accumulate: bool = False,
+            workspace: Optional[torch.Tensor] = None, kl: Optional[torch.Tensor] = None,
+            mean: Optional[torch.Tensor] = None):
+    """(kl [T], mean [], dHs or None, dWs or None): per-token KL(teacher || student),
+    its mean over kept tokens and, when grad_out or grad_mean is given, the
+    student's gradients (one call; the teacher gets none)."""
+    for t in (student_hidden, student_weight, teacher_hidden, teacher_weight):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("hidden states and lm_heads must be contiguous 2-D bf16 on the GPU")
+    T, Ds = student_hidden.shape
+    V = student_weight.shape[0]
+    Dt = teacher_hidden.shape[1]
+    if (student_weight.shape[1] != Ds or teacher_hidden.shape[0] != T
+            or tuple(teacher_weight.shape) != (V, Dt)):
+        raise ValueError("shape mismatch between student and teacher tensors")
+    dev = student_hidden.device
+    if labels is not None and (labels.dtype != torch.int64 or labels.shape != (T,)
+                               or not labels.is_contiguous() or labels.device != dev):
+        raise ValueError("labels must be a contiguous int64 [T] mask on the same device")
+    if grad_out is not None and grad_mean is not None:
+        raise ValueError("give at most one of grad_out and grad_mean")
+    grads = grad_out is not None or grad_mean is not None
+    for t in (grad_out, grad_mean):
+        if t is not None and (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("grad_out / grad_mean must be contiguous fp32 on the GPU")
+    kl = torch.empty(T, dtype=torch.float32, device=dev) if kl is None else kl
+    mean = torch.empty((), dtype=torch.float32, device=dev) if mean is None else mean
+    if grads:
+        if grad_hidden is None:
+            grad_hidden = torch.empty((T, Ds), dtype=torch.bfloat16, device=dev)
+        if grad_weight is None:
+            if accumulate:
+                raise ValueError("accumulate needs an existing grad_weight")
+            grad_weight = torch.empty((V, Ds), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(distill_workspace_bytes(T, Ds, Dt, V, chunk_rows),
+                                dtype=torch.uint8, device=dev)
+    _check(lib.flce_distill(_ptr(student_hidden), _ptr(student_weight), Ds, _ptr(teacher_hidden),
+                            _ptr(teacher_weight), Dt, _ptr(labels), ignore_index, T, V,
+                            chunk_rows, make_transform(**(transform or {})), _ptr(kl),
+                            _ptr(mean), _ptr(grad_out), _ptr(grad_mean),
+                            _ptr(grad_hidden) if grads else None,
+                            _ptr(grad_weight) if grads else None, 1 if accumulate else 0,
+                            _ptr(workspace), workspace.numel(), _stream(dev)))
+    return kl, mean, (grad_hidden if grads else None), (grad_weight if grads else None)
+
+
+class _ChunkedDistillKL(torch.autograd.Function):
+    """Mean (``reduction="mean"``) or per-token (``"none"``) KL(teacher || student).
+
+    The mean's gradients are computed in the forward call (c = 1 / N_kept) and
+    scaled by the upstream scalar in the backward; per-token reduction calls the
+    library again in the backward with the upstream gradient (recompute)."""
+
+    @staticmethod
+    def forward(ctx, s_hidden, s_weight, t_hidden, t_weight, labels, ignore_index, chunk_rows,
+                reduction, transform):
+        kw = dict(ignore_index=ignore_index, chunk_rows=chunk_rows, transform=transform)
+        need = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
+        if reduction == "mean" and need:
+            one = torch.ones((), dtype=torch.float32, device=s_hidden.device)
+            kl, mean, dh, dw = distill(s_hidden, s_weight, t_hidden, t_weight, labels,
+                                       grad_mean=one, **kw)
+            ctx.save_for_backward(dh, dw)
+        else:
+            kl, mean, _, _ = distill(s_hidden, s_weight, t_hidden, t_weight, labels, **kw)
+            ctx.save_for_backward(s_hidden, s_weight, t_hidden, t_weight, labels)
+        ctx.cfg = (reduction, kw, need)
+        return mean if reduction == "mean" else kl
+
+    @staticmethod
+    def backward(ctx, grad):
+        reduction, kw, need = ctx.cfg
+        if not need:
+            return (None,) * 9
+        if reduction == "mean":
+            dh, dw = ctx.saved_tensors
+            g = grad.float()
+            dh = (dh.float() * g).to(torch.bfloat16)
+            dw = dw * g
+        else:
+            s_hidden, s_weight, t_hidden, t_weight, labels = ctx.saved_tensors
+            _, _, dh, dw = distill(s_hidden, s_weight, t_hidden, t_weight, labels,
+                                   grad_out=grad.float().contiguous(), **kw)
+        return dh, dw.to(torch.bfloat16), None, None, None, None, None, None, None
+
+
+def chunked_distill_kl(student_hidden, student_weight, teacher_hidden, teacher_weight,
+                       labels=None, *, ignore_index=-100, chunk_rows=256, reduction="mean",
+                       logit_scale_multiply=0.0, logit_scale_divide=0.0, logit_softcapping=0.0,
+                       temperature=1.0):
+    """Autograd-aware KL(teacher || student) of two LM heads, chunked (gradients reach
+    the student's hidden states and lm_head only)."""
+    xf = _transform_kwargs(logit_scale_multiply, logit_scale_divide, logit_softcapping,
+                           temperature)
+    return _ChunkedDistillKL.apply(student_hidden, student_weight, teacher_hidden,
+                                   teacher_weight, labels, ignore_index, chunk_rows, reduction,
+                                   xf)

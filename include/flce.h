@@ -147,6 +147,47 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Distillation through two LM heads over one vocabulary (TRL v1.13 article,
+ * speed section: the distillation trainer computes every chunk twice, for the
+ * student and for the teacher).  The pages define no divergence; this call
+ * computes the forward Kullback-Leibler divergence of the student from the
+ * teacher per token,
+ *     kl_t = sum_v p_t,v (log p_t,v - log p_s,v),
+ * p_s = softmax(W_s h_s,t), p_t = softmax(W_t h_t,t) (each head's logits through
+ * the same optional logit transform), and, if asked, the student's gradients
+ * of L = sum_t c_t kl_t:
+ *   grad_student_hidden [T x Ds] bf16 = G W_s,
+ *   grad_student_weight [V x Ds] fp32 = G^T H_s (added if accumulate_grad_weight),
+ *   G_tv = c_t (p_s,tv - p_t,tv) dz'_tv/dz_tv.
+ * The teacher gets no gradient.  Inputs: student_hidden [T x Ds],
+ * student_weight [V x Ds], teacher_hidden [T x Dt], teacher_weight [V x Dt],
+ * all bf16 row-major (Ds, Dt multiples of 8).  labels is an optional int64 [T]
+ * mask: tokens whose label equals ignore_index are left out (kl = 0, no
+ * gradient, not counted in the mean); other label values are not used; NULL
+ * keeps every token.  Outputs (each optional): kl_out [T] fp32, *mean_out =
+ * mean of kl over kept tokens (0 if none).  Gradients are computed when
+ * grad_out (dL/d kl_t, [T]) or grad_mean (dL/d mean, device scalar) is given
+ * (at most one): c_t = grad_out[t], or *grad_mean / N_kept; grad_student_hidden
+ * and grad_student_weight must then be non-NULL.  The forward values and the
+ * gradients come from one call: the logits of both heads are recomputed per
+ * block (the two log-sum-exps first), nothing of size T x V is stored, and
+ * the workspace is bounded like that of the cross-entropy path.  T == 0 is
+ * valid.  Same conventions (device pointers, stream, errors, determinism) as
+ * above.
+ */
+size_t flce_distill_workspace_bytes(int64_t T, int64_t Ds, int64_t Dt, int64_t V,
+                                    int64_t chunk_rows);
+
+flce_status flce_distill(const void *student_hidden, const void *student_weight, int64_t Ds,
+                         const void *teacher_hidden, const void *teacher_weight, int64_t Dt,
+                         const int64_t *labels, int64_t ignore_index, int64_t T, int64_t V,
+                         int64_t chunk_rows, const flce_logit_transform *transform,
+                         float *kl_out, float *mean_out, const float *grad_out,
+                         const float *grad_mean, void *grad_student_hidden,
+                         float *grad_student_weight, int accumulate_grad_weight,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * The schedule the library would use for this shape, for inspection and
  * tests (host only, no device call).  Fills info[0..11] with:
  *   0 token tiles of 256 rows     1 vocabulary tiles of 256 rows

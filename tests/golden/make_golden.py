@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.dirname(HERE))
 sys.path.insert(0, ROOT)
 
 from chunked_lm_head_amd import synth  # noqa: E402  (inputs only)
+from oracle import distill_oracle as dst  # noqa: E402
 from oracle import flce_oracle as o  # noqa: E402
 
 FULL = ("single_chunk", "qwen3_8b_sft", "grpo_logprob", "long_context")
@@ -47,7 +48,7 @@ def sample_tokens(w: synth.Workload, labels: np.ndarray, rng) -> np.ndarray:
     picks |= {T - 1 - int(i) for i in range(0, min(T, 300), 37)}     # ragged / last tile
     ign = np.nonzero(labels == synth.IGNORE_INDEX)[0]
     picks |= set(int(i) for i in ign[:3])
-    if w.prompt_len:
+    if getattr(w, "prompt_len", 0):
         picks |= {w.seq_len + 5, w.prompt_len - 1, w.prompt_len}    # zero / nonzero grads
     while len(picks) < 24:
         picks.add(int(rng.integers(0, T)))
@@ -93,6 +94,35 @@ def make(name: str) -> str:
     return path
 
 
+DISTILL = ("distill_qwen3",)
+
+
+def make_distill(name: str) -> str:
+    """Distillation workload: sampled per-token KL and log-sum-exps, the mean,
+    the student's dH rows of the sampled tokens and dW rows of sampled vocabulary
+    entries (those need both log-sum-exps of every token)."""
+    w = synth.DISTILL_WORKLOADS[name]
+    t0 = time.time()
+    x = synth.make_distill_inputs(w)
+    rng = np.random.default_rng(w.seed + 77)
+    f = dst.forward(x.s_hidden, x.s_weight, x.t_hidden, x.t_weight, x.labels)
+    tokens = sample_tokens(w, x.labels, rng)
+    picks = {0, 255, 256, w.V - 1, w.V - 2}
+    while len(picks) < 12:
+        picks.add(int(rng.integers(0, w.V)))
+    vocab = np.array(sorted(picks), dtype=np.int64)
+    c = dst.token_scale(x.labels, w.T, grad_mean=1.0)
+    dh = dst.grad_hidden_rows(x.s_hidden, x.s_weight, x.t_hidden, x.t_weight, tokens, c[tokens])
+    dw = dst.grad_weight_rows(x.s_hidden, x.s_weight, x.t_hidden, x.t_weight, vocab, c,
+                              f.lse_s, f.lse_t)
+    path = os.path.join(HERE, f"{name}.npz")
+    np.savez(path, tokens=tokens, kl=f.kl[tokens], lse_s=f.lse_s[tokens], lse_t=f.lse_t[tokens],
+             mean=np.float64(f.mean), n_valid=np.int64(f.n_valid), vocab=vocab,
+             dh=dh.astype(np.float32), dw=dw.astype(np.float32), seed=np.int64(w.seed))
+    print(f"{name}: {time.time() - t0:.0f} s -> {path}", flush=True)
+    return path
+
+
 if __name__ == "__main__":
-    for n in (sys.argv[1:] or FULL + tuple(VARIANTS)):
-        make(n)
+    for n in (sys.argv[1:] or FULL + tuple(VARIANTS) + DISTILL):
+        (make_distill if n in DISTILL else make)(n)

@@ -135,3 +135,42 @@ def test_plan_at_the_workload_shapes(flce):
     assert p["token_tiles"] * p["fwd_splits"] >= 1024
     p = flce.describe_plan(256, 2048, 248320, 256)
     assert p["vocab_chunks"] == 1 and p["row_blocks"] == 1
+
+
+def _dst(flce, **over):
+    a = dict(sh=16, sw=16, Ds=64, th=16, tw=16, Dt=96, labels=None, ign=-100, T=4, V=100, cr=16,
+             xf=None, kl=4, mean=None, gout=None, gmean=None, gh=None, gw=None, acc=0, ws=16,
+             wsb=1 << 30, stream=None)
+    a.update(over)
+    return flce.lib.flce_distill(a["sh"], a["sw"], a["Ds"], a["th"], a["tw"], a["Dt"],
+                                 a["labels"], a["ign"], a["T"], a["V"], a["cr"], a["xf"],
+                                 a["kl"], a["mean"], a["gout"], a["gmean"], a["gh"], a["gw"],
+                                 a["acc"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_distill_rejects_before_launch(flce):
+    assert _dst(flce, T=-1) == 2
+    assert _dst(flce, Ds=60) == 4                    # student hidden not a multiple of 8
+    assert _dst(flce, Dt=12) == 4                    # teacher hidden not a multiple of 8
+    assert _dst(flce, gout=4, gmean=4, gh=16, gw=16) == 1   # both upstream grads
+    assert _dst(flce, gmean=4, gh=16) == 1           # gradient without grad_student_weight
+    assert _dst(flce, gmean=4, gw=16) == 1           # gradient without grad_student_hidden
+    assert _dst(flce, th=0) == 1
+    assert _dst(flce, tw=8) == 1                     # misaligned
+    assert _dst(flce, wsb=16) == 3
+    bad = ctypes.byref(flce.LogitTransform(0.0, 0.0, 0.0, 0.0))
+    assert _dst(flce, xf=bad) == 1
+
+
+def test_distill_workspace_bound(flce):
+    wb = flce.lib.flce_distill_workspace_bytes
+    assert wb(10, 60, 64, 100, 16) == 0
+    assert wb(10, 64, 0, 100, 16) == 0
+    assert wb(0, 64, 64, 100, 16) > 0
+    # p_t (fp32) + G (bf16) blocks within one chunk of fp32 logits, plus terms linear in T, D
+    for T, Ds, Dt, V, cr in [(16384, 4096, 5120, 151936, 256), (131072, 4096, 4096, 151936, 256),
+                             (4096, 2048, 4096, 248320, 64)]:
+        n = wb(T, Ds, Dt, V, cr)
+        linear = 64 * T * 4 + 256 * 4 * 8192 * 4 + 8192 * Ds * 4 * 2 + (32 << 20)
+        assert n <= cr * V * 4 + linear, (T, V, n)
+        assert n < T * V * 4 / 10
