@@ -585,6 +585,46 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
   return FLCE_OK;
 }
 
+int64_t flce_chunk_rows_for(int64_t context_length, int64_t multiplier) {
+  if (context_length < 1) return 0;
+  if (multiplier <= 0) multiplier = std::max<int64_t>(4, context_length / 4096);
+  return cdiv(context_length, multiplier);
+}
+
+flce_status flce_tune(int64_t batch, int64_t context_length, int64_t D, int64_t V,
+                      size_t budget_bytes, int64_t *mini_batches, int64_t *chunk_rows,
+                      size_t *bytes_needed) {
+  g_last_error[0] = 0;
+  if (!mini_batches || !chunk_rows) return fail(FLCE_ERR_ARG, "output pointer is NULL");
+  if (batch < 1 || context_length < 1)
+    return fail(FLCE_ERR_SHAPE, "batch = %lld and context_length = %lld must be >= 1",
+                (long long)batch, (long long)context_length);
+  if (batch > kMaxTV / context_length)
+    return fail(FLCE_ERR_SHAPE, "batch * context_length is too large");
+  const int64_t k0 = std::max<int64_t>(4, context_length / 4096);
+  for (int64_t m = 1; m <= batch; ++m) {
+    if (m > 1 && cdiv(batch, m) == cdiv(batch, m - 1)) continue;  // same group size
+    const int64_t Tmb = cdiv(batch, m) * context_length;
+    // chunk_rows = ceil(context / k) takes each value once: walk the distinct ones
+    for (int64_t k = std::min(k0, context_length); k <= context_length;) {
+      const int64_t cr = cdiv(context_length, k);
+      Plan p;
+      FLCE_TRY(make_plan(Tmb, D, V, cr, p));
+      const size_t need = p.total + (size_t)Tmb * (size_t)D * 4 + (size_t)Tmb * 16;
+      if (need <= budget_bytes) {
+        *mini_batches = m;
+        *chunk_rows = cr;
+        if (bytes_needed) *bytes_needed = need;
+        return FLCE_OK;
+      }
+      if (cr == 1) break;
+      k = cdiv(context_length, cr - 1);  // smallest multiplier giving fewer rows per chunk
+    }
+  }
+  return fail(FLCE_ERR_WORKSPACE, "no mini-batching and chunk size fit in %zu bytes",
+              budget_bytes);
+}
+
 size_t flce_distill_workspace_bytes(int64_t T, int64_t Ds, int64_t Dt, int64_t V,
                                     int64_t chunk_rows) {
   DistillPlan p;

@@ -30,7 +30,7 @@ STATUS = {0: "FLCE_OK", 1: "FLCE_ERR_ARG", 2: "FLCE_ERR_SHAPE", 3: "FLCE_ERR_WOR
           4: "FLCE_ERR_UNSUPPORTED", 5: "FLCE_ERR_HIP"}
 EXPORTS = ("flce_workspace_bytes", "flce_forward", "flce_backward", "flce_describe_plan",
            "flce_status_string", "flce_last_error", "flce_distill_workspace_bytes",
-           "flce_distill")
+           "flce_distill", "flce_chunk_rows_for", "flce_tune")
 
 
 class LogitTransform(ctypes.Structure):
@@ -58,6 +58,11 @@ def _load() -> ctypes.CDLL:
     lib.flce_distill.argtypes = [vp, vp, i64, vp, vp, i64, vp, i64, i64, i64, i64, xp,
                                  f32p, f32p, f32p, f32p, vp, f32p, ctypes.c_int, vp, sz, vp]
     lib.flce_distill.restype = ctypes.c_int
+    lib.flce_chunk_rows_for.argtypes = [i64, i64]
+    lib.flce_chunk_rows_for.restype = i64
+    lib.flce_tune.argtypes = [i64, i64, i64, i64, sz, ctypes.POINTER(ctypes.c_int64),
+                              ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_size_t)]
+    lib.flce_tune.restype = ctypes.c_int
     lib.flce_describe_plan.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
     lib.flce_describe_plan.restype = ctypes.c_int
     lib.flce_status_string.argtypes = [ctypes.c_int]
@@ -120,6 +125,31 @@ def describe_plan(T: int, D: int, V: int, chunk_rows: int = 256) -> dict:
     info = (ctypes.c_int64 * 12)()
     _check(lib.flce_describe_plan(T, D, V, chunk_rows, info))
     return dict(zip(PLAN_KEYS, list(info)))
+
+
+def chunk_rows_for(context_length: int, multiplier: int = 0) -> int:
+    """Rows per chunk when each sequence is cut into ``multiplier`` chunks
+    (0: the default max(4, context_length // 4096))."""
+    n = lib.flce_chunk_rows_for(context_length, multiplier)
+    if n == 0:
+        raise ValueError(f"context_length = {context_length} must be >= 1")
+    return n
+
+
+def tune(batch: int, context_length: int, D: int, V: int, budget_bytes: int) -> dict:
+    """Fewest hidden-state mini-batches, then the largest chunk (smallest multiplier
+    not below the default), whose per-mini-batch device memory fits the budget."""
+    m, cr, need = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    _check(lib.flce_tune(batch, context_length, D, V, budget_bytes, ctypes.byref(m),
+                         ctypes.byref(cr), ctypes.byref(need)))
+    return dict(mini_batches=m.value, chunk_rows=cr.value, bytes_needed=need.value)
+
+
+def auto_tune(batch: int, context_length: int, D: int, V: int, device=None,
+              fraction: float = 0.9) -> dict:
+    """``tune`` against a fraction of the free memory the device reports now."""
+    free, _ = torch.cuda.mem_get_info(device)
+    return tune(batch, context_length, D, V, int(free * fraction))
 
 
 def _validate(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor) -> None:
@@ -200,27 +230,48 @@ def backward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor,
     return grad_hidden, grad_weight
 
 
+def _offload(t: torch.Tensor) -> torch.Tensor:
+    """Copy to pinned host memory, enqueued on the current stream."""
+    h = torch.empty(t.shape, dtype=t.dtype, device="cpu", pin_memory=True)
+    h.copy_(t, non_blocking=True)
+    return h
+
+
 class _ChunkedLinearCE(torch.autograd.Function):
-    """Mean NLL (``reduction="mean"``) or per-token NLL / log-prob (``"none"``)."""
+    """Mean NLL (``reduction="mean"``) or per-token NLL / log-prob (``"none"``).
+
+    As the Unsloth page's offloaded log-softmax (section "Auslagern von
+    Aktivierungen fuer Log-Softmax"): the forward keeps no logits; the backward
+    recomputes them.  With ``offload`` the saved hidden states wait in pinned
+    host memory between the two (the caller's GPU copy may then be freed)."""
 
     @staticmethod
     def forward(ctx, hidden, weight, labels, ignore_index, chunk_rows, mode, reduction,
-                transform):
+                transform, offload):
         out, lse, mean = forward(hidden, weight, labels, ignore_index=ignore_index,
                                  chunk_rows=chunk_rows, mode=mode, transform=transform)
-        ctx.save_for_backward(hidden, weight, labels, lse)
-        ctx.cfg = (ignore_index, chunk_rows, mode, reduction, transform)
+        if offload:
+            ctx.hidden_host = _offload(hidden)
+            ctx.save_for_backward(weight, labels, lse)
+        else:
+            ctx.save_for_backward(hidden, weight, labels, lse)
+        ctx.cfg = (ignore_index, chunk_rows, mode, reduction, transform, offload)
         return mean if reduction == "mean" else out
 
     @staticmethod
     def backward(ctx, grad):
-        hidden, weight, labels, lse = ctx.saved_tensors
-        ignore_index, chunk_rows, mode, reduction, transform = ctx.cfg
+        ignore_index, chunk_rows, mode, reduction, transform, offload = ctx.cfg
+        if offload:
+            weight, labels, lse = ctx.saved_tensors
+            hidden = ctx.hidden_host.to(weight.device, non_blocking=True)
+            del ctx.hidden_host
+        else:
+            hidden, weight, labels, lse = ctx.saved_tensors
         g = grad.float().contiguous()
         kw = dict(grad_mean=g.reshape(())) if reduction == "mean" else dict(grad_out=g)
         dh, dw = backward(hidden, weight, labels, lse, ignore_index=ignore_index,
                           chunk_rows=chunk_rows, mode=mode, transform=transform, **kw)
-        return dh, dw.to(weight.dtype), None, None, None, None, None, None
+        return dh, dw.to(weight.dtype), None, None, None, None, None, None, None
 
 
 def _transform_kwargs(logit_scale_multiply, logit_scale_divide, logit_softcapping, temperature):
@@ -231,7 +282,7 @@ def _transform_kwargs(logit_scale_multiply, logit_scale_divide, logit_softcappin
 def chunked_linear_cross_entropy(hidden, weight, labels, *, ignore_index=-100, chunk_rows=256,
                                  reduction="mean", logit_scale_multiply=0.0,
                                  logit_scale_divide=0.0, logit_softcapping=0.0,
-                                 temperature=1.0):
+                                 temperature=1.0, offload=False):
     """Autograd-aware chunked NLL of ``hidden @ weight.T`` against ``labels``.
 
     The logit transform arguments follow the chunked call of the Unsloth GRPO
@@ -239,17 +290,54 @@ def chunked_linear_cross_entropy(hidden, weight, labels, *, ignore_index=-100, c
     xf = _transform_kwargs(logit_scale_multiply, logit_scale_divide, logit_softcapping,
                            temperature)
     return _ChunkedLinearCE.apply(hidden, weight, labels, ignore_index, chunk_rows, "nll",
-                                  reduction, xf)
+                                  reduction, xf, offload)
 
 
 def selective_log_softmax(hidden, weight, labels, *, ignore_index=-100, chunk_rows=256,
                           logit_scale_multiply=0.0, logit_scale_divide=0.0,
-                          logit_softcapping=0.0, temperature=1.0):
+                          logit_softcapping=0.0, temperature=1.0, offload=False):
     """Autograd-aware per-token log p(label) without materialising the logits."""
     xf = _transform_kwargs(logit_scale_multiply, logit_scale_divide, logit_softcapping,
                            temperature)
     return _ChunkedLinearCE.apply(hidden, weight, labels, ignore_index, chunk_rows, "logprob",
-                                  "none", xf)
+                                  "none", xf, offload)
+
+
+def mini_batched_log_softmax(hidden_fn, weight, labels, mini_batches: int, *,
+                             grad_out: Optional[torch.Tensor] = None, ignore_index=-100,
+                             chunk_rows=256, transform: Optional[dict] = None):
+    """Selective log-softmax over a batch whose hidden states are produced one
+    mini-batch of sequences at a time (the page's hidden-state mini-batching).
+
+    ``hidden_fn(i, m)`` returns the [T_i, D] hidden states of mini-batch i of
+    m (contiguous rows of the flattened batch, in order); ``labels`` covers the
+    whole batch.  Returns (log p [T], and, if ``grad_out`` (dL/d log p) is
+    given, dH [T, D] bf16 and dW [V, D] fp32 accumulated over the mini-batches).
+    Only one mini-batch's hidden states and workspace are alive at a time."""
+    T = labels.shape[0]
+    dev = labels.device
+    logp = torch.empty(T, dtype=torch.float32, device=dev)
+    dh = dw = None
+    r0 = 0
+    for i in range(mini_batches):
+        h = hidden_fn(i, mini_batches)
+        r1 = r0 + h.shape[0]
+        y = labels[r0:r1]
+        out, lse, _ = forward(h, weight, y, ignore_index=ignore_index, chunk_rows=chunk_rows,
+                              mode="logprob", transform=transform, out=logp[r0:r1])
+        if grad_out is not None:
+            if dh is None:
+                dh = torch.empty((T, h.shape[1]), dtype=torch.bfloat16, device=dev)
+                dw = torch.empty((weight.shape[0], weight.shape[1]), dtype=torch.float32,
+                                 device=dev)
+            backward(h, weight, y, lse, grad_out=grad_out[r0:r1], ignore_index=ignore_index,
+                     chunk_rows=chunk_rows, mode="logprob", transform=transform,
+                     grad_hidden=dh[r0:r1], grad_weight=dw, accumulate=i > 0)
+        del h
+        r0 = r1
+    if r0 != T:
+        raise ValueError(f"mini-batches cover {r0} rows, labels {T}")
+    return logp, dh, dw
 
 
 # ---------------------------------------------------------------------------

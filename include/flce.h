@@ -188,6 +188,38 @@ flce_status flce_distill(const void *student_hidden, const void *student_weight,
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Host policy (no device call).  The Unsloth GRPO page (section "Chunking der
+ * abgeflachten Sequenzlaenge" and the configuration section after it) cuts
+ * each sequence of the flattened batch into `multiplier` chunks, with the
+ * default multiplier max(4, context_length // 4096), i.e. batch * multiplier
+ * chunks of context_length / multiplier rows each.
+ *
+ * flce_chunk_rows_for: rows per chunk, ceil(context_length / multiplier), for
+ * that multiplier (<= 0 selects the default).  Returns 0 if context_length < 1.
+ */
+int64_t flce_chunk_rows_for(int64_t context_length, int64_t multiplier);
+
+/*
+ * flce_tune: the page lets both the hidden-state mini-batching (its
+ * unsloth_grpo_mini_batch: the batch is processed in that many groups of
+ * sequences) and the chunk multiplier be chosen automatically from the free
+ * device memory, without giving the rule.  This one: the fewest mini-batches,
+ * then the smallest multiplier not below the default, such that one
+ * mini-batch's device memory
+ *     flce_workspace_bytes(T_mb, D, V, chunk_rows)
+ *   + T_mb * D * 2 (its hidden states) + T_mb * D * 2 (their gradient)
+ *   + T_mb * 16 (labels, output, lse)
+ * fits in budget_bytes, with T_mb = ceil(batch / mini_batches) * context_length.
+ * Writes *mini_batches, *chunk_rows and, if bytes_needed != NULL, the memory
+ * above.  FLCE_ERR_WORKSPACE if nothing fits; FLCE_ERR_ARG / FLCE_ERR_SHAPE
+ * for invalid arguments.  The gradient of the lm_head (V * D * 4 bytes, fp32)
+ * is the caller's and is not counted.
+ */
+flce_status flce_tune(int64_t batch, int64_t context_length, int64_t D, int64_t V,
+                      size_t budget_bytes, int64_t *mini_batches, int64_t *chunk_rows,
+                      size_t *bytes_needed);
+
+/*
  * The schedule the library would use for this shape, for inspection and
  * tests (host only, no device call).  Fills info[0..11] with:
  *   0 token tiles of 256 rows     1 vocabulary tiles of 256 rows
