@@ -57,7 +57,7 @@ struct Plan {
   int64_t R, n_rb, Vc, n_vc, dh_splits, Tb;   // backward; Tb = n_rb * R
   int64_t n_cblk;
   size_t off_pm, off_ps, off_zl, off_bs, off_bc, fwd_bytes;
-  size_t off_c, off_l2, off_G, off_dh, bwd_bytes;
+  size_t off_c, off_l2, off_G, off_dh, off_ht, bwd_bytes;
   size_t gtile_bytes, chunk_bound;
   size_t total;
 };
@@ -148,6 +148,7 @@ flce_status make_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows, Plan 
   p.off_l2 = off; off = align256(off + (size_t)p.Tb * 4);
   p.off_G = off;  off = align256(off + (size_t)p.R * p.Vc * 2);
   p.off_dh = off; off = align256(off + (size_t)p.dh_splits * p.R * p.D * 4);
+  p.off_ht = off; off = align256(off + (size_t)p.R * p.D * 2);
   p.bwd_bytes = off;
   p.gtile_bytes = (size_t)p.R * p.Vc * 2;
   p.chunk_bound = (size_t)p.chunk_rows * p.V * 4;
@@ -167,7 +168,7 @@ struct DistillPlan {
   int64_t R, n_rb, Tb, Vc, n_vc, vsplits, dh_splits;
   size_t off_pm, off_ps, off_zl, off_bs, off_bc;
   size_t off_lse_s, off_lse_t, off_l2s, off_l2t, off_c, off_A, off_B;
-  size_t off_P, off_G, off_pa, off_pb, off_dh;
+  size_t off_P, off_G, off_pa, off_pb, off_dh, off_ht;
   size_t total;
 };
 
@@ -239,6 +240,7 @@ flce_status make_distill_plan(int64_t T, int64_t Ds, int64_t Dt, int64_t V, int6
   p.off_pa = off;    off = align256(off + (size_t)p.n_vc * p.vsplits * p.R * 4);
   p.off_pb = off;    off = align256(off + (size_t)p.n_vc * p.vsplits * p.R * 4);
   p.off_dh = off;    off = align256(off + (size_t)p.dh_splits * p.R * p.Ds * 4);
+  p.off_ht = off;    off = align256(off + (size_t)p.R * p.Ds * 2);
   p.total = off;
   return FLCE_OK;
 }
@@ -312,8 +314,22 @@ flce_status make_xform(const flce_logit_transform *t, Xform &x, bool &cap) {
 
 // dH partial sums and the dW update of one (row block, vocabulary chunk) from
 // its bf16 gradient block G [R, Gp] (token rows, vocabulary columns).
-flce_status launch_dh_dw(const uint16_t *G, int Gp, const void *weight, const void *hidden,
-                         int64_t D, int64_t V, int64_t R, int64_t rb0, int64_t rcount,
+// H^T of a row block for the dW kernel's K-contiguous operand.
+flce_status launch_ht(const void *hidden, uint16_t *ht, int64_t D, int64_t R, int64_t rb0,
+                      int64_t rcount, hipStream_t s) {
+  BwdHtParams t;
+  t.hidden = (const uint16_t *)hidden;
+  t.ht = ht;
+  t.D = (int)D;
+  t.R = (int)R;
+  t.rb0 = (int)rb0;
+  t.rcount = (int)rcount;
+  bwd_ht_kernel<<<dim3((unsigned)cdiv(rcount, 64), (unsigned)cdiv(D, 64)), 256, 0, s>>>(t);
+  return launched("bwd_ht");
+}
+
+flce_status launch_dh_dw(const uint16_t *G, int Gp, const void *weight, const uint16_t *ht,
+                         int64_t D, int64_t V, int64_t R, int64_t rcount,
                          int64_t vc0, int64_t vcount, int64_t dh_splits, float *dhacc,
                          float *grad_weight, bool acc_dh, bool acc_dw, hipStream_t s) {
   const int tiles_h = (int)cdiv(D, kTile);
@@ -337,11 +353,11 @@ flce_status launch_dh_dw(const uint16_t *G, int Gp, const void *weight, const vo
 
   BwdDwParams w;
   w.G = G;
-  w.hidden = (const uint16_t *)hidden;
+  w.ht = ht;
   w.Gp = Gp;
   w.D = (int)D;
   w.V = (int)V;
-  w.rb0 = (int)rb0;
+  w.R = (int)R;
   w.rcount = (int)rcount;
   w.vc0 = (int)vc0;
   w.tiles_m = Gp / kTile;
@@ -525,6 +541,7 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
   float *l2buf = (float *)(ws + p.off_l2);
   uint16_t *G = (uint16_t *)(ws + p.off_G);
   float *dhacc = (float *)(ws + p.off_dh);
+  uint16_t *ht = (uint16_t *)(ws + p.off_ht);
 
   BwdPrepParams pr;
   pr.labels = labels;
@@ -545,6 +562,7 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
     const int64_t rb0 = rb * p.R;
     const int64_t rcount = std::min<int64_t>(p.R, T - rb0);
     if (rcount <= 0) break;
+    FLCE_TRY(launch_ht(hidden, ht, D, p.R, rb0, rcount, s));
     for (int64_t vc = 0; vc < p.n_vc; ++vc) {
       const int64_t vc0 = vc * p.Vc;
       const int64_t vcount = std::min<int64_t>(p.Vc, V - vc0);
@@ -576,7 +594,7 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
         bwd_grad_kernel<false><<<grid, kThreads, 0, s>>>(g);
       FLCE_TRY(launched("bwd_grad"));
 
-      FLCE_TRY(launch_dh_dw(G, (int)p.Vc, weight, hidden, D, V, p.R, rb0, rcount, vc0, vcount,
+      FLCE_TRY(launch_dh_dw(G, (int)p.Vc, weight, ht, D, V, p.R, rcount, vc0, vcount,
                             p.dh_splits, dhacc, grad_weight, vc > 0,
                             accumulate_grad_weight || rb > 0, s));
     }
@@ -685,6 +703,7 @@ flce_status flce_distill(const void *student_hidden, const void *student_weight,
   uint16_t *G = (uint16_t *)(ws + p.off_G);
   float *part_a = (float *)(ws + p.off_pa), *part_b = (float *)(ws + p.off_pb);
   float *dhacc = (float *)(ws + p.off_dh);
+  uint16_t *ht = (uint16_t *)(ws + p.off_ht);
 
   // Log-sum-exp of each head: the fused forward kernel without labels.
   for (int head = 0; head < 2; ++head) {
@@ -738,6 +757,7 @@ flce_status flce_distill(const void *student_hidden, const void *student_weight,
     const int64_t rcount = std::min<int64_t>(p.R, T - rb0);
     if (rcount <= 0) break;
     const int64_t tiles_n = cdiv(rcount, kTile);
+    if (grads) FLCE_TRY(launch_ht(student_hidden, ht, Ds, p.R, rb0, rcount, s));
     for (int64_t vc = 0; vc < p.n_vc; ++vc) {
       const int64_t vc0 = vc * p.Vc;
       const int64_t vcount = std::min<int64_t>(p.Vc, V - vc0);
@@ -780,9 +800,9 @@ flce_status flce_distill(const void *student_hidden, const void *student_weight,
         dst_tile_kernel<false, false><<<grid, kThreads, 0, s>>>(d);
       FLCE_TRY(launched("dst_tile student"));
       if (grads)
-        FLCE_TRY(launch_dh_dw(G, (int)p.Vc, student_weight, student_hidden, Ds, V, p.R, rb0,
-                              rcount, vc0, vcount, p.dh_splits, dhacc, grad_student_weight,
-                              vc > 0, accumulate_grad_weight || rb > 0, s));
+        FLCE_TRY(launch_dh_dw(G, (int)p.Vc, student_weight, ht, Ds, V, p.R, rcount, vc0,
+                              vcount, p.dh_splits, dhacc, grad_student_weight, vc > 0,
+                              accumulate_grad_weight || rb > 0, s));
     }
     const int nparts = (int)(p.n_vc * p.vsplits);
     dst_reduce_kernel<<<(unsigned)cdiv(rcount, 64), 256, 0, s>>>(part_a, nparts, (int)p.R,

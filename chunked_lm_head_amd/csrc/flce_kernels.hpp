@@ -573,11 +573,49 @@ __global__ void __launch_bounds__(kThreads)
   store_acc_block(acc, rs, p.D, wm * 128, h0 + wn * 128, p.D, p.accumulate != 0, lane);
 }
 
+// H^T of a row block: ht[d][t] = hidden[rb0 + t][d] for t < rcount, zeros for
+// rcount <= t < round_up(rcount, 64); rows of R tokens (K-contiguous for dW).
+// 64 x 64 tiles through LDS, 16-byte loads and stores.
+struct BwdHtParams {
+  const uint16_t *hidden;  // [T, D]
+  uint16_t *ht;            // [D, R]
+  int D, R, rb0, rcount;
+};
+
+__global__ void __launch_bounds__(256) bwd_ht_kernel(BwdHtParams p) {
+  __shared__ uint16_t tile[64][72];  // [d][t]; 8 columns of padding
+  const int t0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
+  const int r8 = threadIdx.x >> 3, c8 = (threadIdx.x & 7) * 8;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int tr = r8 + 32 * j, t = t0 + tr, d = d0 + c8;  // d % 8 == 0 and D % 8 == 0
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (t < p.rcount && d < p.D) v = *(const u32x4 *)(p.hidden + (size_t)(p.rb0 + t) * p.D + d);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[c8 + 2 * e][tr] = (uint16_t)(v[e] & 0xffffu);
+      tile[c8 + 2 * e + 1][tr] = (uint16_t)(v[e] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int dr = r8 + 32 * j, d = d0 + dr, t = t0 + c8;  // t % 8 == 0 and R % 256 == 0
+    if (d < p.D && t < p.R) {
+      u32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = (uint32_t)tile[dr][c8 + 2 * e] | ((uint32_t)tile[dr][c8 + 2 * e + 1] << 16);
+      *(u32x4 *)(p.ht + (size_t)d * p.R + t) = v;
+    }
+  }
+}
+
 struct BwdDwParams {
   const uint16_t *G;
-  const uint16_t *hidden;
-  int Gp, D, V;
-  int rb0, rcount;       // tokens [rb0, rb0 + rcount) of this row block exist
+  const uint16_t *ht;    // [D, R] H^T of the row block (bwd_ht_kernel)
+  int Gp, D, V, R;
+  int rcount;            // tokens [0, rcount) of this row block exist
   int vc0;
   int tiles_m, tiles_n;
   float *dW;             // [V, D] fp32
@@ -599,8 +637,8 @@ __global__ void __launch_bounds__(kThreads)
 
   OperandMN A;     // G^T: G[k = token][m = vocabulary]
   A.init(p.G + tm * kTile, p.Gp, kTile, p.rcount, wave, lane);
-  OperandMN B;     // H[rb0 + k][h0 + n]
-  B.init(p.hidden + (size_t)p.rb0 * p.D + h0, p.D, min(kTile, p.D - h0), p.rcount, wave, lane);
+  OperandK B;      // H^T[h0 + n][k = token], K-contiguous; zeros past rcount
+  B.init(p.ht + (size_t)h0 * p.R, p.R, min(kTile, p.D - h0), (p.rcount + 7) & ~7, wave, lane);
   Acc acc;
   acc.zero();
   tile_mainloop(A, B, (p.rcount + kKS - 1) / kKS, smem, acc, wave, lane);
