@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--cpu-sample-vocab", type=int, default=65536)
     ap.add_argument("--gemm-ceiling", action="store_true",
                     help="only time the vendor GEMM (torch.mm -> hipBLASLt) at this path's shapes")
+    ap.add_argument("--lds-rate", action="store_true",
+                    help="only run the LDS read-rate probe (4, 8 and 16 waves per CU)")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only run the sustained-MFMA probe (random operands, no memory traffic)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -113,6 +115,9 @@ def main():
 
     if args.mfma_ceiling:
         mfma_ceiling()
+        return
+    if args.lds_rate:
+        print(json.dumps(_run_probe("lds_rate")), flush=True)
         return
     if args.gemm_ceiling:
         gemm_ceiling(synth.WORKLOADS[args.workload])
@@ -336,18 +341,24 @@ def distill_cpu_baseline(x, n_tokens: int, n_vocab: int) -> dict:
                       f"by {n_vocab}/{V}"}
 
 
-def mfma_ceiling() -> None:
-    """Runs chunked_lm_head_amd/mfma_ceiling (built with the library) in a child process and
-    reports its sustained bf16 rates as fractions of the 2.5 PFLOP/s data-sheet peak."""
+def _run_probe(name: str) -> dict:
+    """Runs chunked_lm_head_amd/<name> (a measurement program built with the library) in a
+    child process and returns the JSON object of its last output line."""
     import subprocess
 
-    exe = os.path.join(ROOT, "chunked_lm_head_amd", "mfma_ceiling")
+    exe = os.path.join(ROOT, "chunked_lm_head_amd", name)
     if not os.path.exists(exe):
         raise SystemExit(f"{exe} is not built; run __graft_entry__.build() first")
     proc = subprocess.run([exe], capture_output=True, text=True, timeout=300)
     if proc.returncode != 0:
-        raise SystemExit(f"mfma_ceiling failed ({proc.returncode}): {proc.stderr.strip()}")
-    rec = json.loads(proc.stdout.strip().splitlines()[-1])["mfma_ceiling"]
+        raise SystemExit(f"{name} failed ({proc.returncode}): {proc.stderr.strip()}")
+    return json.loads(proc.stdout.strip().splitlines()[-1])
+
+
+def mfma_ceiling() -> None:
+    """Runs the sustained-MFMA probe and reports its bf16 rates as fractions of the
+    2.5 PFLOP/s data-sheet peak."""
+    rec = _run_probe("mfma_ceiling")["mfma_ceiling"]
     for k in ("v_mfma_f32_32x32x16_bf16", "v_mfma_f32_16x16x32_bf16"):
         rec[k.replace("v_mfma_f32_", "frac_")] = round(rec[k] / PEAK_BF16, 4)
     print(json.dumps({"mfma_ceiling": rec}), flush=True)

@@ -13,6 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libflce.so")
 CEILING_SRC = os.path.join(CSRC, "mfma_ceiling.hip")
 CEILING_BIN = os.path.join(PKG, "mfma_ceiling")  # measurement program, not part of the library
+LDS_SRC = os.path.join(CSRC, "lds_rate.hip")
+LDS_BIN = os.path.join(PKG, "lds_rate")          # measurement program, not part of the library
 SOURCES = [os.path.join(CSRC, "flce_api.hip")]
 DEPENDS = SOURCES + [os.path.join(CSRC, f) for f in ("flce_tile.hpp", "flce_kernels.hpp")] + [
     os.path.join(INCLUDE, "flce.h")]
@@ -51,21 +53,27 @@ def build_library(verbose: bool = False) -> str:
         print(err, file=sys.stderr)
     os.replace(tmp, LIB)
     build_ceiling_probe(verbose)
+    build_probe(LDS_SRC, LDS_BIN, verbose)
     return LIB
 
 
 def build_ceiling_probe(verbose: bool = False) -> str:
     """Compile the sustained-MFMA probe that bench.py --mfma-ceiling runs."""
+    return build_probe(CEILING_SRC, CEILING_BIN, verbose)
+
+
+def build_probe(src: str, out: str, verbose: bool = False) -> str:
+    """Compile one stand-alone measurement program (bench.py runs them on request)."""
     flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
-    tmp = CEILING_BIN + ".tmp"
-    cmd = [hipcc(), *flags, CEILING_SRC, "-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *flags, src, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {CEILING_SRC} ({proc.returncode}):\n{proc.stderr}")
-    os.replace(tmp, CEILING_BIN)
-    return CEILING_BIN
+        raise RuntimeError(f"hipcc failed on {src} ({proc.returncode}):\n{proc.stderr}")
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
