@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--cpu-sample-vocab", type=int, default=65536)
     ap.add_argument("--gemm-ceiling", action="store_true",
                     help="only time the vendor GEMM (torch.mm -> hipBLASLt) at this path's shapes")
+    ap.add_argument("--sample-power", action="store_true",
+                    help="sample socket power and GFX clocks with amd-smi during the timed steps")
     ap.add_argument("--lds-rate", action="store_true",
                     help="only run the LDS read-rate probe (4, 8 and 16 waves per CU)")
     ap.add_argument("--mfma-ceiling", action="store_true",
@@ -172,12 +174,16 @@ def main():
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sampler = PowerSampler() if args.sample_power else None
     torch.cuda.synchronize()
+    if sampler:
+        sampler.start()
     start.record()
     for i in range(args.steps):
         step(evs[i])
     end.record()
     torch.cuda.synchronize()
+    power = sampler.stop() if sampler else None
     total_ms = start.elapsed_time(end)
     ms = total_ms / args.steps
     fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
@@ -232,6 +238,8 @@ def main():
             "note": "event pair brackets flce_forward: the fused kernel plus two O(T) kernels",
         },
     }
+    if power is not None:
+        line["power"] = power
     print(f"[bench] {args.workload}: inputs drawn in {t_gen:.1f} s; step {ms:.3f} ms "
           f"(fwd {fwd_avg:.3f}, bwd {bwd_avg:.3f})", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
@@ -339,6 +347,47 @@ def distill_cpu_baseline(x, n_tokens: int, n_vocab: int) -> dict:
             "sample": f"first {n_tokens} tokens x first {n_vocab} of {V} vocabulary rows of "
                       f"both heads, float64 numpy forward + backward in {dt:.1f} s; rate scaled "
                       f"by {n_vocab}/{V}"}
+
+
+class PowerSampler:
+    """Samples socket power and the GFX clocks with `amd-smi metric -p -c` in a thread
+    (a read-only query, about twice a second) while the timed steps run."""
+
+    def __init__(self):
+        import threading
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        import re
+        import subprocess
+        while not self._stop.is_set():
+            try:
+                out = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True,
+                                     text=True, timeout=5).stdout
+            except Exception:  # pragma: no cover - tool missing or slow
+                return
+            w = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", out)
+            clks = [float(c) for c in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", out)]
+            if w:
+                self.samples.append((float(w.group(1)), clks))
+            self._stop.wait(0.4)
+
+    def start(self):
+        self._thread.start()
+
+    def stop(self) -> dict:
+        self._stop.set()
+        self._thread.join(timeout=10)
+        s = self.samples[1:] or self.samples  # the first sample may precede the load
+        if not s:
+            return {"samples": 0}
+        watts = [w for w, _ in s]
+        clks = [c for _, cs in s for c in cs]
+        return {"samples": len(s), "socket_w_mean": round(sum(watts) / len(watts), 1),
+                "socket_w_max": max(watts), "cap_w": 1400.0,
+                "gfx_clk_mhz_mean": round(sum(clks) / len(clks), 0) if clks else None}
 
 
 def _run_probe(name: str) -> dict:
