@@ -9,8 +9,14 @@
 //  * Backward: rows are taken in blocks of R tokens (R <= 8192) and the
 //    vocabulary in chunks of Vc rows, with R * Vc bf16 gradient values no more
 //    than the fp32 logits of one chunk of chunk_rows rows (chunk_rows * V * 4
-//    bytes), the bound the pages' Equation 3 describes.  Per (row block,
-//    vocabulary chunk): recompute + G, dH partial sums, dW update.
+//    bytes), the bound the pages' Equation 3 describes.  Per row block: H^T
+//    (the dW kernel's K-contiguous operand); per (row block, vocabulary
+//    chunk): recompute + G, dH partial sums, dW update.
+//  * Distillation: both log-sum-exps by the forward kernel, then per block the
+//    teacher's probabilities (fp32) and the student's G (bf16), 6 bytes per
+//    element within the same bound, and the student's dH and dW.
+//  * Host policy: rows per chunk from the chunk multiplier, and the choice of
+//    mini-batches and chunk size for a memory budget (no device call).
 #include <hip/hip_runtime.h>
 
 #include <stdarg.h>
