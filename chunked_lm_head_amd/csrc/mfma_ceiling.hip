@@ -11,9 +11,12 @@
 // this library's history are timed:
 //   v_mfma_f32_32x32x16_bf16 (32 cycles, 16 accumulators per lane per block)
 //   v_mfma_f32_16x16x32_bf16 (16 cycles,  4 accumulators per lane per block)
-// Prints one JSON line: best of 4 launches per shape, in FLOP/s.
+// Prints one JSON line: best of 4 launches per shape, in FLOP/s.  An optional
+// argument sets the launches per shape (for example 200, about 5 s per shape,
+// long enough to sample board power meanwhile).
 #include <hip/hip_runtime.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -107,7 +110,9 @@ int check(hipError_t e, const char *what) {
 
 }  // namespace
 
-int main() {
+int main(int argc, char **argv) {
+  int reps = argc > 1 ? atoi(argv[1]) : 4;
+  if (reps < 1 || reps > 100000) reps = 4;
   int dev = 0, cus = 0;
   if (check(hipGetDevice(&dev), "hipGetDevice") ||
       check(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "attr"))
@@ -121,7 +126,7 @@ int main() {
   const double flops = (double)blocks * 4 * kIters * 32 * 32768.0;
   double best[2] = {0, 0};
   for (int shape = 0; shape < 2; ++shape) {
-    for (int rep = 0; rep < 4; ++rep) {
+    for (int rep = 0; rep < reps; ++rep) {
       if (check(hipEventRecord(e0), "record")) return 1;
       if (shape == 0)
         shape32<<<blocks, 256>>>(d, kIters);
