@@ -169,9 +169,14 @@ def main():
         if ev is not None:
             ev[2].record()
 
+    torch.cuda.synchronize()
+    base_alloc = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # device memory the step needs beyond its resident inputs and outputs: the workspace
+    peak_extra = torch.cuda.max_memory_allocated(dev) - base_alloc + ws.numel()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     sampler = PowerSampler() if args.sample_power else None
@@ -190,6 +195,8 @@ def main():
     bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
     fwd_avg = sum(fwd_ms) / len(fwd_ms)
     bwd_avg = sum(bwd_ms) / len(bwd_ms)
+    step_ms = sorted(f + b for f, b in zip(fwd_ms, bwd_ms))
+    median_ms = step_ms[len(step_ms) // 2]
     tokens_per_s = T / (ms / 1e3)
     step_flops = 8.0 * T * V * D
     fwd_flops = 2.0 * T * V * D
@@ -223,9 +230,11 @@ def main():
                    "ignored_tokens": w.ignore_count,
                    **({"logit_transform": xf_vals} if has_xf else {})},
         "mfma_frac_of_step": round(step_flops / (ms / 1e3) / PEAK_BF16, 4),
+        "ms_per_step_median": round(median_ms, 4),
         "fwd_ms": round(fwd_avg, 4),
         "bwd_ms": round(bwd_avg, 4),
         "workspace_bytes": int(ws.numel()),
+        "peak_extra_bytes": int(peak_extra),
         "roofline": {
             "kernel": "fwd_lse_kernel",
             "bound": "mfma",
