@@ -626,9 +626,10 @@ flce_status flce_tune(int64_t batch, int64_t context_length, int64_t D, int64_t 
   if (batch > kMaxTV / context_length)
     return fail(FLCE_ERR_SHAPE, "batch * context_length is too large");
   const int64_t k0 = std::max<int64_t>(4, context_length / 4096);
-  for (int64_t m = 1; m <= batch; ++m) {
-    if (m > 1 && cdiv(batch, m) == cdiv(batch, m - 1)) continue;  // same group size
-    const int64_t Tmb = cdiv(batch, m) * context_length;
+  // each distinct group size ceil(batch / m) once, smallest m first
+  for (int64_t m = 1; m <= batch;) {
+    const int64_t g = cdiv(batch, m);
+    const int64_t Tmb = g * context_length;
     // chunk_rows = ceil(context / k) takes each value once: walk the distinct ones
     for (int64_t k = std::min(k0, context_length); k <= context_length;) {
       const int64_t cr = cdiv(context_length, k);
@@ -644,6 +645,8 @@ flce_status flce_tune(int64_t batch, int64_t context_length, int64_t D, int64_t 
       if (cr == 1) break;
       k = cdiv(context_length, cr - 1);  // smallest multiplier giving fewer rows per chunk
     }
+    if (g == 1) break;
+    m = cdiv(batch, g - 1);  // smallest m giving smaller groups
   }
   return fail(FLCE_ERR_WORKSPACE, "no mini-batching and chunk size fit in %zu bytes",
               budget_bytes);
