@@ -168,6 +168,22 @@ def _validate(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor) 
             raise ValueError("tensors on different devices")
 
 
+def _check_buffer(name: str, t: torch.Tensor, dtype, shape, device) -> None:
+    """A caller-provided output or workspace: the library writes through its pointer, so its
+    dtype, device, layout and size must be exactly what the call needs."""
+    if t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor on {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_workspace(t: torch.Tensor, need: int, device) -> None:
+    if t.dtype != torch.uint8 or t.device != device or not t.is_contiguous() or t.dim() != 1:
+        raise ValueError(f"workspace must be a contiguous 1-D uint8 tensor on {device}")
+    if t.numel() < need:
+        raise ValueError(f"workspace has {t.numel()} bytes, {need} needed")
+
+
 def alloc_workspace(T: int, D: int, V: int, chunk_rows: int, device) -> torch.Tensor:
     return torch.empty(workspace_bytes(T, D, V, chunk_rows), dtype=torch.uint8, device=device)
 
@@ -187,8 +203,12 @@ def forward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor, *,
     out = torch.empty(T, dtype=torch.float32, device=dev) if out is None else out
     lse = torch.empty(T, dtype=torch.float32, device=dev) if lse is None else lse
     mean = torch.empty((), dtype=torch.float32, device=dev) if mean is None else mean
+    _check_buffer("out", out, torch.float32, (T,), dev)
+    _check_buffer("lse", lse, torch.float32, (T,), dev)
+    _check_buffer("mean", mean, torch.float32, (), dev)
     if workspace is None:
         workspace = alloc_workspace(T, D, V, chunk_rows, dev)
+    _check_workspace(workspace, workspace_bytes(T, D, V, chunk_rows), dev)
     _check(lib.flce_forward(_ptr(hidden), _ptr(weight), _ptr(labels), T, D, V, ignore_index,
                             chunk_rows, _MODES[mode], make_transform(**(transform or {})),
                             _ptr(out), _ptr(lse), _ptr(mean),
@@ -210,17 +230,22 @@ def backward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor,
     dev = hidden.device
     if (grad_out is None) == (grad_mean is None):
         raise ValueError("give exactly one of grad_out and grad_mean")
-    for t in (lse, grad_out, grad_mean):
-        if t is not None and (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()):
-            raise ValueError("lse / grad_out / grad_mean must be contiguous fp32 on the GPU")
+    _check_buffer("lse", lse, torch.float32, (T,), dev)
+    if grad_out is not None:
+        _check_buffer("grad_out", grad_out, torch.float32, (T,), dev)
+    if grad_mean is not None:
+        _check_buffer("grad_mean", grad_mean, torch.float32, (), dev)
     if grad_hidden is None:
         grad_hidden = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
     if grad_weight is None:
         if accumulate:
             raise ValueError("accumulate needs an existing grad_weight")
         grad_weight = torch.empty((V, D), dtype=torch.float32, device=dev)
+    _check_buffer("grad_hidden", grad_hidden, torch.bfloat16, (T, D), dev)
+    _check_buffer("grad_weight", grad_weight, torch.float32, (V, D), dev)
     if workspace is None:
         workspace = alloc_workspace(T, D, V, chunk_rows, dev)
+    _check_workspace(workspace, workspace_bytes(T, D, V, chunk_rows), dev)
     _check(lib.flce_backward(_ptr(hidden), _ptr(weight), _ptr(labels), _ptr(lse), T, D, V,
                              ignore_index, chunk_rows, _MODES[mode],
                              make_transform(**(transform or {})), _ptr(grad_out),
@@ -378,11 +403,14 @@ def distill(student_hidden, student_weight, teacher_hidden, teacher_weight,
     if grad_out is not None and grad_mean is not None:
         raise ValueError("give at most one of grad_out and grad_mean")
     grads = grad_out is not None or grad_mean is not None
-    for t in (grad_out, grad_mean):
-        if t is not None and (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()):
-            raise ValueError("grad_out / grad_mean must be contiguous fp32 on the GPU")
+    if grad_out is not None:
+        _check_buffer("grad_out", grad_out, torch.float32, (T,), dev)
+    if grad_mean is not None:
+        _check_buffer("grad_mean", grad_mean, torch.float32, (), dev)
     kl = torch.empty(T, dtype=torch.float32, device=dev) if kl is None else kl
     mean = torch.empty((), dtype=torch.float32, device=dev) if mean is None else mean
+    _check_buffer("kl", kl, torch.float32, (T,), dev)
+    _check_buffer("mean", mean, torch.float32, (), dev)
     if grads:
         if grad_hidden is None:
             grad_hidden = torch.empty((T, Ds), dtype=torch.bfloat16, device=dev)
@@ -390,9 +418,12 @@ def distill(student_hidden, student_weight, teacher_hidden, teacher_weight,
             if accumulate:
                 raise ValueError("accumulate needs an existing grad_weight")
             grad_weight = torch.empty((V, Ds), dtype=torch.float32, device=dev)
+        _check_buffer("grad_hidden", grad_hidden, torch.bfloat16, (T, Ds), dev)
+        _check_buffer("grad_weight", grad_weight, torch.float32, (V, Ds), dev)
+    need = distill_workspace_bytes(T, Ds, Dt, V, chunk_rows)
     if workspace is None:
-        workspace = torch.empty(distill_workspace_bytes(T, Ds, Dt, V, chunk_rows),
-                                dtype=torch.uint8, device=dev)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, need, dev)
     _check(lib.flce_distill(_ptr(student_hidden), _ptr(student_weight), Ds, _ptr(teacher_hidden),
                             _ptr(teacher_weight), Dt, _ptr(labels), ignore_index, T, V,
                             chunk_rows, make_transform(**(transform or {})), _ptr(kl),

@@ -182,3 +182,38 @@ def test_empty_batch():
     torch.cuda.synchronize()
     assert float(mean.cpu()) == 0.0
     assert float(gw.abs().max().cpu()) == 0.0
+
+
+def test_binding_rejects_wrong_buffers():
+    """Caller-provided outputs and workspaces of the wrong size, dtype or device are refused
+    before the library is called (the kernels write through their pointers)."""
+    import torch
+
+    from chunked_lm_head_amd import flce
+
+    x = synth.make_inputs(synth.WORKLOADS["tiny"])
+    dev = gu.device()
+    h, W = gu.bf16_tensor(x.hidden, dev), gu.bf16_tensor(x.weight, dev)
+    y = torch.from_numpy(x.labels).to(dev)
+    T, D = h.shape
+    V = W.shape[0]
+    bad = [
+        dict(out=torch.empty(T - 1, dtype=torch.float32, device=dev)),
+        dict(lse=torch.empty(T, dtype=torch.float64, device=dev)),
+        dict(mean=torch.empty(1, dtype=torch.float32, device=dev)),
+        dict(workspace=torch.empty(16, dtype=torch.uint8, device=dev)),
+        dict(out=torch.empty(T, dtype=torch.float32)),
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            flce.forward(h, W, y, chunk_rows=16, **kw)
+    _, lse, _ = flce.forward(h, W, y, chunk_rows=16)
+    one = torch.ones((), device=dev)
+    for kw in (dict(grad_hidden=torch.empty((T, D - 8), dtype=torch.bfloat16, device=dev)),
+               dict(grad_weight=torch.empty((V, D), dtype=torch.bfloat16, device=dev)),
+               dict(grad_mean=torch.ones(2, device=dev))):
+        args = dict(grad_mean=one)
+        args.update(kw)
+        with pytest.raises(ValueError):
+            flce.backward(h, W, y, lse, chunk_rows=16, **args)
+    torch.cuda.synchronize()
