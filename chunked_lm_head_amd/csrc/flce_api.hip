@@ -61,7 +61,7 @@ struct Plan {
   int64_t T, D, V, chunk_rows;
   int64_t n_tt, n_vt, splits, T_pad;          // forward
   int64_t R, n_rb, Vc, n_vc, dh_splits, Tb;   // backward; Tb = n_rb * R
-  int64_t n_cblk;
+  int64_t comb_lanes, n_cblk;  // forward combine: lanes per token, blocks
   size_t off_pm, off_ps, off_zl, off_bs, off_bc, fwd_bytes;
   size_t off_c, off_l2, off_G, off_dh, off_ht, bwd_bytes;
   size_t gtile_bytes, chunk_bound;
@@ -113,6 +113,14 @@ void block_shape(int64_t n_tt, int64_t n_vt, int64_t D, int64_t V, int64_t chunk
   n_vc = cdiv(n_vt, tiles_per_chunk);
 }
 
+// Lanes that merge one token's split partials: the power of two covering the
+// splits, at most a wave.  A 256-thread block then takes 256 / lanes tokens.
+int64_t combine_lanes(int64_t splits) {
+  int64_t l = 1;
+  while (l < 64 && l < splits) l <<= 1;
+  return l;
+}
+
 flce_status make_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows, Plan &p) {
   flce_status st = check_shape(T, D, V, chunk_rows);
   if (st != FLCE_OK) return st;
@@ -126,7 +134,8 @@ flce_status make_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows, Plan 
   p.n_vt = cdiv(V, kTile);
   p.T_pad = p.n_tt * kTile;
   p.splits = std::min<int64_t>(std::max<int64_t>(cdiv(kFwdTargetWG, p.n_tt), 1), p.n_vt);
-  p.n_cblk = cdiv(Tn, 256);
+  p.comb_lanes = combine_lanes(p.splits);
+  p.n_cblk = cdiv(Tn, 256 / p.comb_lanes);
 
   // Backward blocking: bf16 gradient values, 2 bytes each.
   int64_t R, n_vc, tiles_per_chunk;
@@ -495,6 +504,7 @@ flce_status flce_forward(const void *hidden, const void *weight, const int64_t *
   c.splits = (int)p.splits;
   c.T_pad = (int)p.T_pad;
   c.mode = mode;
+  c.lanes = (int)p.comb_lanes;
   c.out = out;
   c.lse = lse;
   c.blk_sum = (double *)(ws + p.off_bs);
@@ -744,9 +754,10 @@ flce_status flce_distill(const void *student_hidden, const void *student_weight,
     l.splits = (int)p.splits;
     l.T_pad = (int)p.T_pad;
     l.n = (int)p.Tb;
+    l.lanes = (int)combine_lanes(p.splits);
     l.lse = head ? lse_s : lse_t;
     l.lse2 = head ? l2s : l2t;
-    dst_lse_kernel<<<(unsigned)cdiv(p.Tb, 256), 256, 0, s>>>(l);
+    dst_lse_kernel<<<(unsigned)cdiv(p.Tb, 256 / l.lanes), 256, 0, s>>>(l);
     FLCE_TRY(launched("dst_lse"));
   }
 

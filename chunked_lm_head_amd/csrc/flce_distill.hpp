@@ -27,32 +27,41 @@ namespace flce {
 
 // lse (natural log) and lse * log2(e) of every token from the forward
 // kernel's per-split partials; rows T <= t < n get lse2 = +inf so their
-// softmax terms vanish.
+// softmax terms vanish.  As in the forward combine, `lanes` lanes merge one
+// token's partials and a fixed shuffle tree combines them; a block takes
+// 256 / lanes tokens.
 struct DstLseParams {
   const float *part_m, *part_s;
   int T, splits, T_pad, n;
+  int lanes;     // power of two <= 64
   float *lse;    // [n]
   float *lse2;   // [n]
 };
 
 __global__ void __launch_bounds__(256) dst_lse_kernel(DstLseParams p) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= p.n) return;
-  if (t >= p.T) {
-    p.lse[t] = 0.f;
-    p.lse2[t] = kInf;
-    return;
+  const int L = p.lanes, g = threadIdx.x / L, j = threadIdx.x % L, per = 256 / L;
+  {
+    const int t = blockIdx.x * per + g;
+    float M = -kInf, S = 0.f;
+    if (t < p.T) {
+      for (int s = j; s < p.splits; s += L)
+        lse_merge(M, S, p.part_m[(size_t)s * p.T_pad + t], p.part_s[(size_t)s * p.T_pad + t]);
+    }
+    for (int w = 1; w < L; w <<= 1) {
+      const float m2 = __shfl_xor(M, w), s2 = __shfl_xor(S, w);
+      lse_merge(M, S, m2, s2);
+    }
+    if (j == 0 && t < p.n) {
+      if (t < p.T) {
+        const float l2 = M + fast_log2(S);
+        p.lse[t] = l2 * kLn2;
+        p.lse2[t] = l2;
+      } else {
+        p.lse[t] = 0.f;
+        p.lse2[t] = kInf;
+      }
+    }
   }
-  float M = -kInf;
-  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.part_m[(size_t)s * p.T_pad + t]);
-  float S = 0.f;
-  for (int s = 0; s < p.splits; ++s) {
-    const float m = p.part_m[(size_t)s * p.T_pad + t];
-    if (m != -kInf) S += p.part_s[(size_t)s * p.T_pad + t] * fast_exp2(m - M);
-  }
-  const float l2 = M + fast_log2(S);
-  p.lse[t] = l2 * kLn2;
-  p.lse2[t] = l2;
 }
 
 // Upstream scale c_t of each token (0 for masked tokens and rows past T).

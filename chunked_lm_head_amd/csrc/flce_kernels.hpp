@@ -241,42 +241,54 @@ struct FwdCombineParams {
   const int64_t *labels;
   int64_t ignore_index;
   int T, V, splits, T_pad, mode;
+  int lanes;  // lanes merging one token's split partials: a power of two <= 64
   float *out, *lse;
   double *blk_sum;
   int *blk_cnt;
 };
 
+// Per token: merge the splits' (max, sum) partials into lse, then out and the
+// block's share of the mean.  `lanes` lanes of one wave merge one token's
+// partials (lane j takes splits j, j + lanes, ...) and a fixed shuffle tree
+// combines them; a block takes 256 / lanes tokens.  So many splits (small T,
+// large V) spread over many blocks instead of serialising on one thread, and
+// the result is the same on every run.
 __global__ void __launch_bounds__(256) fwd_combine_kernel(FwdCombineParams p) {
   __shared__ double ssum[256];
   __shared__ int scnt[256];
-  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int L = p.lanes, g = threadIdx.x / L, j = threadIdx.x % L, per = 256 / L;
   double contrib = 0.0;
   int cnt = 0;
-  if (t < p.T) {
-    float M = -kInf;
-    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.part_m[(size_t)s * p.T_pad + t]);
-    float S = 0.f;
-    for (int s = 0; s < p.splits; ++s) {
-      const float m = p.part_m[(size_t)s * p.T_pad + t];
-      if (m != -kInf) S += p.part_s[(size_t)s * p.T_pad + t] * fast_exp2(m - M);
+  {
+    const int t = blockIdx.x * per + g;
+    float M = -kInf, S = 0.f;
+    if (t < p.T) {
+      for (int s = j; s < p.splits; s += L)
+        lse_merge(M, S, p.part_m[(size_t)s * p.T_pad + t], p.part_s[(size_t)s * p.T_pad + t]);
     }
-    const float lse = (M + fast_log2(S)) * kLn2;
-    const int64_t y = p.labels[t];
-    float o;
-    if (y == p.ignore_index) {
-      o = 0.f;
-    } else if (y < 0 || y >= p.V) {
-      o = __builtin_nanf("");
-      contrib = (double)o;
-      cnt = 1;
-    } else {
-      const float nll = lse - p.zlab[t];
-      o = p.mode == 0 ? nll : -nll;
-      contrib = (double)o;
-      cnt = 1;
+    for (int w = 1; w < L; w <<= 1) {  // lanes of a group stay within one wave
+      const float m2 = __shfl_xor(M, w), s2 = __shfl_xor(S, w);
+      lse_merge(M, S, m2, s2);
     }
-    p.out[t] = o;
-    p.lse[t] = lse;
+    if (j == 0 && t < p.T) {
+      const float lse = (M + fast_log2(S)) * kLn2;
+      const int64_t y = p.labels[t];
+      float o;
+      if (y == p.ignore_index) {
+        o = 0.f;
+      } else if (y < 0 || y >= p.V) {
+        o = __builtin_nanf("");
+        contrib += (double)o;
+        ++cnt;
+      } else {
+        const float nll = lse - p.zlab[t];
+        o = p.mode == 0 ? nll : -nll;
+        contrib += (double)o;
+        ++cnt;
+      }
+      p.out[t] = o;
+      p.lse[t] = lse;
+    }
   }
   ssum[threadIdx.x] = contrib;
   scnt[threadIdx.x] = cnt;
