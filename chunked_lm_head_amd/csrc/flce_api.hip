@@ -13,8 +13,9 @@
 //    (the dW kernel's K-contiguous operand); per (row block, vocabulary
 //    chunk): recompute + G, dH partial sums, dW update.
 //  * Distillation: both log-sum-exps by the forward kernel, then per block the
-//    teacher's probabilities (fp32) and the student's G (bf16), 6 bytes per
-//    element within the same bound, and the student's dH and dW.
+//    teacher's probabilities (fp32) and the student's G (bf16) written over
+//    them, 4 bytes per element within the same bound, and the student's dH
+//    and dW.
 //  * Host policy: rows per chunk from the chunk multiplier, and the choice of
 //    mini-batches and chunk size for a memory budget (no device call).
 #include <hip/hip_runtime.h>
@@ -175,15 +176,15 @@ bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 // Schedule of the distillation call: the forward layout for the two
 // log-sum-exps, and blocks of R rows x Vc vocabulary entries holding the
-// teacher's fp32 probabilities and the student's bf16 gradient (6 bytes per
-// element) within the fp32 logits of one chunk of chunk_rows rows.
+// teacher's fp32 probabilities, then the student's bf16 gradient over them (4
+// bytes per element), within the fp32 logits of one chunk of chunk_rows rows.
 struct DistillPlan {
   int64_t T, Ds, Dt, V, chunk_rows;
   int64_t n_tt, n_vt, splits, T_pad, n_cblk;
   int64_t R, n_rb, Tb, Vc, n_vc, vsplits, dh_splits;
   size_t off_pm, off_ps, off_zl, off_bs, off_bc;
   size_t off_lse_s, off_lse_t, off_l2s, off_l2t, off_c, off_A, off_B;
-  size_t off_P, off_G, off_pa, off_pb, off_dh, off_ht;
+  size_t off_P, off_pa, off_pb, off_dh, off_ht;
   size_t total;
 };
 
@@ -206,10 +207,10 @@ flce_status make_distill_plan(int64_t T, int64_t Ds, int64_t Dt, int64_t V, int6
   p.splits = std::min<int64_t>(std::max<int64_t>(cdiv(kFwdTargetWG, p.n_tt), 1), p.n_vt);
   p.n_cblk = cdiv(Tn, 256);
   int64_t R, tiles_per_chunk, n_vc;
-  block_shape(p.n_tt, p.n_vt, std::max(Ds, Dt), V, chunk_rows, 6, 4, R, tiles_per_chunk, n_vc);
+  block_shape(p.n_tt, p.n_vt, std::max(Ds, Dt), V, chunk_rows, 4, 4, R, tiles_per_chunk, n_vc);
   // Prefer chunks of a multiple of 16 vocabulary tiles (whole-wave dW grids and
   // tile launches): halve the row block while that makes room for them.
-  const int64_t cap = std::max<int64_t>(std::min<int64_t>(chunk_rows, kMaxTV) * V * 4 / 6,
+  const int64_t cap = std::max<int64_t>(std::min<int64_t>(chunk_rows, kMaxTV) * V,
                                         (int64_t)kTile * kTile);
   const int64_t vc_lim = std::max<int64_t>(kTile, (kI32Bytes / (2 * std::max(Ds, Dt))) / kTile * kTile);
   while (tiles_per_chunk < 16 && tiles_per_chunk < p.n_vt && R >= 4 * kTile) {
@@ -250,8 +251,7 @@ flce_status make_distill_plan(int64_t T, int64_t Ds, int64_t Dt, int64_t V, int6
   p.off_c = off;     off = align256(off + (size_t)p.Tb * 4);
   p.off_A = off;     off = align256(off + (size_t)p.Tb * 4);
   p.off_B = off;     off = align256(off + (size_t)p.Tb * 4);
-  p.off_P = off;     off = align256(off + (size_t)p.R * p.Vc * 4);
-  p.off_G = off;     off = align256(off + (size_t)p.R * p.Vc * 2);
+  p.off_P = off;     off = align256(off + (size_t)p.R * p.Vc * 4);  // p_t, then G over it
   p.off_pa = off;    off = align256(off + (size_t)p.n_vc * p.vsplits * p.R * 4);
   p.off_pb = off;    off = align256(off + (size_t)p.n_vc * p.vsplits * p.R * 4);
   p.off_dh = off;    off = align256(off + (size_t)p.dh_splits * p.R * p.Ds * 4);
@@ -327,8 +327,6 @@ flce_status make_xform(const flce_logit_transform *t, Xform &x, bool &cap) {
   return FLCE_OK;
 }
 
-// dH partial sums and the dW update of one (row block, vocabulary chunk) from
-// its bf16 gradient block G [R, Gp] (token rows, vocabulary columns).
 // H^T of a row block for the dW kernel's K-contiguous operand.
 flce_status launch_ht(const void *hidden, uint16_t *ht, int64_t D, int64_t R, int64_t rb0,
                       int64_t rcount, hipStream_t s) {
@@ -343,10 +341,15 @@ flce_status launch_ht(const void *hidden, uint16_t *ht, int64_t D, int64_t R, in
   return launched("bwd_ht");
 }
 
-flce_status launch_dh_dw(const uint16_t *G, int Gp, const void *weight, const uint16_t *ht,
-                         int64_t D, int64_t V, int64_t R, int64_t rcount,
-                         int64_t vc0, int64_t vcount, int64_t dh_splits, float *dhacc,
-                         float *grad_weight, bool acc_dh, bool acc_dw, hipStream_t s) {
+// dH partial sums and the dW update of one (row block, vocabulary chunk) from
+// its bf16 gradient block G: token rows of pitch Gp, gcols vocabulary columns
+// (a multiple of 256), plain or grouped (written over an fp32 block: Gp =
+// 2 gcols, each 128-column group in the first half of its fp32 bytes).
+flce_status launch_dh_dw(const uint16_t *G, int Gp, int64_t gcols, bool grouped,
+                         const void *weight, const uint16_t *ht, int64_t D, int64_t V, int64_t R,
+                         int64_t rcount, int64_t vc0, int64_t vcount, int64_t dh_splits,
+                         float *dhacc, float *grad_weight, bool acc_dh, bool acc_dw,
+                         hipStream_t s) {
   const int tiles_h = (int)cdiv(D, kTile);
   BwdDhParams h;
   h.G = G;
@@ -356,14 +359,18 @@ flce_status launch_dh_dw(const uint16_t *G, int Gp, const void *weight, const ui
   h.V = (int)V;
   h.vc0 = (int)vc0;
   h.vcount = (int)vcount;
-  h.Kc = (int)std::min<int64_t>(Gp, cdiv(vcount, kBK) * kBK);  // G is zero past vcount
+  h.Kc = (int)std::min<int64_t>(gcols, cdiv(vcount, kBK) * kBK);  // G is zero past vcount
   h.R = (int)R;
   h.tiles_m = (int)(R / kTile);
   h.tiles_n = tiles_h;
   h.splits = (int)dh_splits;
   h.acc = dhacc;
   h.accumulate = acc_dh ? 1 : 0;
-  bwd_dh_kernel<<<(unsigned)(h.tiles_m * h.tiles_n * h.splits), kThreads, 0, s>>>(h);
+  const unsigned dh_grid = (unsigned)(h.tiles_m * h.tiles_n * h.splits);
+  if (grouped)
+    dst_dh_kernel<<<dh_grid, kThreads, 0, s>>>(h);
+  else
+    bwd_dh_kernel<<<dh_grid, kThreads, 0, s>>>(h);
   FLCE_TRY(launched("bwd_dh"));
 
   BwdDwParams w;
@@ -375,11 +382,14 @@ flce_status launch_dh_dw(const uint16_t *G, int Gp, const void *weight, const ui
   w.R = (int)R;
   w.rcount = (int)rcount;
   w.vc0 = (int)vc0;
-  w.tiles_m = Gp / kTile;
+  w.tiles_m = (int)(gcols / kTile);
   w.tiles_n = tiles_h;
   w.dW = grad_weight;
   w.accumulate = acc_dw ? 1 : 0;
-  bwd_dw_kernel<<<(unsigned)(w.tiles_m * w.tiles_n), kThreads, 0, s>>>(w);
+  if (grouped)
+    dst_dw_kernel<<<(unsigned)(w.tiles_m * w.tiles_n), kThreads, 0, s>>>(w);
+  else
+    bwd_dw_kernel<<<(unsigned)(w.tiles_m * w.tiles_n), kThreads, 0, s>>>(w);
   return launched("bwd_dw");
 }
 
@@ -610,7 +620,7 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
         bwd_grad_kernel<false><<<grid, kThreads, 0, s>>>(g);
       FLCE_TRY(launched("bwd_grad"));
 
-      FLCE_TRY(launch_dh_dw(G, (int)p.Vc, weight, ht, D, V, p.R, rcount, vc0, vcount,
+      FLCE_TRY(launch_dh_dw(G, (int)p.Vc, p.Vc, false, weight, ht, D, V, p.R, rcount, vc0, vcount,
                             p.dh_splits, dhacc, grad_weight, vc > 0,
                             accumulate_grad_weight || rb > 0, s));
     }
@@ -719,7 +729,7 @@ flce_status flce_distill(const void *student_hidden, const void *student_weight,
   float *cbuf = (float *)(ws + p.off_c);
   float *Abuf = (float *)(ws + p.off_A), *Bbuf = (float *)(ws + p.off_B);
   float *Pbuf = (float *)(ws + p.off_P);
-  uint16_t *G = (uint16_t *)(ws + p.off_G);
+  uint16_t *G = (uint16_t *)Pbuf;  // the student's gradient replaces p_t in place
   float *part_a = (float *)(ws + p.off_pa), *part_b = (float *)(ws + p.off_pb);
   float *dhacc = (float *)(ws + p.off_dh);
   uint16_t *ht = (uint16_t *)(ws + p.off_ht);
@@ -795,8 +805,8 @@ flce_status flce_distill(const void *student_hidden, const void *student_weight,
       d.xf = xf;
       d.P = Pbuf;
       d.Pp = (int)p.Vc;
-      d.G = G;
-      d.Gp = (int)p.Vc;
+      d.G = G;  // over P, grouped
+      d.Gp = (int)(2 * p.Vc);
       const unsigned grid = (unsigned)(tiles_n * p.vsplits);
       // teacher: p_t block and partial sums of A
       d.hidden = (const uint16_t *)teacher_hidden;
@@ -820,9 +830,9 @@ flce_status flce_distill(const void *student_hidden, const void *student_weight,
         dst_tile_kernel<false, false><<<grid, kThreads, 0, s>>>(d);
       FLCE_TRY(launched("dst_tile student"));
       if (grads)
-        FLCE_TRY(launch_dh_dw(G, (int)p.Vc, student_weight, ht, Ds, V, p.R, rcount, vc0,
-                              vcount, p.dh_splits, dhacc, grad_student_weight, vc > 0,
-                              accumulate_grad_weight || rb > 0, s));
+        FLCE_TRY(launch_dh_dw(G, (int)(2 * p.Vc), p.Vc, true, student_weight, ht, Ds, V, p.R,
+                              rcount, vc0, vcount, p.dh_splits, dhacc, grad_student_weight,
+                              vc > 0, accumulate_grad_weight || rb > 0, s));
     }
     const int nparts = (int)(p.n_vc * p.vsplits);
     dst_reduce_kernel<<<(unsigned)cdiv(rcount, 64), 256, 0, s>>>(part_a, nparts, (int)p.R,

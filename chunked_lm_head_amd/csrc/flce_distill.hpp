@@ -16,9 +16,11 @@
 // kernel without labels; then, per block of rows and vocabulary chunk, the
 // teacher kernel recomputes its logits and writes p_t in fp32 (with partial
 // sums of A), and the student kernel recomputes its logits, reads p_t, adds
-// partial sums of B and writes G = c (p_s - p_t) dz_s'/dz_s in bf16 for the
-// dH and dW kernels.  The fp32 p_t block and the bf16 G block together stay
-// within the fp32 logits of one chunk of chunk_rows rows.
+// partial sums of B and writes G = c (p_s - p_t) dz_s'/dz_s in bf16 over p_t,
+// in place (each 128-column group's bf16 values in the first half of its fp32
+// bytes), for the dH and dW kernels, which read that grouped layout.  The
+// block, 4 bytes per element, stays within the fp32 logits of one chunk of
+// chunk_rows rows.
 #pragma once
 
 #include "flce_kernels.hpp"
@@ -108,8 +110,8 @@ struct DstTileParams {
   Xform xf;
   float *P;                         // [R, Pp] teacher probabilities, fp32
   int Pp;
-  uint16_t *G;                      // [R, Gp] student gradient, bf16 (zeros when c = 0)
-  int Gp;
+  uint16_t *G;                      // student gradient, bf16 (zeros when c = 0), written over
+  int Gp;                           // P: the same bytes, Gp = 2 Pp, grouped columns
   float *part;                      // [vsplits, R] this launch's per-token partial sums
 };
 
@@ -118,7 +120,11 @@ struct DstTileParams {
 //   teacher (kTeacher): P = p_t = 2^(z_t' log2 e - lse2_t) -> fp32 block,
 //                       partial sums of p_t z_t' (A);
 //   student:            reads p_t, partial sums of p_t z_s' (B), and
-//                       G = c (p_s - p_t) dz_s'/dz_s -> bf16 block.
+//                       G = c (p_s - p_t) dz_s'/dz_s -> bf16, over p_t.
+// A student wave reads the p_t values of one token row (its 128 columns) and
+// then writes that row's G into the first half of the same bytes: each G store
+// overlaps only p_t values of the same or earlier blocks of the row, which the
+// store's own data already waited for; no other wave touches those bytes.
 // Rows past the vocabulary have z = -inf: p = 0 there and the products are
 // taken as 0.  Every workgroup writes its partial-sum slot (zeros when its
 // vocabulary range is empty), so the reduction reads no stale values.
@@ -180,6 +186,8 @@ __global__ void __launch_bounds__(kThreads)
         if constexpr (!kTeacher) {
 #pragma unroll
           for (int mb = 0; mb < 8; ++mb) pt[mb] = *(const f32x4 *)(prow + acc_row(mb, 0, lane));
+          // G is written over these bytes below: keep every read of the row first
+          __asm__ volatile("" ::: "memory");
         }
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) {
@@ -209,7 +217,7 @@ __global__ void __launch_bounds__(kThreads)
             u32x2 w;
             w[0] = pack_bf16(g[0], g[1]);
             w[1] = pack_bf16(g[2], g[3]);
-            *(u32x2 *)(p.G + (size_t)tl * p.Gp + col + acc_row(mb, 0, lane)) = w;
+            *(u32x2 *)(p.G + (size_t)tl * p.Gp + grouped_col(col + acc_row(mb, 0, lane))) = w;
           }
         }
       }
@@ -233,6 +241,19 @@ __global__ void __launch_bounds__(kThreads)
       p.part[(size_t)sp * p.R + tl] = psum[nb] + xch[(wn * 8 + nb) * 16 + lane];
     }
   }
+}
+
+// dH and dW of the student from its G block in the grouped layout above.
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(1, 1))) dst_dh_kernel(BwdDhParams p) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[kPipeBytes];
+  dh_tile<OperandKG>(p, (lds_t *)smem_raw);
+}
+
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(1, 1))) dst_dw_kernel(BwdDwParams p) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[kPipeBytes];
+  dw_tile<OperandMNG>(p, (lds_t *)smem_raw);
 }
 
 // out[rb0 + t] = sum over the nparts slots of part[slot, t], t < rcount, in a

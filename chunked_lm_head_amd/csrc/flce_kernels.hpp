@@ -552,10 +552,10 @@ struct BwdDhParams {
   int accumulate;
 };
 
-__global__ void __launch_bounds__(kThreads)
-    __attribute__((amdgpu_waves_per_eu(1, 1))) bwd_dh_kernel(BwdDhParams p) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[kPipeBytes];
-  lds_t *smem = (lds_t *)smem_raw;
+// One dH tile (split s of K): A = G rows, plain (OperandK) or grouped in
+// place of an fp32 block (OperandKG, the distillation's layout).
+template <class OA>
+__device__ __forceinline__ void dh_tile(const BwdDhParams &p, lds_t *smem) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -570,8 +570,11 @@ __global__ void __launch_bounds__(kThreads)
   const int kend = min(p.Kc, (int)((int64_t)(s + 1) * ktiles / p.splits) * kBK);
   const int h0 = tn * kTile;
 
-  OperandK A;      // G rows of this tile, K = vocabulary (contiguous)
-  A.init(p.G + (size_t)(tm * kTile) * p.Gp + kbeg, p.Gp, kTile, kend - kbeg, wave, lane);
+  OA A;            // G rows of this tile, K = vocabulary (contiguous)
+  if constexpr (OA::kGrouped)
+    A.init(p.G + (size_t)(tm * kTile) * p.Gp, p.Gp, kTile, kbeg, kend - kbeg, wave, lane);
+  else
+    A.init(p.G + (size_t)(tm * kTile) * p.Gp + kbeg, p.Gp, kTile, kend - kbeg, wave, lane);
   OperandMN B;     // W[vc0 + k][h0 + n]: K = vocabulary rows
   B.init(p.weight + (size_t)(p.vc0 + kbeg) * p.D + h0, p.D, min(kTile, p.D - h0),
          min(kend, p.vcount) - kbeg, wave, lane);
@@ -583,6 +586,12 @@ __global__ void __launch_bounds__(kThreads)
   const float *tile = p.acc + ((size_t)s * p.R + (size_t)tm * kTile) * p.D;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, (uint32_t)kTile * (uint32_t)p.D * 4u);
   store_acc_block(acc, rs, p.D, wm * 128, h0 + wn * 128, p.D, p.accumulate != 0, lane);
+}
+
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(1, 1))) bwd_dh_kernel(BwdDhParams p) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[kPipeBytes];
+  dh_tile<OperandK>(p, (lds_t *)smem_raw);
 }
 
 // H^T of a row block: ht[d][t] = hidden[rb0 + t][d] for t < rcount, zeros for
@@ -634,10 +643,9 @@ struct BwdDwParams {
   int accumulate;
 };
 
-__global__ void __launch_bounds__(kThreads)
-    __attribute__((amdgpu_waves_per_eu(1, 1))) bwd_dw_kernel(BwdDwParams p) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[kPipeBytes];
-  lds_t *smem = (lds_t *)smem_raw;
+// One dW tile: A = G^T, plain (OperandMN) or grouped (OperandMNG).
+template <class OA>
+__device__ __forceinline__ void dw_tile(const BwdDwParams &p, lds_t *smem) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -647,8 +655,9 @@ __global__ void __launch_bounds__(kThreads)
   if (v0 >= p.V) return;  // the whole tile lies past the vocabulary
   const int h0 = tn * kTile;
 
-  OperandMN A;     // G^T: G[k = token][m = vocabulary]
-  A.init(p.G + tm * kTile, p.Gp, kTile, p.rcount, wave, lane);
+  OA A;            // G^T: G[k = token][m = vocabulary]
+  A.init(p.G + (OA::kGrouped ? grouped_col(tm * kTile) : tm * kTile), p.Gp, kTile, p.rcount,
+         wave, lane);
   OperandK B;      // H^T[h0 + n][k = token], K-contiguous; zeros past rcount
   B.init(p.ht + (size_t)h0 * p.R, p.R, min(kTile, p.D - h0), (p.rcount + 7) & ~7, wave, lane);
   Acc acc;
@@ -659,6 +668,12 @@ __global__ void __launch_bounds__(kThreads)
   const uint32_t rows = (uint32_t)min(kTile, p.V - v0);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.dW + (size_t)v0 * p.D, rows * (uint32_t)p.D * 4u);
   store_acc_block(acc, rs, p.D, wm * 128, h0 + wn * 128, p.D, p.accumulate != 0, lane);
+}
+
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(1, 1))) bwd_dw_kernel(BwdDwParams p) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[kPipeBytes];
+  dw_tile<OperandMN>(p, (lds_t *)smem_raw);
 }
 
 struct BwdDhOutParams {

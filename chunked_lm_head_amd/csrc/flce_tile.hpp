@@ -9,20 +9,21 @@
 // chip holds at full load, which is why it is used although it needs the
 // same LDS traffic per FLOP.
 //
-// Pipeline: K advances 32 at a time through a 4-stage LDS ring (4 x 32 KiB);
-// stage k + 3 is in flight while stage k is multiplied.  Every operand moves
-// global -> LDS by the direct-to-LDS form of buffer_load_dwordx4 (no
-// registers, no VALU), from a buffer descriptor that covers exactly the valid
-// bytes; masked lanes use an offset past its end, so ragged edges read zeros
-// and no load can leave its tensor.  One barrier per K step, placed between
-// the MFMAs of B blocks 0..3 and 4..7, so that the fragment reads of the next
-// stage overlap the MFMAs of the current one.
+// Pipeline: K advances 64 at a time (two MFMA steps of 32) through a 2-stage
+// LDS ring (2 x 64 KiB, A and B 32 KiB each); the next stage is in flight
+// while the current one is multiplied.  Every operand moves global -> LDS by
+// the direct-to-LDS form of buffer_load_dwordx4 (no registers, no VALU), from
+// a buffer descriptor that covers exactly the valid bytes; masked lanes use an
+// offset past its end, so ragged edges read zeros and no load can leave its
+// tensor.  One barrier per stage, placed between the MFMAs of B blocks 0..3
+// and 4..7 of its second step, so that the fragment reads of the next stage
+// overlap the MFMAs of the current one.
 //
 // Two operand layouts in global memory, two layouts in LDS:
-//  * K-contiguous ([mn][k], e.g. H and W in the logit GEMM): LDS rows of 32 k
-//    (64 B); chunk c of row r sits at chunk c ^ k_swizzle(r).  Fragments are
+//  * K-contiguous ([mn][k], e.g. H and W in the logit GEMM): LDS rows of 64 k
+//    (128 B); chunk c of row r sits at chunk c ^ k_swizzle(r).  Fragments are
 //    ds_read_b128.
-//  * MN-contiguous ([k][mn], e.g. W in dH = G W, H and G in dW = G^T H): LDS
+//  * MN-contiguous ([k][mn], e.g. W in dH = G W, G in dW = G^T H): LDS
 //    rows of 256 mn (512 B) per k; 16-byte chunk c of row k sits at
 //    c ^ mn_swizzle(k).  Fragments are two ds_read_b64_tr_b16, which transpose
 //    4 x 4 blocks of 16-bit values across lanes: within each group of 16
@@ -153,7 +154,7 @@ __device__ __forceinline__ void grouped_tile(int L, int tiles_m, int tiles_n, in
 }
 
 // ---------------------------------------------------------------------------
-// Operands.  Each wave issues 4 DMA instructions per operand per stage.
+// Operands.  Each wave issues 8 DMA instructions per operand per stage.
 // ---------------------------------------------------------------------------
 
 // Chunk swizzle of the K-major LDS layout (rows of eight 16-byte chunks, one
@@ -177,6 +178,7 @@ struct DmaSlice {
 // full row per 8 lanes, in 8 loads of 8 rows.
 struct OperandK {
   static constexpr int kReads = 1;  // LDS reads per MFMA fragment
+  static constexpr bool kGrouped = false;
   const char *base;  // tile origin (row 0, k 0)
   uint32_t nbytes;   // valid bytes from base
   int kext;          // valid K extent (multiple of 8)
@@ -236,6 +238,7 @@ __device__ __forceinline__ int mn_swizzle(int k) { return 4 * (k & 3) + 2 * ((k 
 // them, two per load.
 struct OperandMN {
   static constexpr int kReads = 2;  // LDS reads per MFMA fragment
+  static constexpr bool kGrouped = false;
   const char *base;   // tile origin (k 0, column 0)
   uint32_t nbytes;    // valid bytes from base
   uint32_t row_bytes; // ld * 2
@@ -296,6 +299,62 @@ struct OperandMN {
     const short v8 __attribute__((ext_vector_type(8))) = {lo[0], lo[1], lo[2], lo[3],
                                                            hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v8);
+  }
+};
+
+// A bf16 block written in place of an fp32 block of the same shape: each
+// 128-column group of a row keeps its values in the first half of the group's
+// 512 bytes, so logical column k sits at bf16 position k + (k & ~127) of the
+// row (every group followed by 128 unused positions).
+__device__ __forceinline__ int grouped_col(int k) { return k + (k & ~127); }
+
+// OperandK over such a grouped block: K (the columns) starts at logical
+// column kbase, a multiple of kBK, so each stage's 64 columns lie inside one
+// group and are contiguous.  `base` is the row origin (logical column 0).
+struct OperandKG : OperandK {
+  static constexpr bool kGrouped = true;
+  int kbase;
+
+  __device__ __forceinline__ void init(const uint16_t *row_base, int ld, int rows, int kbase_,
+                                       int kext_, int wave, int lane) {
+    OperandK::init(row_base, ld, rows, kext_, wave, lane);
+    kbase = kbase_;
+    nbytes = (rows > 0 && kext > 0)
+                 ? (uint32_t)((rows - 1) * ld + grouped_col(kbase + kext - 1) + 1) * 2u
+                 : 0u;
+  }
+  __device__ __forceinline__ DmaSlice prep(int k0) const {
+    const uint32_t adv = (uint32_t)grouped_col(kbase + k0) * 2u;
+    return DmaSlice{rsrc_words(base + adv, remaining(nbytes, adv)), k0, k0 + kBK <= kext};
+  }
+  __device__ __forceinline__ void issue(lds_t *stage, int k0, int wave) const {
+    const DmaSlice d = prep(k0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) issue_one(d, stage, i, wave);
+  }
+};
+
+// OperandMN over a grouped block: a tile of 256 logical columns starting at a
+// multiple of 256 spans two groups; `base` is the tile's first column (its
+// physical position, twice the logical one).  Only the per-lane column offsets
+// differ from OperandMN.
+struct OperandMNG : OperandMN {
+  static constexpr bool kGrouped = true;
+  __device__ __forceinline__ void init(const uint16_t *base_, int ld, int cols, int kext_,
+                                       int wave, int lane) {
+    base = (const char *)base_;
+    cols = cols < 0 ? 0 : cols;
+    kext = kext_ < 0 ? 0 : kext_;
+    row_bytes = (uint32_t)ld * 2u;
+    nbytes = (cols > 0 && kext > 0) ? (uint32_t)((kext - 1) * ld + grouped_col(cols - 1) + 1) * 2u
+                                    : 0u;
+    kr0 = wave * 16 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = kr0 + 2 * i;
+      const int c = (lane & 31) ^ mn_swizzle(k);
+      voff[i] = c * 8 < cols ? (uint32_t)(k * ld + grouped_col(c * 8)) * 2u : kOOB;
+    }
   }
 };
 
