@@ -29,6 +29,8 @@ CASES = [
     ("softcap_temperature", (300, 256, 384, 5000, 64, 0.05, "mean", 0.2, 0.2),
      (0.0, 0.0, 1.5, 0.7), True),
     ("scaled", (520, 200, 136, 3001, 256, 0.0, "none", 0.3, 0.3), (1.3, 0.8, 0.0, 0.6), True),
+    # the largest hidden size accepted, on the student (the block shape follows max(Ds, Dt))
+    ("max_d", (200, 65536, 1024, 600, 64, 0.05, "mean", None, None), None, True),
 ]
 
 

@@ -5,6 +5,7 @@ relative Frobenius error (dH is bf16, G is rounded to bf16 before the backward
 GEMMs, logits and accumulation are fp32).
 """
 import math
+import zlib
 
 import numpy as np
 import pytest
@@ -26,6 +27,7 @@ SHAPES = [
     ("many_blocks", 8500, 64, 700, 256, 0.03, "nll", "mean"),
     ("one_token", 1, 64, 300, 256, 0.0, "nll", "mean"),
     ("wide_d", 130, 1032, 777, 16, 0.1, "logprob", "mean"),
+    ("max_d", 300, 65536, 600, 64, 0.05, "nll", "mean"),   # the largest hidden size accepted
 ]
 
 
@@ -35,7 +37,7 @@ def _workload(spec):
         return synth.WORKLOADS[name]
     kw = dict(seq_len=260, prompt_len=40) if red == "none" else {}
     return synth.custom(name, T=T, H=D, V=V, chunk_rows=cr, ignore_frac=ign, mode=mode,
-                        reduction=red, seed=hash(name) % 1000, **kw)
+                        reduction=red, seed=zlib.crc32(name.encode()) % 1000, **kw)
 
 
 def _oracle(x, labels=None, weight=None, grad_out=None, grad_mean=1.0, mode=None):
