@@ -437,9 +437,11 @@ def distill(student_hidden, student_weight, teacher_hidden, teacher_weight,
 class _ChunkedDistillKL(torch.autograd.Function):
     """Mean (``reduction="mean"``) or per-token (``"none"``) KL(teacher || student).
 
-    The mean's gradients are computed in the forward call (c = 1 / N_kept) and
-    scaled by the upstream scalar in the backward; per-token reduction calls the
-    library again in the backward with the upstream gradient (recompute)."""
+    The mean's gradients are computed in the forward call (c = 1 / N_kept), which
+    saves a second recompute, and scaled by the upstream scalar in the backward
+    (two elementwise products in PyTorch; dH is rounded to bf16 once more);
+    per-token reduction calls the library again in the backward with the
+    upstream gradient (recompute)."""
 
     @staticmethod
     def forward(ctx, s_hidden, s_weight, t_hidden, t_weight, labels, ignore_index, chunk_rows,
