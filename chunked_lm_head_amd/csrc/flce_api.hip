@@ -30,6 +30,7 @@
 
 #include "flce.h"
 #include "flce_distill.hpp"
+#include "flce_policy.hpp"
 
 namespace {
 
@@ -863,6 +864,209 @@ flce_status flce_distill(const void *student_hidden, const void *student_weight,
     FLCE_TRY(launched("fwd_mean"));
   }
   return FLCE_OK;
+}
+
+}  // extern "C"
+
+
+namespace {
+
+// Workspace of a policy-loss call: the cross-entropy workspace (the log-prob
+// forward and backward run in it), then per-token log-probs (when the caller
+// keeps none), lse and upstream gradients, and per-sequence values.
+struct PolicyLayout {
+  size_t flce, off_logp, off_lse, off_c, off_val, off_n, off_g, total;
+};
+
+flce_status policy_layout(int64_t T, int64_t D, int64_t V, int64_t chunk_rows, int64_t n_seq,
+                          PolicyLayout &l) {
+  Plan p;
+  FLCE_TRY(make_plan(T, D, V, chunk_rows, p));
+  if (n_seq < 1 || n_seq > std::max<int64_t>(T, 1) || T % n_seq)
+    return fail(FLCE_ERR_SHAPE, "n_seq = %lld must be >= 1 and divide T = %lld",
+                (long long)n_seq, (long long)T);
+  size_t off = align256(p.total);
+  l.flce = p.total;
+  l.off_logp = off; off = align256(off + (size_t)T * 4);
+  l.off_lse = off;  off = align256(off + (size_t)T * 4);
+  l.off_c = off;    off = align256(off + (size_t)T * 4);
+  l.off_val = off;  off = align256(off + (size_t)n_seq * 8);
+  l.off_n = off;    off = align256(off + (size_t)n_seq * 4);
+  l.off_g = off;    off = align256(off + (size_t)n_seq * 4);
+  l.total = off;
+  return FLCE_OK;
+}
+
+bool finite_nonneg(float x) { return std::isfinite(x) && x >= 0.f; }
+
+struct PolicyInputs {
+  const float *advantages, *old_logp, *ref_logp, *ref_seq, *kl_ref;
+  const uint8_t *desirable;
+};
+
+template <int kKind>
+void launch_policy_kernels(const PolicyParams &pp, bool grads, hipStream_t s) {
+  pol_seq_kernel<kKind><<<(unsigned)pp.n_seq, 256, 0, s>>>(pp);
+  pol_loss_kernel<kKind><<<1, 1024, 0, s>>>(pp);
+  if (grads) pol_grad_kernel<kKind><<<(unsigned)cdiv(pp.T, 256), 256, 0, s>>>(pp);
+}
+
+flce_status policy_loss(int kind, const PolicyInputs &in, const flce_policy_params *params,
+                        const void *hidden, const void *weight, const int64_t *labels,
+                        int64_t ignore_index, int64_t T, int64_t D, int64_t V,
+                        int64_t chunk_rows, const flce_logit_transform *transform,
+                        int64_t n_seq, float *loss_out, float *logp_out,
+                        const float *grad_loss, void *grad_hidden, float *grad_weight,
+                        int accumulate_grad_weight, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+  g_last_error[0] = 0;
+  PolicyLayout l;
+  FLCE_TRY(policy_layout(T, D, V, chunk_rows, n_seq, l));
+  Xform xf;
+  bool cap;
+  FLCE_TRY(make_xform(transform, xf, cap));
+  if (!params) return fail(FLCE_ERR_ARG, "params is NULL");
+  const flce_policy_params &pr = *params;
+  if (kind == kPolicyGrpo) {
+    if (!finite_nonneg(pr.beta) || !finite_nonneg(pr.eps_low) || pr.eps_low >= 1.f ||
+        !finite_nonneg(pr.eps_high))
+      return fail(FLCE_ERR_ARG, "GRPO needs beta >= 0, 0 <= eps_low < 1, eps_high >= 0");
+  } else {
+    if (!std::isfinite(pr.beta) || pr.beta <= 0.f)
+      return fail(FLCE_ERR_ARG, "beta = %g must be positive", (double)pr.beta);
+    if (kind == kPolicyDpo && n_seq % 2)
+      return fail(FLCE_ERR_SHAPE, "DPO needs an even n_seq (chosen, then rejected); got %lld",
+                  (long long)n_seq);
+    if (kind == kPolicyKto &&
+        (!finite_nonneg(pr.desirable_weight) || !finite_nonneg(pr.undesirable_weight)))
+      return fail(FLCE_ERR_ARG, "KTO weights must be finite and >= 0");
+  }
+  const bool grads = grad_loss != nullptr;
+  if (!loss_out) return fail(FLCE_ERR_ARG, "loss_out is NULL");
+  if (grads && !grad_weight)
+    return fail(FLCE_ERR_ARG, "a gradient was requested but grad_weight is NULL");
+  if (grad_weight && !aligned(grad_weight, 16))
+    return fail(FLCE_ERR_ARG, "grad_weight not 16-byte aligned");
+  if (!aligned(loss_out, 4) || (grad_loss && !aligned(grad_loss, 4)))
+    return fail(FLCE_ERR_ARG, "misaligned pointer");
+  if (T > 0) {
+    const bool need_seq = kind != kPolicyGrpo;
+    if (!hidden || !weight || !labels || !workspace || (grads && !grad_hidden) ||
+        (kind == kPolicyGrpo && !in.advantages) || (need_seq && !in.ref_seq) ||
+        (kind == kPolicyKto && !in.desirable))
+      return fail(FLCE_ERR_ARG, "a required pointer is NULL");
+    if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(labels, 8) ||
+        !aligned(workspace, 16) || (grads && !aligned(grad_hidden, 16)) ||
+        (logp_out && !aligned(logp_out, 4)) || (in.advantages && !aligned(in.advantages, 4)) ||
+        (in.old_logp && !aligned(in.old_logp, 4)) || (in.ref_logp && !aligned(in.ref_logp, 4)) ||
+        (in.ref_seq && !aligned(in.ref_seq, 4)) || (in.kl_ref && !aligned(in.kl_ref, 4)))
+      return fail(FLCE_ERR_ARG, "misaligned pointer");
+    if (workspace_bytes < l.total)
+      return fail(FLCE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
+                  l.total);
+  }
+  FLCE_TRY(check_device());
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) {
+    FLCE_TRY(fill(loss_out, 1, 0.f, s));
+    if (grads && !accumulate_grad_weight) FLCE_TRY(fill(grad_weight, V * D, 0.f, s));
+    return FLCE_OK;
+  }
+
+  char *ws = (char *)workspace;
+  float *logp = logp_out ? logp_out : (float *)(ws + l.off_logp);
+  float *lse = (float *)(ws + l.off_lse);
+  FLCE_TRY(flce_forward(hidden, weight, labels, T, D, V, ignore_index, chunk_rows,
+                        FLCE_MODE_LOGPROB, transform, logp, lse, nullptr, workspace, l.flce,
+                        stream));
+  PolicyParams pp;
+  pp.labels = labels;
+  pp.ignore_index = ignore_index;
+  pp.T = (int)T;
+  pp.n_seq = (int)n_seq;
+  pp.S = (int)(T / n_seq);
+  pp.logp = logp;
+  pp.advantages = in.advantages;
+  pp.old_logp = in.old_logp;
+  pp.ref_logp = in.ref_logp;
+  pp.ref_seq = in.ref_seq;
+  pp.desirable = in.desirable;
+  pp.kl_ref = in.kl_ref;
+  pp.grad_loss = grad_loss;
+  pp.beta = pr.beta;
+  pp.eps_low = pr.eps_low;
+  pp.eps_high = pr.eps_high;
+  pp.w_des = pr.desirable_weight;
+  pp.w_und = pr.undesirable_weight;
+  pp.seq_val = (double *)(ws + l.off_val);
+  pp.seq_n = (int *)(ws + l.off_n);
+  pp.seq_g = (float *)(ws + l.off_g);
+  pp.loss = loss_out;
+  pp.c = (float *)(ws + l.off_c);
+  if (kind == kPolicyGrpo)
+    launch_policy_kernels<kPolicyGrpo>(pp, grads, s);
+  else if (kind == kPolicyDpo)
+    launch_policy_kernels<kPolicyDpo>(pp, grads, s);
+  else
+    launch_policy_kernels<kPolicyKto>(pp, grads, s);
+  FLCE_TRY(launched("policy loss"));
+  if (!grads) return FLCE_OK;
+  return flce_backward(hidden, weight, labels, lse, T, D, V, ignore_index, chunk_rows,
+                       FLCE_MODE_LOGPROB, transform, pp.c, nullptr, grad_hidden, grad_weight,
+                       accumulate_grad_weight, workspace, l.flce, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t flce_policy_workspace_bytes(int64_t T, int64_t D, int64_t V, int64_t chunk_rows,
+                                   int64_t n_seq) {
+  PolicyLayout l;
+  if (policy_layout(T, D, V, chunk_rows, n_seq, l) != FLCE_OK) return 0;
+  return l.total;
+}
+
+flce_status flce_grpo_loss(const void *hidden, const void *weight, const int64_t *labels,
+                           int64_t ignore_index, int64_t T, int64_t D, int64_t V,
+                           int64_t chunk_rows, const flce_logit_transform *transform,
+                           int64_t n_seq, const float *advantages, const float *old_logp,
+                           const float *ref_logp, const flce_policy_params *params,
+                           float *loss_out, float *logp_out, const float *grad_loss,
+                           void *grad_hidden, float *grad_weight, int accumulate_grad_weight,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  PolicyInputs in = {advantages, old_logp, ref_logp, nullptr, nullptr, nullptr};
+  return policy_loss(kPolicyGrpo, in, params, hidden, weight, labels, ignore_index, T, D, V,
+                     chunk_rows, transform, n_seq, loss_out, logp_out, grad_loss, grad_hidden,
+                     grad_weight, accumulate_grad_weight, workspace, workspace_bytes, stream);
+}
+
+flce_status flce_dpo_loss(const void *hidden, const void *weight, const int64_t *labels,
+                          int64_t ignore_index, int64_t T, int64_t D, int64_t V,
+                          int64_t chunk_rows, const flce_logit_transform *transform,
+                          int64_t n_seq, const float *ref_seq_logp,
+                          const flce_policy_params *params, float *loss_out, float *logp_out,
+                          const float *grad_loss, void *grad_hidden, float *grad_weight,
+                          int accumulate_grad_weight, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  PolicyInputs in = {nullptr, nullptr, nullptr, ref_seq_logp, nullptr, nullptr};
+  return policy_loss(kPolicyDpo, in, params, hidden, weight, labels, ignore_index, T, D, V,
+                     chunk_rows, transform, n_seq, loss_out, logp_out, grad_loss, grad_hidden,
+                     grad_weight, accumulate_grad_weight, workspace, workspace_bytes, stream);
+}
+
+flce_status flce_kto_loss(const void *hidden, const void *weight, const int64_t *labels,
+                          int64_t ignore_index, int64_t T, int64_t D, int64_t V,
+                          int64_t chunk_rows, const flce_logit_transform *transform,
+                          int64_t n_seq, const float *ref_seq_logp, const uint8_t *desirable,
+                          const float *kl_ref, const flce_policy_params *params,
+                          float *loss_out, float *logp_out, const float *grad_loss,
+                          void *grad_hidden, float *grad_weight, int accumulate_grad_weight,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  PolicyInputs in = {nullptr, nullptr, nullptr, ref_seq_logp, kl_ref, desirable};
+  return policy_loss(kPolicyKto, in, params, hidden, weight, labels, ignore_index, T, D, V,
+                     chunk_rows, transform, n_seq, loss_out, logp_out, grad_loss, grad_hidden,
+                     grad_weight, accumulate_grad_weight, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -30,13 +30,21 @@ STATUS = {0: "FLCE_OK", 1: "FLCE_ERR_ARG", 2: "FLCE_ERR_SHAPE", 3: "FLCE_ERR_WOR
           4: "FLCE_ERR_UNSUPPORTED", 5: "FLCE_ERR_HIP"}
 EXPORTS = ("flce_workspace_bytes", "flce_forward", "flce_backward", "flce_describe_plan",
            "flce_status_string", "flce_last_error", "flce_distill_workspace_bytes",
-           "flce_distill", "flce_chunk_rows_for", "flce_tune")
+           "flce_distill", "flce_chunk_rows_for", "flce_tune", "flce_policy_workspace_bytes",
+           "flce_grpo_loss", "flce_dpo_loss", "flce_kto_loss")
 
 
 class LogitTransform(ctypes.Structure):
     """``flce_logit_transform``: multiply, divide, softcap, temperature (0 = skipped)."""
     _fields_ = [("scale_multiply", ctypes.c_float), ("scale_divide", ctypes.c_float),
                 ("softcap", ctypes.c_float), ("temperature", ctypes.c_float)]
+
+
+class PolicyParams(ctypes.Structure):
+    """``flce_policy_params``: beta, GRPO's clip range, KTO's weights."""
+    _fields_ = [("beta", ctypes.c_float), ("eps_low", ctypes.c_float),
+                ("eps_high", ctypes.c_float), ("desirable_weight", ctypes.c_float),
+                ("undesirable_weight", ctypes.c_float)]
 
 
 def _load() -> ctypes.CDLL:
@@ -63,6 +71,17 @@ def _load() -> ctypes.CDLL:
     lib.flce_tune.argtypes = [i64, i64, i64, i64, sz, ctypes.POINTER(ctypes.c_int64),
                               ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_size_t)]
     lib.flce_tune.restype = ctypes.c_int
+    pp = ctypes.POINTER(PolicyParams)
+    lib.flce_policy_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.flce_policy_workspace_bytes.restype = sz
+    head = [vp, vp, vp, i64, i64, i64, i64, i64, xp, i64]  # hidden .. transform, n_seq
+    tail = [pp, f32p, f32p, f32p, vp, f32p, ctypes.c_int, vp, sz, vp]
+    lib.flce_grpo_loss.argtypes = head + [f32p, f32p, f32p] + tail
+    lib.flce_grpo_loss.restype = ctypes.c_int
+    lib.flce_dpo_loss.argtypes = head + [f32p] + tail
+    lib.flce_dpo_loss.restype = ctypes.c_int
+    lib.flce_kto_loss.argtypes = head + [f32p, vp, f32p] + tail
+    lib.flce_kto_loss.restype = ctypes.c_int
     lib.flce_describe_plan.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
     lib.flce_describe_plan.restype = ctypes.c_int
     lib.flce_status_string.argtypes = [ctypes.c_int]
@@ -487,3 +506,109 @@ def chunked_distill_kl(student_hidden, student_weight, teacher_hidden, teacher_w
     return _ChunkedDistillKL.apply(student_hidden, student_weight, teacher_hidden,
                                    teacher_weight, labels, ignore_index, chunk_rows, reduction,
                                    xf)
+
+
+# ---------------------------------------------------------------------------
+# Policy-optimisation losses (GRPO, DPO, KTO) on the selective log-softmax
+# ---------------------------------------------------------------------------
+
+def policy_workspace_bytes(T: int, D: int, V: int, chunk_rows: int, n_seq: int) -> int:
+    n = lib.flce_policy_workspace_bytes(T, D, V, chunk_rows, n_seq)
+    if n == 0:
+        raise ValueError(f"invalid shape T={T} D={D} V={V} chunk_rows={chunk_rows} "
+                         f"n_seq={n_seq}")
+    return n
+
+
+def _f32_input(name, t, shape, dev, optional=True):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    _check_buffer(name, t, torch.float32, shape, dev)
+    return t
+
+
+def _policy(kind, hidden, weight, labels, n_seq, extra, params, *, ignore_index, chunk_rows,
+            transform, grad_loss, grad_hidden, grad_weight, accumulate, workspace, loss, logp):
+    _validate(hidden, weight, labels)
+    T, D = hidden.shape
+    V = weight.shape[0]
+    dev = hidden.device
+    loss = torch.empty((), dtype=torch.float32, device=dev) if loss is None else loss
+    _check_buffer("loss", loss, torch.float32, (), dev)
+    if logp is not None:
+        _check_buffer("logp", logp, torch.float32, (T,), dev)
+    grads = grad_loss is not None
+    if grads:
+        _check_buffer("grad_loss", grad_loss, torch.float32, (), dev)
+        if grad_hidden is None:
+            grad_hidden = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+        if grad_weight is None:
+            if accumulate:
+                raise ValueError("accumulate needs an existing grad_weight")
+            grad_weight = torch.empty((V, D), dtype=torch.float32, device=dev)
+        _check_buffer("grad_hidden", grad_hidden, torch.bfloat16, (T, D), dev)
+        _check_buffer("grad_weight", grad_weight, torch.float32, (V, D), dev)
+    need = policy_workspace_bytes(T, D, V, chunk_rows, n_seq)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, need, dev)
+    fn = {"grpo": lib.flce_grpo_loss, "dpo": lib.flce_dpo_loss, "kto": lib.flce_kto_loss}[kind]
+    _check(fn(_ptr(hidden), _ptr(weight), _ptr(labels), ignore_index, T, D, V, chunk_rows,
+              make_transform(**(transform or {})), n_seq, *extra, ctypes.byref(params),
+              _ptr(loss), _ptr(logp), _ptr(grad_loss),
+              _ptr(grad_hidden) if grads else None, _ptr(grad_weight) if grads else None,
+              1 if accumulate else 0, _ptr(workspace), workspace.numel(), _stream(dev)))
+    return loss, logp, (grad_hidden if grads else None), (grad_weight if grads else None)
+
+
+def grpo_loss(hidden, weight, labels, n_seq: int, advantages, *, old_logp=None, ref_logp=None,
+              beta: float = 0.0, eps_low: float = 0.2, eps_high: float = 0.2,
+              ignore_index: int = -100, chunk_rows: int = 256, transform=None,
+              grad_loss=None, grad_hidden=None, grad_weight=None, accumulate=False,
+              workspace=None, loss=None, logp=None):
+    """GRPO loss over n_seq sequences of the flattened batch (``flce_grpo_loss``):
+    (loss [], logp [T] or None, dH or None, dW or None)."""
+    T = hidden.shape[0]
+    dev = hidden.device
+    extra = (_ptr(_f32_input("advantages", advantages, (n_seq,), dev, optional=False)),
+             _ptr(_f32_input("old_logp", old_logp, (T,), dev)),
+             _ptr(_f32_input("ref_logp", ref_logp, (T,), dev)))
+    prm = PolicyParams(beta, eps_low, eps_high, 0.0, 0.0)
+    return _policy("grpo", hidden, weight, labels, n_seq, extra, prm, ignore_index=ignore_index,
+                   chunk_rows=chunk_rows, transform=transform, grad_loss=grad_loss,
+                   grad_hidden=grad_hidden, grad_weight=grad_weight, accumulate=accumulate,
+                   workspace=workspace, loss=loss, logp=logp)
+
+
+def dpo_loss(hidden, weight, labels, n_seq: int, ref_seq_logp, *, beta: float = 0.1,
+             ignore_index: int = -100, chunk_rows: int = 256, transform=None, grad_loss=None,
+             grad_hidden=None, grad_weight=None, accumulate=False, workspace=None, loss=None,
+             logp=None):
+    """DPO loss; sequences [0, n_seq/2) chosen, [n_seq/2, n_seq) rejected (``flce_dpo_loss``)."""
+    dev = hidden.device
+    extra = (_ptr(_f32_input("ref_seq_logp", ref_seq_logp, (n_seq,), dev, optional=False)),)
+    prm = PolicyParams(beta, 0.0, 0.0, 0.0, 0.0)
+    return _policy("dpo", hidden, weight, labels, n_seq, extra, prm, ignore_index=ignore_index,
+                   chunk_rows=chunk_rows, transform=transform, grad_loss=grad_loss,
+                   grad_hidden=grad_hidden, grad_weight=grad_weight, accumulate=accumulate,
+                   workspace=workspace, loss=loss, logp=logp)
+
+
+def kto_loss(hidden, weight, labels, n_seq: int, ref_seq_logp, desirable, *, kl_ref=None,
+             beta: float = 0.1, desirable_weight: float = 1.0, undesirable_weight: float = 1.0,
+             ignore_index: int = -100, chunk_rows: int = 256, transform=None, grad_loss=None,
+             grad_hidden=None, grad_weight=None, accumulate=False, workspace=None, loss=None,
+             logp=None):
+    """KTO loss with the reference point kl_ref (device scalar, clamped at 0; None = 0)
+    (``flce_kto_loss``)."""
+    dev = hidden.device
+    _check_buffer("desirable", desirable, torch.uint8, (n_seq,), dev)
+    extra = (_ptr(_f32_input("ref_seq_logp", ref_seq_logp, (n_seq,), dev, optional=False)),
+             _ptr(desirable), _ptr(_f32_input("kl_ref", kl_ref, (), dev)))
+    prm = PolicyParams(beta, 0.0, 0.0, desirable_weight, undesirable_weight)
+    return _policy("kto", hidden, weight, labels, n_seq, extra, prm, ignore_index=ignore_index,
+                   chunk_rows=chunk_rows, transform=transform, grad_loss=grad_loss,
+                   grad_hidden=grad_hidden, grad_weight=grad_weight, accumulate=accumulate,
+                   workspace=workspace, loss=loss, logp=logp)

@@ -247,3 +247,73 @@ def make_distill_inputs(w: DistillWorkload) -> DistillInputs:
     if w.reduction == "none":
         grad = np.random.default_rng(s_grad).standard_normal(w.T, dtype=np.float32)
     return DistillInputs(w, s_hidden, s_weight, t_hidden, t_weight, labels, grad)
+
+
+# ---------------------------------------------------------------------------
+# Policy-optimisation losses: the flattened batch is n_seq sequences of
+# seq_len tokens whose first prompt_len tokens are the prompt (label =
+# IGNORE_INDEX, not completion tokens); per-sequence and per-token side inputs
+# are standard normals that a caller scales and offsets (e.g. old log-probs =
+# the policy's log-probs + sigma * old_noise).
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class PolicyWorkload:
+    name: str
+    n_seq: int
+    seq_len: int
+    prompt_len: int
+    H: int
+    V: int
+    chunk_rows: int
+    w_std: float
+    seed: int
+
+    @property
+    def T(self) -> int:
+        return self.n_seq * self.seq_len
+
+
+POLICY_WORKLOADS = {
+    # the GRPO log-prob example (batch 4 x context 8,192 x vocab 128,000, hidden 4,096)
+    "grpo_qwen3": PolicyWorkload("grpo_qwen3", n_seq=4, seq_len=8192, prompt_len=1024, H=4096,
+                                 V=128000, chunk_rows=256, w_std=0.02, seed=3001),
+}
+
+
+def policy_custom(name: str, n_seq: int, seq_len: int, prompt_len: int, H: int, V: int, *,
+                  chunk_rows: int = 256, w_std: Optional[float] = None,
+                  seed: int = 7) -> PolicyWorkload:
+    return PolicyWorkload(name, n_seq=n_seq, seq_len=seq_len, prompt_len=prompt_len, H=H, V=V,
+                          chunk_rows=chunk_rows,
+                          w_std=1.0 / math.sqrt(H) if w_std is None else w_std, seed=seed)
+
+
+@dataclasses.dataclass
+class PolicyInputs:
+    workload: PolicyWorkload
+    hidden: np.ndarray        # uint16 bf16 bits [T, H]
+    weight: np.ndarray        # uint16 bf16 bits [V, H]
+    labels: np.ndarray        # int64 [T]: completion ids, IGNORE_INDEX on the prompts
+    advantages: np.ndarray    # float32 [n_seq] ~ N(0, 1)
+    old_noise: np.ndarray     # float32 [T] ~ N(0, 1)
+    ref_noise: np.ndarray     # float32 [T] ~ N(0, 1)
+    seq_noise: np.ndarray     # float32 [n_seq] ~ N(0, 1)
+    desirable: np.ndarray     # uint8 [n_seq], each 1 with probability 1/2
+
+
+def make_policy_inputs(w: PolicyWorkload) -> PolicyInputs:
+    root = np.random.SeedSequence(w.seed)
+    s_h, s_w, s_y, s_a, s_o, s_r, s_s, s_d = root.spawn(8)
+    hidden = normal_bf16_matrix(s_h, w.T, w.H, 1.0)
+    weight = normal_bf16_matrix(s_w, w.V, w.H, w.w_std)
+    labels = np.random.default_rng(s_y).integers(0, w.V, size=w.T, dtype=np.int64)
+    labels[(np.arange(w.T) % w.seq_len) < w.prompt_len] = IGNORE_INDEX
+    f32 = np.float32
+    return PolicyInputs(
+        w, hidden, weight, labels,
+        advantages=np.random.default_rng(s_a).standard_normal(w.n_seq, dtype=f32),
+        old_noise=np.random.default_rng(s_o).standard_normal(w.T, dtype=f32),
+        ref_noise=np.random.default_rng(s_r).standard_normal(w.T, dtype=f32),
+        seq_noise=np.random.default_rng(s_s).standard_normal(w.n_seq, dtype=f32),
+        desirable=(np.random.default_rng(s_d).random(w.n_seq) < 0.5).astype(np.uint8))

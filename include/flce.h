@@ -188,6 +188,87 @@ flce_status flce_distill(const void *student_hidden, const void *student_weight,
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Policy-optimisation losses on the selective log-softmax.  The TRL v1.13
+ * article (section on the other v1.13 changes) names fused linear GRPO, DPO
+ * and KTO losses built on the chunked LM head, and the Unsloth GRPO
+ * long-context page feeds the chunked selective log-softmax into GRPO; neither
+ * defines the losses, so these calls compute the published objectives:
+ *
+ *   GRPO (DeepSeekMath's group relative policy optimisation with its unbiased
+ *   KL estimator):  r_t = exp(logp_t - old_t),
+ *     s_t = min(r_t A_b, clip(r_t, 1 - eps_low, 1 + eps_high) A_b),
+ *     k_t = exp(ref_t - logp_t) - (ref_t - logp_t) - 1,
+ *     L = -(1/B') sum_{b: n_b > 0} (1/n_b) sum_{t in b} (s_t - beta k_t);
+ *   DPO (direct preference optimisation): pi_b = sum_{t in b} logp_t, the first
+ *     P = n_seq/2 sequences chosen and the last P rejected (pair i = (i, P+i)),
+ *     Delta_i = beta ((pi_i - ref_i) - (pi_{P+i} - ref_{P+i})),
+ *     L = (1/P) sum_i log(1 + exp(-Delta_i));
+ *   KTO (Kahneman-Tversky optimisation): r_b = pi_b - ref_b, z0 = max(*kl_ref, 0),
+ *     v_b = desirable_weight sigmoid(beta (r_b - z0)) for desirable sequences,
+ *           undesirable_weight sigmoid(beta (z0 - r_b)) otherwise,
+ *     L = (1/n_seq) sum_b (lambda_b - v_b).
+ *
+ * logp_t is log softmax(W h_t)[labels_t] (through the optional logit transform),
+ * as flce_forward computes it in FLCE_MODE_LOGPROB.  The T = n_seq * S tokens
+ * are n_seq sequences of S consecutive rows; tokens whose label is ignore_index
+ * are not completion tokens (no term, no gradient); n_b counts the completion
+ * tokens of sequence b and B' the sequences with at least one.  Inputs besides
+ * those of flce_forward, all device memory: GRPO advantages [n_seq] fp32,
+ * old_logp [T] fp32 (NULL: old = logp, ratio 1), ref_logp [T] fp32 (NULL: no
+ * KL term); DPO/KTO ref_seq_logp [n_seq] fp32 (the reference model's summed
+ * completion log-probs); KTO desirable [n_seq] uint8 (nonzero = desirable) and
+ * kl_ref (device scalar z0 estimate, NULL = 0).  old, ref, advantages and z0
+ * are constants.  params is a host pointer: beta (GRPO: KL weight >= 0;
+ * DPO/KTO: > 0), eps_low in [0, 1) and eps_high >= 0 (GRPO), the KTO weights
+ * (>= 0).  Outputs: *loss_out (device scalar, required), logp_out [T] (optional:
+ * the per-token log-probs, 0 off the completions).  If grad_loss (device scalar
+ * dTotal/dL) is given, grad_hidden [T x D] bf16 and grad_weight [V x D] fp32
+ * (added if accumulate_grad_weight) receive grad_loss * dL/dH and dL/dW through
+ * the log-prob backward (recompute), with grad_out_t = grad_loss * dL/dlogp_t.
+ * At a clipping kink GRPO takes the unclipped derivative.  Errors: n_seq must
+ * divide T (FLCE_ERR_SHAPE), DPO needs an even n_seq, parameters out of range
+ * give FLCE_ERR_ARG; otherwise the conventions of flce_forward (T == 0 gives
+ * *loss_out = 0 and, unless accumulating, a zero grad_weight).  The workspace,
+ * flce_policy_workspace_bytes(...), holds the cross-entropy workspace plus
+ * 12 T + 16 n_seq bytes (rounded).
+ */
+typedef struct flce_policy_params {
+  float beta;
+  float eps_low, eps_high;  /* GRPO */
+  float desirable_weight, undesirable_weight;  /* KTO */
+} flce_policy_params;
+
+size_t flce_policy_workspace_bytes(int64_t T, int64_t D, int64_t V, int64_t chunk_rows,
+                                   int64_t n_seq);
+
+flce_status flce_grpo_loss(const void *hidden, const void *weight, const int64_t *labels,
+                           int64_t ignore_index, int64_t T, int64_t D, int64_t V,
+                           int64_t chunk_rows, const flce_logit_transform *transform,
+                           int64_t n_seq, const float *advantages, const float *old_logp,
+                           const float *ref_logp, const flce_policy_params *params,
+                           float *loss_out, float *logp_out, const float *grad_loss,
+                           void *grad_hidden, float *grad_weight, int accumulate_grad_weight,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+flce_status flce_dpo_loss(const void *hidden, const void *weight, const int64_t *labels,
+                          int64_t ignore_index, int64_t T, int64_t D, int64_t V,
+                          int64_t chunk_rows, const flce_logit_transform *transform,
+                          int64_t n_seq, const float *ref_seq_logp,
+                          const flce_policy_params *params, float *loss_out, float *logp_out,
+                          const float *grad_loss, void *grad_hidden, float *grad_weight,
+                          int accumulate_grad_weight, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+flce_status flce_kto_loss(const void *hidden, const void *weight, const int64_t *labels,
+                          int64_t ignore_index, int64_t T, int64_t D, int64_t V,
+                          int64_t chunk_rows, const flce_logit_transform *transform,
+                          int64_t n_seq, const float *ref_seq_logp, const uint8_t *desirable,
+                          const float *kl_ref, const flce_policy_params *params,
+                          float *loss_out, float *logp_out, const float *grad_loss,
+                          void *grad_hidden, float *grad_weight, int accumulate_grad_weight,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Host policy (no device call).  The Unsloth GRPO page (section "Chunking der
  * abgeflachten Sequenzlaenge" and the configuration section after it) cuts
  * each sequence of the flattened batch into `multiplier` chunks, with the

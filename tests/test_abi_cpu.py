@@ -167,10 +167,74 @@ def test_distill_workspace_bound(flce):
     assert wb(10, 60, 64, 100, 16) == 0
     assert wb(10, 64, 0, 100, 16) == 0
     assert wb(0, 64, 64, 100, 16) > 0
-    # p_t (fp32) + G (bf16) blocks within one chunk of fp32 logits, plus terms linear in T, D
+    # the p_t block (fp32, G written over it) within one chunk of fp32 logits, plus terms
+    # linear in T and D
     for T, Ds, Dt, V, cr in [(16384, 4096, 5120, 151936, 256), (131072, 4096, 4096, 151936, 256),
                              (4096, 2048, 4096, 248320, 64)]:
         n = wb(T, Ds, Dt, V, cr)
         linear = 64 * T * 4 + 256 * 4 * 8192 * 4 + 8192 * Ds * 4 * 2 + (32 << 20)
         assert n <= cr * V * 4 + linear, (T, V, n)
         assert n < T * V * 4 / 10
+
+
+def _pol(flce, kind="grpo", **over):
+    a = dict(h=16, w=16, labels=16, ign=-100, T=8, D=64, V=100, cr=16, xf=None, n_seq=2,
+             adv=16, old=None, ref=None, refseq=16, des=16, klref=None,
+             prm=ctypes.byref(flce.PolicyParams(0.1, 0.2, 0.2, 1.0, 1.0)), loss=4, logp=None,
+             gl=None, gh=None, gw=None, acc=0, ws=16, wsb=1 << 30, stream=None)
+    a.update(over)
+    head = (a["h"], a["w"], a["labels"], a["ign"], a["T"], a["D"], a["V"], a["cr"], a["xf"],
+            a["n_seq"])
+    tail = (a["prm"], a["loss"], a["logp"], a["gl"], a["gh"], a["gw"], a["acc"], a["ws"],
+            a["wsb"], a["stream"])
+    if kind == "grpo":
+        return flce.lib.flce_grpo_loss(*head, a["adv"], a["old"], a["ref"], *tail)
+    if kind == "dpo":
+        return flce.lib.flce_dpo_loss(*head, a["refseq"], *tail)
+    return flce.lib.flce_kto_loss(*head, a["refseq"], a["des"], a["klref"], *tail)
+
+
+def _prm(flce, *v):
+    return ctypes.byref(flce.PolicyParams(*v))
+
+
+@pytest.mark.parametrize("kind", ["grpo", "dpo", "kto"])
+def test_policy_rejects_before_launch(flce, kind):
+    assert _pol(flce, kind, n_seq=3) == 2            # n_seq does not divide T
+    assert _pol(flce, kind, n_seq=0) == 2
+    assert _pol(flce, kind, T=-1) == 2
+    assert _pol(flce, kind, D=60) == 4
+    assert _pol(flce, kind, prm=None) == 1
+    assert _pol(flce, kind, loss=None) == 1
+    assert _pol(flce, kind, gl=4, gh=16) == 1        # gradient without grad_weight
+    assert _pol(flce, kind, gl=4, gw=16) == 1        # gradient without grad_hidden
+    assert _pol(flce, kind, h=None) == 1
+    assert _pol(flce, kind, h=8) == 1                # misaligned
+    assert _pol(flce, kind, wsb=16) == 3
+    bad = ctypes.byref(flce.LogitTransform(0.0, 0.0, 0.0, -1.0))
+    assert _pol(flce, kind, xf=bad) == 1
+
+
+def test_policy_parameter_checks(flce):
+    assert _pol(flce, "grpo", adv=None) == 1
+    assert _pol(flce, "grpo", prm=_prm(flce, -0.1, 0.2, 0.2, 0, 0)) == 1   # beta < 0
+    assert _pol(flce, "grpo", prm=_prm(flce, 0.0, 1.0, 0.2, 0, 0)) == 1    # eps_low >= 1
+    assert _pol(flce, "grpo", prm=_prm(flce, 0.0, 0.2, -0.5, 0, 0)) == 1   # eps_high < 0
+    assert _pol(flce, "grpo", prm=_prm(flce, float("nan"), 0.2, 0.2, 0, 0)) == 1
+    assert _pol(flce, "dpo", refseq=None) == 1
+    assert _pol(flce, "dpo", T=6, n_seq=3) == 2     # DPO pairs need an even count
+    assert _pol(flce, "dpo", prm=_prm(flce, 0.0, 0, 0, 0, 0)) == 1         # beta must be > 0
+    assert _pol(flce, "kto", des=None) == 1
+    assert _pol(flce, "kto", prm=_prm(flce, 0.1, 0, 0, -1.0, 1.0)) == 1    # weight < 0
+    assert _pol(flce, "kto", prm=_prm(flce, 0.1, 0, 0, 1.0, float("inf"))) == 1
+
+
+def test_policy_workspace_bytes(flce):
+    pb = flce.lib.flce_policy_workspace_bytes
+    assert pb(8, 64, 100, 16, 3) == 0
+    assert pb(8, 64, 100, 16, 0) == 0
+    assert pb(8, 60, 100, 16, 2) == 0
+    for T, D, V, cr, n in [(32768, 4096, 128000, 256, 4), (8, 64, 100, 16, 8), (0, 64, 100, 16, 1)]:
+        base = flce.lib.flce_workspace_bytes(T, D, V, cr)
+        got = pb(T, D, V, cr, n)
+        assert base + 12 * T + 16 * n <= got <= base + 12 * T + 16 * n + 7 * 256, (T, got, base)
