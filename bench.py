@@ -33,6 +33,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3_8b_sft")
+    ap.add_argument("--loss", choices=("grpo", "dpo", "kto"), default="grpo",
+                    help="policy loss of a policy workload (grpo_qwen3)")
     ap.add_argument("--chunk-rows", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
@@ -130,6 +132,9 @@ def main():
 
     if args.workload in synth.DISTILL_WORKLOADS:
         distill_main(args)
+        return
+    if args.workload in synth.POLICY_WORKLOADS:
+        policy_main(args)
         return
     w = synth.WORKLOADS[args.workload]
     chunk_rows = args.chunk_rows or w.chunk_rows
@@ -344,6 +349,139 @@ def distill_main(args) -> None:
         line["cpu_baseline"] = distill_cpu_baseline(x, min(args.cpu_sample_tokens, T),
                                                     args.cpu_sample_vocab)
     print(json.dumps(line), flush=True)
+
+
+# loss parameters of the policy workloads (GRPO: DeepSeekMath's beta and clip range)
+POLICY_PARAMS = dict(grpo=dict(beta=0.04, eps_low=0.2, eps_high=0.2), dpo=dict(beta=0.1),
+                     kto=dict(beta=0.1, desirable_weight=1.0, undesirable_weight=1.33))
+
+
+def policy_main(args):
+    """One step = one flce_{grpo,dpo,kto}_loss call with gradients: the fused log-prob
+    forward, the loss kernels and the log-prob backward over the whole batch."""
+    import numpy as np
+    import torch
+
+    from chunked_lm_head_amd import flce, synth
+
+    w = synth.POLICY_WORKLOADS[args.workload]
+    chunk_rows = args.chunk_rows or w.chunk_rows
+    t_gen = time.perf_counter()
+    x = synth.make_policy_inputs(w)
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    h, W = bf16(x.hidden), bf16(x.weight)
+    y = torch.from_numpy(x.labels).to(dev)
+    T, D, V, B = w.T, w.H, w.V, w.n_seq
+    prm = POLICY_PARAMS[args.loss]
+    # side inputs near the policy's own log-probs, formed before the timed region
+    lp, _, _ = flce.forward(h, W, y, chunk_rows=chunk_rows, mode="logprob")
+    noise = {k: torch.from_numpy(getattr(x, k)).to(dev)
+             for k in ("advantages", "old_noise", "ref_noise", "seq_noise")}
+    mask = y != synth.IGNORE_INDEX
+    pi = torch.where(mask, lp, 0.0).view(B, -1).double().sum(dim=1)
+    ws = torch.empty(flce.policy_workspace_bytes(T, D, V, chunk_rows, B), dtype=torch.uint8,
+                     device=dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    logp = torch.empty(T, dtype=torch.float32, device=dev)
+    dh = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((V, D), dtype=torch.float32, device=dev)
+    one = torch.ones((), dtype=torch.float32, device=dev)
+    common = dict(chunk_rows=chunk_rows, grad_loss=one, grad_hidden=dh, grad_weight=dw,
+                  workspace=ws, loss=loss, logp=logp)
+    if args.loss == "grpo":
+        old = (lp + 0.15 * noise["old_noise"]).float().contiguous()
+        ref = (lp + 0.3 * noise["ref_noise"]).float().contiguous()
+
+        def step():
+            flce.grpo_loss(h, W, y, B, noise["advantages"], old_logp=old, ref_logp=ref,
+                           **prm, **common)
+    elif args.loss == "dpo":
+        ref_seq = (pi + (1.5 / prm["beta"]) * noise["seq_noise"].double()).float().contiguous()
+
+        def step():
+            flce.dpo_loss(h, W, y, B, ref_seq, **prm, **common)
+    else:
+        ref_seq = (pi + (1.5 / prm["beta"]) * noise["seq_noise"].double()).float().contiguous()
+        des = torch.from_numpy(x.desirable).to(dev)
+        kl_ref = torch.tensor(0.05, dtype=torch.float32, device=dev)
+
+        def step():
+            flce.kto_loss(h, W, y, B, ref_seq, des, kl_ref=kl_ref, **prm, **common)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    flops = 8.0 * T * V * D
+    achieved = flops / (ms / 1e3)
+    line = {
+        "metric": f"{args.loss.upper()} loss fwd+bwd tokens/s (fused LM head, selective log-softmax)",
+        "value": round(T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "loss": args.loss, "tokens": T, "hidden": D,
+                   "vocab": V, "sequences": B, "seq_len": w.seq_len,
+                   "prompt_tokens_per_sequence": w.prompt_len, "chunk_rows": chunk_rows,
+                   "params": prm},
+        "loss_value": round(float(loss.cpu()), 6),
+        "workspace_bytes": int(ws.numel()),
+        "roofline": {
+            "kernel": f"whole flce_{args.loss}_loss call (log-prob forward, loss kernels, "
+                      "recompute, dH, dW; prompt rows are computed too)",
+            "bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": PEAK_BF16 / 1e12,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4), "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+        },
+    }
+    print(f"[bench] {args.workload} {args.loss}: inputs drawn in {t_gen:.1f} s; step {ms:.3f} ms",
+          file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = policy_cpu_baseline(x, args.loss, prm,
+                                                   min(args.cpu_sample_tokens, T))
+    print(json.dumps(line), flush=True)
+
+
+def policy_cpu_baseline(x, loss: str, prm: dict, n_tokens: int) -> dict:
+    """The oracle, untouched, on the first n_tokens tokens against the whole vocabulary:
+    log-probs, the loss (the sample as one sequence, or for DPO its halves as one pair;
+    on-policy ratios, reference = policy) and the log-prob backward."""
+    import numpy as np
+
+    from oracle import policy_oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    h, wt, y = x.hidden[:n_tokens], x.weight, x.labels[:n_tokens]
+    t0 = time.perf_counter()
+    lp = policy_oracle.logp(h, wt, y)
+    if loss == "grpo":
+        r = policy_oracle.grpo_from_logp(lp, y, 1, x.advantages[:1], ref_logp=lp, **prm)
+    elif loss == "dpo":  # the two halves of the sample as one chosen / rejected pair
+        r = policy_oracle.dpo_from_logp(lp, y, 2, np.zeros(2), **prm)
+    else:
+        r = policy_oracle.kto_from_logp(lp, y, 1, np.zeros(1), x.desirable[:1], **prm)
+    policy_oracle.grads(h, wt, y, r.dlogp)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"first {n_tokens} tokens x all {wt.shape[0]} vocabulary rows, float64 "
+                      f"numpy log-probs + {loss.upper()} loss + backward in {dt:.1f} s"}
 
 
 def distill_cpu_baseline(x, n_tokens: int, n_vocab: int) -> dict:

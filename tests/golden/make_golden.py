@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 from chunked_lm_head_amd import synth  # noqa: E402  (inputs only)
 from oracle import distill_oracle as dst  # noqa: E402
 from oracle import flce_oracle as o  # noqa: E402
+from oracle import policy_oracle as po  # noqa: E402
 
 FULL = ("single_chunk", "qwen3_8b_sft", "grpo_logprob", "long_context")
 # name -> (workload, transform)
@@ -123,6 +124,81 @@ def make_distill(name: str) -> str:
     return path
 
 
+POLICY = ("grpo_qwen3",)
+# loss parameters of the policy goldens (GRPO: DeepSeekMath's beta and clip range)
+POLICY_PARAMS = dict(grpo_beta=0.04, eps_low=0.2, eps_high=0.2, dpo_beta=0.1, kto_beta=0.1,
+                     kl_ref=0.05, desirable_weight=1.0, undesirable_weight=1.33)
+GRAD_LOSS = 1.0
+
+
+def kink_free_old(lp, old, eps_low, eps_high, mask):
+    """Shift float32 old log-probs until no ratio lies within 1e-3 of a clip bound, so that
+    fp32 and fp64 log-probs take the same branch of the clipped surrogate."""
+    old = old.copy()
+    for _ in range(10):
+        r = np.exp(lp - old.astype(np.float64))
+        near = ((np.abs(r - (1 + eps_high)) < 1e-3) | (np.abs(r - (1 - eps_low)) < 1e-3)) & mask
+        if not near.any():
+            return old
+        old[near] += np.float32(0.01)
+    raise RuntimeError("could not move the ratios off the clipping bounds")
+
+
+def make_policy(name: str) -> str:
+    """GRPO, DPO and KTO at full size from one float64 forward over all tokens: the
+    side inputs built from the oracle's log-probs (old and reference log-probs, reference
+    sequence log-probs), each loss, and for each the dH rows of sampled tokens and the dW
+    rows of sampled vocabulary entries (those need every token's lse and dL/dlogp)."""
+    w = synth.POLICY_WORKLOADS[name]
+    P = POLICY_PARAMS
+    t0 = time.time()
+    x = synth.make_policy_inputs(w)
+    rng = np.random.default_rng(w.seed + 77)
+    f = o.forward(x.hidden, x.weight, x.labels, synth.IGNORE_INDEX, "logprob")
+    lp = f.out
+    mask = x.labels != synth.IGNORE_INDEX
+    old = kink_free_old(lp, (lp + 0.15 * x.old_noise).astype(np.float32), P["eps_low"],
+                        P["eps_high"], mask)
+    ref = (lp + 0.3 * x.ref_noise).astype(np.float32)
+    pi = np.where(mask, lp, 0.0).reshape(w.n_seq, w.seq_len).sum(axis=1)
+    ref_dpo = (pi + (1.5 / P["dpo_beta"]) * x.seq_noise).astype(np.float32)
+    ref_kto = (pi + (1.5 / P["kto_beta"]) * x.seq_noise).astype(np.float32)
+    losses = {
+        "grpo": po.grpo_from_logp(lp, x.labels, w.n_seq, x.advantages, old_logp=old,
+                                  ref_logp=ref, beta=P["grpo_beta"], eps_low=P["eps_low"],
+                                  eps_high=P["eps_high"]),
+        "dpo": po.dpo_from_logp(lp, x.labels, w.n_seq, ref_dpo, beta=P["dpo_beta"]),
+        "kto": po.kto_from_logp(lp, x.labels, w.n_seq, ref_kto, x.desirable,
+                                kl_ref=P["kl_ref"], beta=P["kto_beta"],
+                                desirable_weight=P["desirable_weight"],
+                                undesirable_weight=P["undesirable_weight"]),
+    }
+    tw = synth.Workload(name, T=w.T, H=w.H, V=w.V, chunk_rows=w.chunk_rows, w_std=w.w_std,
+                        ignore_count=0, mode="logprob", reduction="none", seed=w.seed,
+                        seq_len=w.seq_len, prompt_len=w.prompt_len)
+    tokens = sample_tokens(tw, x.labels, rng)
+    vocab = sample_vocab(tw, x.labels, tokens, rng)
+    out = dict(tokens=tokens, vocab=vocab, logp=lp[tokens], seed=np.int64(w.seed), old=old,
+               ref=ref, ref_dpo=ref_dpo, ref_kto=ref_kto, grad_loss=np.float64(GRAD_LOSS),
+               **{k: np.float64(v) for k, v in P.items()})
+    for k, r in losses.items():
+        c = -GRAD_LOSS * r.dlogp          # log-prob mode: G = -grad_out (P - onehot)
+        out[f"{k}_loss"] = np.float64(r.loss)
+        out[f"{k}_dh"] = o.grad_hidden_rows(x.hidden, x.weight, x.labels, tokens, c[tokens],
+                                            synth.IGNORE_INDEX).astype(np.float32)
+        out[f"{k}_dw"] = o.grad_weight_rows(x.hidden, x.weight, x.labels, vocab, c,
+                                            f.lse).astype(np.float32)
+    path = os.path.join(HERE, f"{name}.npz")
+    np.savez(path, **out)
+    print(f"{name}: {time.time() - t0:.0f} s -> {path}", flush=True)
+    return path
+
+
 if __name__ == "__main__":
-    for n in (sys.argv[1:] or FULL + tuple(VARIANTS) + DISTILL):
-        (make_distill if n in DISTILL else make)(n)
+    for n in (sys.argv[1:] or FULL + tuple(VARIANTS) + DISTILL + POLICY):
+        if n in DISTILL:
+            make_distill(n)
+        elif n in POLICY:
+            make_policy(n)
+        else:
+            make(n)

@@ -161,3 +161,73 @@ def test_distill_full_size_against_oracle_samples():
     lhs = float((dh.double() * sh.double()).sum())
     rhs = float((dw.double() * sw.double()).sum())
     assert abs(lhs - rhs) <= 1e-2 * max(abs(lhs), abs(rhs), 1e-30), (lhs, rhs)
+
+
+_POLICY = {}
+
+
+def _policy_inputs():
+    if not _POLICY:
+        w = synth.POLICY_WORKLOADS["grpo_qwen3"]
+        _POLICY.update(w=w, x=synth.make_policy_inputs(w))
+    return _POLICY["w"], _POLICY["x"]
+
+
+@pytest.mark.parametrize("kind", ["grpo", "dpo", "kto"])
+def test_policy_full_size_against_oracle_samples(kind):
+    """GRPO, DPO and KTO at the GRPO example's size (4 sequences of 8,192 tokens, 1,024 of
+    them prompt, hidden 4,096, vocabulary 128,000); old / reference log-probs and reference
+    sequence log-probs are stored with the oracle values (built from the oracle's own
+    log-probs by the golden script)."""
+    from chunked_lm_head_amd import flce
+
+    g = _golden("grpo_qwen3")
+    w, x = _policy_inputs()
+    assert int(g["seed"]) == w.seed
+    print(f"case grpo_qwen3 {kind}: T={w.T} D={w.H} V={w.V} sequences {w.n_seq}", flush=True)
+    dev = gu.device()
+    h = gu.bf16_tensor(x.hidden, dev)
+    W = gu.bf16_tensor(x.weight, dev)
+    y = torch.from_numpy(x.labels).to(dev)
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    ws = torch.empty(flce.policy_workspace_bytes(w.T, w.H, w.V, w.chunk_rows, w.n_seq),
+                     dtype=torch.uint8, device=dev)
+    common = dict(chunk_rows=w.chunk_rows, workspace=ws,
+                  grad_loss=torch.tensor(float(g["grad_loss"]), dtype=torch.float32, device=dev),
+                  logp=torch.empty(w.T, dtype=torch.float32, device=dev))
+    if kind == "grpo":
+        out = flce.grpo_loss(h, W, y, w.n_seq, t(x.advantages), old_logp=t(g["old"]),
+                             ref_logp=t(g["ref"]), beta=float(g["grpo_beta"]),
+                             eps_low=float(g["eps_low"]), eps_high=float(g["eps_high"]), **common)
+    elif kind == "dpo":
+        out = flce.dpo_loss(h, W, y, w.n_seq, t(g["ref_dpo"]), beta=float(g["dpo_beta"]),
+                            **common)
+    else:
+        out = flce.kto_loss(h, W, y, w.n_seq, t(g["ref_kto"]), t(x.desirable),
+                            kl_ref=torch.tensor(float(g["kl_ref"]), dtype=torch.float32,
+                                                device=dev),
+                            beta=float(g["kto_beta"]),
+                            desirable_weight=float(g["desirable_weight"]),
+                            undesirable_weight=float(g["undesirable_weight"]), **common)
+    torch.cuda.synchronize()
+    loss, logp, dh, dw = out
+    tok = torch.from_numpy(g["tokens"]).to(dev)
+    voc = torch.from_numpy(g["vocab"]).to(dev)
+    e = (abs(float(loss.cpu()) - float(g[f"{kind}_loss"])),
+         gu.max_abs(logp[tok].cpu().numpy(), g["logp"]),
+         gu.rel_fro(dh[tok].float().cpu().numpy(), g[f"{kind}_dh"].astype(np.float64)),
+         gu.rel_fro(dw[voc].cpu().numpy(), g[f"{kind}_dw"].astype(np.float64)))
+    print(f"  loss {float(loss.cpu()):.6f} (oracle {float(g[f'{kind}_loss']):.6f}) |d loss| "
+          f"{e[0]:.2e} |d logp| {e[1]:.2e} dH rel {e[2]:.2e} dW rel {e[3]:.2e}", flush=True)
+    assert e[0] <= gu.OUT_TOL and e[1] <= gu.OUT_TOL, e
+    assert e[2] <= gu.GRAD_TOL and e[3] <= gu.GRAD_TOL, e
+    # properties on the complete outputs
+    lhs = float((dh.double() * h.double()).sum())
+    rhs = float((dw.double() * W.double()).sum())
+    assert abs(lhs - rhs) <= 1e-2 * max(abs(lhs), abs(rhs), 1e-30), (lhs, rhs)
+    prompt = y == synth.IGNORE_INDEX
+    assert bool((dh[prompt] == 0).all()) and bool((logp[prompt] == 0).all())
+    assert bool(torch.isfinite(logp).all())
