@@ -612,3 +612,48 @@ def kto_loss(hidden, weight, labels, n_seq: int, ref_seq_logp, desirable, *, kl_
                    chunk_rows=chunk_rows, transform=transform, grad_loss=grad_loss,
                    grad_hidden=grad_hidden, grad_weight=grad_weight, accumulate=accumulate,
                    workspace=workspace, loss=loss, logp=logp)
+
+
+class _PolicyLossFn(torch.autograd.Function):
+    """A policy loss as a scalar of the policy's hidden states and lm_head.
+
+    The library call computes the loss and, with an upstream scalar of 1, its
+    gradients in one pass (the log-prob forward, the loss kernels and the
+    recomputing backward); the backward multiplies them by the upstream scalar
+    (two elementwise products in PyTorch; dH is rounded to bf16 once more)."""
+
+    @staticmethod
+    def forward(ctx, hidden, weight, call):
+        need = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
+        one = torch.ones((), dtype=torch.float32, device=hidden.device)
+        loss, _, dh, dw = call(hidden, weight, one if need else None)
+        if need:
+            ctx.save_for_backward(dh, dw)
+        ctx.need = need
+        return loss
+
+    @staticmethod
+    def backward(ctx, grad):
+        if not ctx.need:
+            return None, None, None
+        dh, dw = ctx.saved_tensors
+        g = grad.float()
+        return (dh.float() * g).to(torch.bfloat16), (dw * g).to(torch.bfloat16), None
+
+
+def grpo_loss_fn(hidden, weight, labels, n_seq: int, advantages, **kw):
+    """Autograd-aware ``grpo_loss`` (keyword arguments as there, without the gradient ones)."""
+    return _PolicyLossFn.apply(hidden, weight, lambda h, w, gl: grpo_loss(
+        h.detach(), w.detach(), labels, n_seq, advantages, grad_loss=gl, **kw))
+
+
+def dpo_loss_fn(hidden, weight, labels, n_seq: int, ref_seq_logp, **kw):
+    """Autograd-aware ``dpo_loss``."""
+    return _PolicyLossFn.apply(hidden, weight, lambda h, w, gl: dpo_loss(
+        h.detach(), w.detach(), labels, n_seq, ref_seq_logp, grad_loss=gl, **kw))
+
+
+def kto_loss_fn(hidden, weight, labels, n_seq: int, ref_seq_logp, desirable, **kw):
+    """Autograd-aware ``kto_loss``."""
+    return _PolicyLossFn.apply(hidden, weight, lambda h, w, gl: kto_loss(
+        h.detach(), w.detach(), labels, n_seq, ref_seq_logp, desirable, grad_loss=gl, **kw))

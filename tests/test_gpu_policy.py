@@ -206,3 +206,40 @@ def test_empty_batch():
     torch.cuda.synchronize()
     assert float(loss.cpu()) == 0.0 and float(dw.abs().max().cpu()) == 0.0
     assert math.isfinite(float(loss.cpu()))
+
+
+def test_autograd_wrappers():
+    from chunked_lm_head_amd import flce
+
+    dev = gu.device()
+    for case in (CASES[0], CASES[7], CASES[10]):  # GRPO, DPO, KTO
+        _, kind, _, opt = case
+        x, labels, tr, side = _prepare(case)
+        want, dh, dw = _oracle(kind, x, labels, tr, side, opt)   # upstream GRAD_LOSS
+        h = gu.bf16_tensor(x.hidden, dev).requires_grad_()
+        W = gu.bf16_tensor(x.weight, dev).requires_grad_()
+        y = torch.from_numpy(labels).to(dev)
+
+        def t(a):
+            return torch.from_numpy(np.asarray(a)).to(dev)
+
+        kw = dict(chunk_rows=x.workload.chunk_rows, transform=gu.binding_transform(tr))
+        if kind == "grpo":
+            loss = flce.grpo_loss_fn(h, W, y, x.workload.n_seq, t(side["advantages"]),
+                                     old_logp=t(side["old"]), ref_logp=t(side["ref"]),
+                                     beta=opt["beta"], **kw)
+        elif kind == "dpo":
+            loss = flce.dpo_loss_fn(h, W, y, x.workload.n_seq, t(side["ref_seq"]),
+                                    beta=opt["beta"], **kw)
+        else:
+            loss = flce.kto_loss_fn(h, W, y, x.workload.n_seq, t(side["ref_seq"]),
+                                    t(side["desirable"]),
+                                    kl_ref=torch.tensor(opt["kl_ref"], dtype=torch.float32,
+                                                        device=dev),
+                                    beta=opt["beta"], desirable_weight=opt["wd"],
+                                    undesirable_weight=opt["wu"], **kw)
+        (loss * GRAD_LOSS).backward()
+        torch.cuda.synchronize()
+        assert abs(float(loss.detach().cpu()) - want.loss) <= gu.OUT_TOL
+        assert gu.rel_fro(h.grad.float().cpu().numpy(), dh) <= gu.GRAD_TOL
+        assert gu.rel_fro(W.grad.float().cpu().numpy(), dw) <= gu.GRAD_TOL
