@@ -15,9 +15,7 @@ CEILING_SRC = os.path.join(CSRC, "mfma_ceiling.hip")
 CEILING_BIN = os.path.join(PKG, "mfma_ceiling")  # measurement program, not part of the library
 LDS_SRC = os.path.join(CSRC, "lds_rate.hip")
 LDS_BIN = os.path.join(PKG, "lds_rate")          # measurement program, not part of the library
-SOURCES = [os.path.join(CSRC, "flce_api.hip")]
-DEPENDS = SOURCES + [os.path.join(CSRC, f) for f in ("flce_tile.hpp", "flce_kernels.hpp")] + [
-    os.path.join(INCLUDE, "flce.h")]
+SOURCES = [os.path.join(CSRC, "flce_api.hip")]  # includes every kernel header of csrc/
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
