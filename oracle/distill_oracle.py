@@ -26,6 +26,14 @@ Reading (a plain, slow, obviously correct definition in float64):
   ``dHs = G Ws`` and ``dWs = G^T Hs``, exactly the cross-entropy backward
   with the one-hot target replaced by the teacher's distribution.
 
+The same article lists a fused linear JSD loss by name.  ``divergence="jsd"``
+takes the generalized Jensen-Shannon divergence with weight beta in (0, 1), the
+textbook definition (Lin, 1991; the skewed form used for distillation):
+``M = beta p_t + (1 - beta) p_s`` and
+``JSD_t = beta KL(p_t || M) + (1 - beta) KL(p_s || M)`` (beta = 1/2 is the
+symmetric JSD).  Its gradient in the student's logits is
+``dJSD/dzs_v = p_s,v (g_v - sum_u p_s,u g_u)``, ``g = (1 - beta) log(p_s / M)``.
+
 Large inputs are processed in row blocks of complete vocabulary rows; a block
 is a schedule detail, not part of the method.
 """
@@ -64,9 +72,33 @@ def _rows(h, w, transform, r0, r1):
     return fo._logits(h[r0:r1], w, transform)
 
 
+def _xlogy_ratio(a, log_a, log_m):
+    """a (log a - log m), taken as 0 where a = 0."""
+    return np.where(a > 0, a * (log_a - log_m), 0.0)
+
+
+def jsd_rows(log_ps, log_pt, beta: float) -> np.ndarray:
+    """Per-row generalized JSD of the student (log_ps) and teacher (log_pt) rows."""
+    ps, pt = np.exp(log_ps), np.exp(log_pt)
+    m = beta * pt + (1.0 - beta) * ps
+    with np.errstate(divide="ignore"):
+        log_m = np.log(m)
+    return (beta * _xlogy_ratio(pt, log_pt, log_m)
+            + (1.0 - beta) * _xlogy_ratio(ps, log_ps, log_m)).sum(axis=1)
+
+
+def _check_divergence(divergence: str, beta: float) -> None:
+    if divergence not in ("kl", "jsd"):
+        raise ValueError(divergence)
+    if divergence == "jsd" and not 0.0 < beta < 1.0:
+        raise ValueError(f"beta = {beta} must lie in (0, 1)")
+
+
 def forward(s_hidden, s_weight, t_hidden, t_weight, labels=None,
             ignore_index: int = IGNORE_INDEX,
-            transform: Optional[fo.LogitTransform] = None) -> DistillForward:
+            transform: Optional[fo.LogitTransform] = None, divergence: str = "kl",
+            beta: float = 0.5) -> DistillForward:
+    _check_divergence(divergence, beta)
     hs, ws = fo._as_f64(s_hidden), fo._as_f64(s_weight)
     ht, wt = fo._as_f64(t_hidden), fo._as_f64(t_weight)
     T, V = hs.shape[0], ws.shape[0]
@@ -85,7 +117,10 @@ def forward(s_hidden, s_weight, t_hidden, t_weight, labels=None,
         lse_t[r0:r1] = fo.logsumexp_rows(zt)
         log_ps = zs - lse_s[r0:r1, None]
         log_pt = zt - lse_t[r0:r1, None]
-        kl[r0:r1] = (np.exp(log_pt) * (log_pt - log_ps)).sum(axis=1)
+        if divergence == "kl":
+            kl[r0:r1] = (np.exp(log_pt) * (log_pt - log_ps)).sum(axis=1)
+        else:
+            kl[r0:r1] = jsd_rows(log_ps, log_pt, beta)
     kl = np.where(valid, kl, 0.0)
     n_valid = int(valid.sum())
     mean = float(kl[valid].sum() / n_valid) if n_valid else 0.0
@@ -106,17 +141,28 @@ def token_scale(labels, T: int, ignore_index: int = IGNORE_INDEX,
     return np.where(valid, g, 0.0)
 
 
-def grad_logits(zs, zt, c, dzs=None) -> np.ndarray:
-    """G = c_t (softmax(zs_t) - softmax(zt_t)), times dzs'/dzs under a transform."""
-    g = (np.exp(_log_softmax(zs)) - np.exp(_log_softmax(zt))) * c[:, None]
+def grad_logits(zs, zt, c, dzs=None, divergence: str = "kl", beta: float = 0.5) -> np.ndarray:
+    """dL/dzs: KL: c_t (softmax(zs_t) - softmax(zt_t)); JSD: c_t p_s (g - sum p_s g) with
+    g = (1 - beta) log(p_s / M); times dzs'/dzs under a transform."""
+    if divergence == "kl":
+        g = (np.exp(_log_softmax(zs)) - np.exp(_log_softmax(zt))) * c[:, None]
+    else:
+        log_ps, log_pt = _log_softmax(zs), _log_softmax(zt)
+        ps = np.exp(log_ps)
+        log_m = np.log(beta * np.exp(log_pt) + (1.0 - beta) * ps)
+        gv = (1.0 - beta) * (log_ps - log_m)
+        gbar = (ps * gv).sum(axis=1, keepdims=True)
+        g = ps * (gv - gbar) * c[:, None]
     return g if dzs is None else g * dzs
 
 
 def backward(s_hidden, s_weight, t_hidden, t_weight, labels=None,
              ignore_index: int = IGNORE_INDEX, grad_out: Optional[np.ndarray] = None,
              grad_mean: Optional[float] = None,
-             transform: Optional[fo.LogitTransform] = None):
+             transform: Optional[fo.LogitTransform] = None, divergence: str = "kl",
+             beta: float = 0.5):
     """(dHs [T, Hs], dWs [V, Hs]) in float64; the teacher receives no gradient."""
+    _check_divergence(divergence, beta)
     hs, ws = fo._as_f64(s_hidden), fo._as_f64(s_weight)
     ht, wt = fo._as_f64(t_hidden), fo._as_f64(t_weight)
     T, V = hs.shape[0], ws.shape[0]
@@ -128,7 +174,7 @@ def backward(s_hidden, s_weight, t_hidden, t_weight, labels=None,
         r1 = min(T, r0 + step)
         zs, dzs = _rows(hs, ws, transform, r0, r1)
         zt, _ = _rows(ht, wt, transform, r0, r1)
-        g = grad_logits(zs, zt, c[r0:r1], dzs)
+        g = grad_logits(zs, zt, c[r0:r1], dzs, divergence, beta)
         dh[r0:r1] = g @ ws
         dw += g.T @ hs[r0:r1]
     return dh, dw
@@ -136,40 +182,71 @@ def backward(s_hidden, s_weight, t_hidden, t_weight, labels=None,
 
 def forward_rows(s_hidden, s_weight, t_hidden, t_weight, rows: Sequence[int], labels=None,
                  ignore_index: int = IGNORE_INDEX,
-                 transform: Optional[fo.LogitTransform] = None):
+                 transform: Optional[fo.LogitTransform] = None, divergence: str = "kl",
+                 beta: float = 0.5):
     """(kl, lse_s, lse_t) of the selected tokens only (each row needs its own logits)."""
     rows = np.asarray(rows, dtype=np.int64)
     lab = None if labels is None else np.asarray(labels)[rows]
     f = forward(np.asarray(s_hidden)[rows], s_weight, np.asarray(t_hidden)[rows], t_weight,
-                lab, ignore_index, transform)
+                lab, ignore_index, transform, divergence, beta)
     return f.kl, f.lse_s, f.lse_t
 
 
 def grad_hidden_rows(s_hidden, s_weight, t_hidden, t_weight, rows: Sequence[int],
-                     c_rows: np.ndarray, transform: Optional[fo.LogitTransform] = None):
+                     c_rows: np.ndarray, transform: Optional[fo.LogitTransform] = None,
+                     divergence: str = "kl", beta: float = 0.5):
     """dHs rows of the selected tokens given their scales c_t."""
     rows = np.asarray(rows, dtype=np.int64)
     hs, ws = fo._as_f64(np.asarray(s_hidden)[rows]), fo._as_f64(s_weight)
     ht, wt = fo._as_f64(np.asarray(t_hidden)[rows]), fo._as_f64(t_weight)
     zs, dzs = fo._logits(hs, ws, transform)
     zt, _ = fo._logits(ht, wt, transform)
-    return grad_logits(zs, zt, np.asarray(c_rows, dtype=np.float64), dzs) @ ws
+    return grad_logits(zs, zt, np.asarray(c_rows, dtype=np.float64), dzs, divergence, beta) @ ws
 
 
 def grad_weight_rows(s_hidden, s_weight, t_hidden, t_weight, vocab_rows: Sequence[int],
                      c: np.ndarray, lse_s: np.ndarray, lse_t: np.ndarray,
-                     transform: Optional[fo.LogitTransform] = None) -> np.ndarray:
+                     transform: Optional[fo.LogitTransform] = None, divergence: str = "kl",
+                     beta: float = 0.5, gbar: Optional[np.ndarray] = None) -> np.ndarray:
     """dWs rows of the selected vocabulary entries: dWs_v = sum_t G_tv hs_t.
 
-    Needs both log-sum-exps of every token (from ``forward``); only the
-    selected columns of the logits are formed."""
+    Needs both log-sum-exps of every token (from ``forward``), and for JSD the
+    per-token sum_u p_s,u g_u (``jsd_gbar``); only the selected columns of the
+    logits are formed."""
     vr = np.asarray(vocab_rows, dtype=np.int64)
     hs = fo._as_f64(s_hidden)
     ht = fo._as_f64(t_hidden)
     zs, dzs = fo._logits(hs, fo._as_f64(np.asarray(s_weight)[vr]), transform)
     zt, _ = fo._logits(ht, fo._as_f64(np.asarray(t_weight)[vr]), transform)
-    g = np.exp(zs - np.asarray(lse_s)[:, None]) - np.exp(zt - np.asarray(lse_t)[:, None])
+    log_ps = zs - np.asarray(lse_s)[:, None]
+    log_pt = zt - np.asarray(lse_t)[:, None]
+    if divergence == "kl":
+        g = np.exp(log_ps) - np.exp(log_pt)
+    else:
+        ps = np.exp(log_ps)
+        gv = (1.0 - beta) * (log_ps - np.log(beta * np.exp(log_pt) + (1.0 - beta) * ps))
+        g = ps * (gv - np.asarray(gbar)[:, None])
     g *= np.asarray(c, dtype=np.float64)[:, None]
     if dzs is not None:
         g *= dzs
     return g.T @ hs
+
+
+def jsd_gbar(s_hidden, s_weight, t_hidden, t_weight, beta: float = 0.5,
+             transform: Optional[fo.LogitTransform] = None) -> np.ndarray:
+    """Per token sum_v p_s,v g_v, g = (1 - beta) log(p_s / M): the row sum the JSD
+    gradient subtracts (full vocabulary rows)."""
+    hs, ws = fo._as_f64(s_hidden), fo._as_f64(s_weight)
+    ht, wt = fo._as_f64(t_hidden), fo._as_f64(t_weight)
+    T, V = hs.shape[0], ws.shape[0]
+    out = np.empty(T)
+    step = fo._rows_per_block(V, T)
+    for r0 in range(0, T, step):
+        r1 = min(T, r0 + step)
+        zs, _ = _rows(hs, ws, transform, r0, r1)
+        zt, _ = _rows(ht, wt, transform, r0, r1)
+        log_ps, log_pt = _log_softmax(zs), _log_softmax(zt)
+        ps = np.exp(log_ps)
+        gv = (1.0 - beta) * (log_ps - np.log(beta * np.exp(log_pt) + (1.0 - beta) * ps))
+        out[r0:r1] = (ps * gv).sum(axis=1)
+    return out

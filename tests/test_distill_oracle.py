@@ -31,9 +31,15 @@ MUTANTS = {
                              "mean = float(kl.sum() / T)"),
     "masked_tokens_get_grad": ("    return np.where(valid, g, 0.0)", "    return g"),
     "no_chain_rule": ("return g if dzs is None else g * dzs", "return g"),
-    "weight_rows_no_teacher": ("g = np.exp(zs - np.asarray(lse_s)[:, None]) - np.exp(zt - np.asarray(lse_t)[:, None])",
-                               "g = np.exp(zs - np.asarray(lse_s)[:, None])"),
+    "weight_rows_no_teacher": ("g = np.exp(log_ps) - np.exp(log_pt)", "g = np.exp(log_ps)"),
     "lse_swapped": ("        log_pt = zt - lse_t[r0:r1, None]", "        log_pt = zt - lse_s[r0:r1, None]"),
+    "jsd_mixture_weights_swapped": ("    m = beta * pt + (1.0 - beta) * ps",
+                                    "    m = beta * ps + (1.0 - beta) * pt"),
+    "jsd_teacher_term_weight": ("    return (beta * _xlogy_ratio(pt, log_pt, log_m)",
+                                "    return ((1.0 - beta) * _xlogy_ratio(pt, log_pt, log_m)"),
+    "jsd_grad_without_row_sum": ("g = ps * (gv - gbar) * c[:, None]", "g = ps * gv * c[:, None]"),
+    "jsd_grad_weight": ("        gv = (1.0 - beta) * (log_ps - log_m)\n",
+                        "        gv = beta * (log_ps - log_m)\n"),
 }
 
 
