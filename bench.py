@@ -35,6 +35,10 @@ def parse():
     ap.add_argument("--workload", default="qwen3_8b_sft")
     ap.add_argument("--loss", choices=("grpo", "dpo", "kto"), default="grpo",
                     help="policy loss of a policy workload (grpo_qwen3)")
+    ap.add_argument("--divergence", choices=("kl", "jsd"), default="kl",
+                    help="divergence of a distillation workload")
+    ap.add_argument("--beta", type=float, default=0.5,
+                    help="JSD weight of the teacher in the mixture (--divergence jsd)")
     ap.add_argument("--chunk-rows", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
@@ -311,7 +315,8 @@ def distill_main(args) -> None:
 
     def step():
         flce.distill(sh, sw, th, tw, y, chunk_rows=chunk_rows, transform=xf, grad_mean=one,
-                     grad_hidden=dh, grad_weight=dw, workspace=ws, kl=kl, mean=mean)
+                     grad_hidden=dh, grad_weight=dw, workspace=ws, kl=kl, mean=mean,
+                     divergence=args.divergence, beta=args.beta)
 
     for _ in range(args.warmup):
         step()
@@ -323,7 +328,15 @@ def distill_main(args) -> None:
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    flops = 4.0 * T * V * Dt + 8.0 * T * V * Ds
+    if args.divergence == "kl":
+        flops = 4.0 * T * V * Dt + 8.0 * T * V * Ds
+        passes = "2 lse passes, teacher and student block passes, dH, dW"
+        loss = "mean KL(teacher || student)"
+    else:  # one more teacher + student pass: the gradient needs each row's full sum first
+        flops = 6.0 * T * V * Dt + 10.0 * T * V * Ds
+        passes = ("2 lse passes, teacher and student statistics passes, teacher and student "
+                  "gradient passes, dH, dW")
+        loss = f"mean generalized JSD (beta {args.beta})"
     achieved = flops / (ms / 1e3)
     line = {
         "metric": "distillation fwd+bwd tokens/s (student and teacher LM heads)",
@@ -333,11 +346,10 @@ def distill_main(args) -> None:
         "data": "synthetic",
         "config": {"workload": args.workload, "tokens": T, "student_hidden": Ds,
                    "teacher_hidden": Dt, "vocab": V, "chunk_rows": chunk_rows,
-                   "masked_tokens": w.ignore_count, "loss": "mean KL(teacher || student)"},
+                   "masked_tokens": w.ignore_count, "loss": loss},
         "workspace_bytes": int(ws.numel()),
         "roofline": {
-            "kernel": "whole flce_distill call (2 lse passes, teacher and student block passes, "
-                      "dH, dW)",
+            "kernel": f"whole distillation call ({passes})",
             "bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": PEAK_BF16 / 1e12,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4), "traffic": None,
             "algorithmic_flops_per_launch": flops,
@@ -347,7 +359,8 @@ def distill_main(args) -> None:
           file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = distill_cpu_baseline(x, min(args.cpu_sample_tokens, T),
-                                                    args.cpu_sample_vocab)
+                                                    args.cpu_sample_vocab, args.divergence,
+                                                    args.beta)
     print(json.dumps(line), flush=True)
 
 
@@ -484,7 +497,8 @@ def policy_cpu_baseline(x, loss: str, prm: dict, n_tokens: int) -> dict:
                       f"numpy log-probs + {loss.upper()} loss + backward in {dt:.1f} s"}
 
 
-def distill_cpu_baseline(x, n_tokens: int, n_vocab: int) -> dict:
+def distill_cpu_baseline(x, n_tokens: int, n_vocab: int, divergence: str = "kl",
+                         beta: float = 0.5) -> dict:
     """The distillation oracle, untouched, on the first n_tokens tokens against the first
     n_vocab vocabulary rows of both heads; the rate is scaled by n_vocab / V."""
     from oracle import distill_oracle
@@ -499,8 +513,8 @@ def distill_cpu_baseline(x, n_tokens: int, n_vocab: int) -> dict:
     args = (x.s_hidden[:n_tokens], x.s_weight[:n_vocab], x.t_hidden[:n_tokens],
             x.t_weight[:n_vocab], x.labels[:n_tokens])
     t0 = time.perf_counter()
-    distill_oracle.forward(*args)
-    distill_oracle.backward(*args, grad_mean=1.0)
+    distill_oracle.forward(*args, divergence=divergence, beta=beta)
+    distill_oracle.backward(*args, grad_mean=1.0, divergence=divergence, beta=beta)
     dt = time.perf_counter() - t0
     return {"value": round(n_tokens / dt * n_vocab / V, 3), "unit": "tokens/s",
             "cores": int(cores), "kind": "oracle",

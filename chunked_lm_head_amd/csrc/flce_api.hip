@@ -417,6 +417,226 @@ flce_status fill(float *dst, int64_t n, float v, hipStream_t s) {
   return launched("fill");
 }
 
+// Forward KL (jsd = false) or the generalized Jensen-Shannon divergence with
+// weight beta (jsd = true); the entry points below differ only in that.
+flce_status distill_run(bool jsd, float beta, const void *student_hidden,
+                        const void *student_weight, int64_t Ds, const void *teacher_hidden,
+                        const void *teacher_weight, int64_t Dt, const int64_t *labels,
+                        int64_t ignore_index, int64_t T, int64_t V, int64_t chunk_rows,
+                        const flce_logit_transform *transform, float *kl_out, float *mean_out,
+                        const float *grad_out, const float *grad_mean, void *grad_student_hidden,
+                        float *grad_student_weight, int accumulate_grad_weight, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+  g_last_error[0] = 0;
+  DistillPlan p;
+  FLCE_TRY(make_distill_plan(T, Ds, Dt, V, chunk_rows, p));
+  Xform xf;
+  bool cap;
+  FLCE_TRY(make_xform(transform, xf, cap));
+  if (jsd && !(beta > 0.f && beta < 1.f))
+    return fail(FLCE_ERR_ARG, "JSD weight beta = %g must lie in (0, 1)", (double)beta);
+  if (grad_out && grad_mean)
+    return fail(FLCE_ERR_ARG, "give at most one of grad_out and grad_mean");
+  const bool grads = grad_out || grad_mean;
+  if (grads && !grad_student_weight)
+    return fail(FLCE_ERR_ARG, "a gradient was requested but grad_student_weight is NULL");
+  if (grad_student_weight && !aligned(grad_student_weight, 16))
+    return fail(FLCE_ERR_ARG, "grad_student_weight not 16-byte aligned");
+  if (T > 0) {
+    if (!student_hidden || !student_weight || !teacher_hidden || !teacher_weight || !workspace ||
+        (grads && !grad_student_hidden))
+      return fail(FLCE_ERR_ARG, "a required pointer is NULL");
+    if (!aligned(student_hidden, 16) || !aligned(student_weight, 16) ||
+        !aligned(teacher_hidden, 16) || !aligned(teacher_weight, 16) ||
+        !aligned(workspace, 16) || (labels && !aligned(labels, 8)) ||
+        (kl_out && !aligned(kl_out, 4)) || (mean_out && !aligned(mean_out, 4)) ||
+        (grad_out && !aligned(grad_out, 4)) || (grad_mean && !aligned(grad_mean, 4)) ||
+        (grads && !aligned(grad_student_hidden, 16)))
+      return fail(FLCE_ERR_ARG, "misaligned pointer");
+    if (workspace_bytes < p.total)
+      return fail(FLCE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
+                  p.total);
+  }
+  FLCE_TRY(check_device());
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) {
+    if (mean_out) FLCE_TRY(fill(mean_out, 1, 0.f, s));
+    if (grads && !accumulate_grad_weight) FLCE_TRY(fill(grad_student_weight, V * Ds, 0.f, s));
+    return FLCE_OK;
+  }
+
+  char *ws = (char *)workspace;
+  float *lse_s = (float *)(ws + p.off_lse_s), *lse_t = (float *)(ws + p.off_lse_t);
+  float *l2s = (float *)(ws + p.off_l2s), *l2t = (float *)(ws + p.off_l2t);
+  float *cbuf = (float *)(ws + p.off_c);
+  float *Abuf = (float *)(ws + p.off_A), *Bbuf = (float *)(ws + p.off_B);
+  float *Pbuf = (float *)(ws + p.off_P);
+  uint16_t *G = (uint16_t *)Pbuf;  // the student's gradient replaces p_t in place
+  float *part_a = (float *)(ws + p.off_pa), *part_b = (float *)(ws + p.off_pb);
+  float *dhacc = (float *)(ws + p.off_dh);
+  uint16_t *ht = (uint16_t *)(ws + p.off_ht);
+
+  // Log-sum-exp of each head: the fused forward kernel without labels.
+  for (int head = 0; head < 2; ++head) {
+    FwdLseParams a;
+    a.hidden = (const uint16_t *)(head ? student_hidden : teacher_hidden);
+    a.weight = (const uint16_t *)(head ? student_weight : teacher_weight);
+    a.labels = nullptr;
+    a.ignore_index = ignore_index;
+    a.T = (int)T;
+    a.D = (int)(head ? Ds : Dt);
+    a.V = (int)V;
+    a.n_tt = (int)p.n_tt;
+    a.n_vt = (int)p.n_vt;
+    a.splits = (int)p.splits;
+    a.T_pad = (int)p.T_pad;
+    a.xf = xf;
+    a.part_m = (float *)(ws + p.off_pm);
+    a.part_s = (float *)(ws + p.off_ps);
+    a.zlab = (float *)(ws + p.off_zl);
+    if (cap)
+      fwd_lse_kernel<true><<<(unsigned)(p.n_tt * p.splits), kThreads, 0, s>>>(a);
+    else
+      fwd_lse_kernel<false><<<(unsigned)(p.n_tt * p.splits), kThreads, 0, s>>>(a);
+    FLCE_TRY(launched("fwd_lse"));
+    DstLseParams l;
+    l.part_m = a.part_m;
+    l.part_s = a.part_s;
+    l.T = (int)T;
+    l.splits = (int)p.splits;
+    l.T_pad = (int)p.T_pad;
+    l.n = (int)p.Tb;
+    l.lanes = (int)combine_lanes(p.splits);
+    l.lse = head ? lse_s : lse_t;
+    l.lse2 = head ? l2s : l2t;
+    dst_lse_kernel<<<(unsigned)cdiv(p.Tb, 256 / l.lanes), 256, 0, s>>>(l);
+    FLCE_TRY(launched("dst_lse"));
+  }
+
+  DstPrepParams pr;
+  pr.labels = labels;
+  pr.grad_out = grad_out;
+  pr.grad_mean = grad_mean;
+  pr.ignore_index = ignore_index;
+  pr.T = grads ? (int)T : 0;  // no gradient: c = 0 everywhere
+  pr.n = (int)p.Tb;
+  pr.c = cbuf;
+  dst_prep_kernel<<<1, 1024, 0, s>>>(pr);
+  FLCE_TRY(launched("dst_prep"));
+
+  // One block pass of dst_tile_kernel in the given role over the chunk at vc0.
+  auto tile_pass = [&](int role, int64_t rb0, int64_t tiles_n, int64_t vc, float *part,
+                       float *part2) -> flce_status {
+    const int64_t vc0 = vc * p.Vc;
+    const int64_t vcount = std::min<int64_t>(p.Vc, V - vc0);
+    const bool teacher = role == kRoleTeacher;
+    DstTileParams d;
+    d.hidden = (const uint16_t *)(teacher ? teacher_hidden : student_hidden);
+    d.weight = (const uint16_t *)(teacher ? teacher_weight : student_weight);
+    d.lse2 = teacher ? l2t : l2s;
+    d.c = cbuf;
+    d.gbar2 = Bbuf;
+    d.beta = beta;
+    d.T = (int)T;
+    d.D = (int)(teacher ? Dt : Ds);
+    d.V = (int)V;
+    d.rb0 = (int)rb0;
+    d.vc0 = (int)vc0;
+    d.n_vt = (int)cdiv(vcount, kTile);
+    d.tiles_n = (int)tiles_n;
+    d.vsplits = (int)p.vsplits;
+    d.R = (int)p.R;
+    d.xf = xf;
+    d.P = Pbuf;
+    d.Pp = (int)p.Vc;
+    d.G = G;  // over P, grouped
+    d.Gp = (int)(2 * p.Vc);
+    d.part = part;
+    d.part2 = part2;
+    const unsigned grid = (unsigned)(tiles_n * p.vsplits);
+#define FLCE_TILE(R)                                                              \
+  (cap ? dst_tile_kernel<R, true><<<grid, kThreads, 0, s>>>(d)                   \
+       : dst_tile_kernel<R, false><<<grid, kThreads, 0, s>>>(d))
+    switch (role) {
+      case kRoleTeacher: FLCE_TILE(kRoleTeacher); break;
+      case kRoleStudentKL: FLCE_TILE(kRoleStudentKL); break;
+      case kRoleJsdStats: FLCE_TILE(kRoleJsdStats); break;
+      default: FLCE_TILE(kRoleJsdGrad); break;
+    }
+#undef FLCE_TILE
+    return launched(teacher ? "dst_tile teacher" : "dst_tile student");
+  };
+  auto dh_dw = [&](int64_t rb, int64_t rcount, int64_t vc) -> flce_status {
+    const int64_t vc0 = vc * p.Vc;
+    const int64_t vcount = std::min<int64_t>(p.Vc, V - vc0);
+    return launch_dh_dw(G, (int)(2 * p.Vc), p.Vc, true, student_weight, ht, Ds, V, p.R, rcount,
+                        vc0, vcount, p.dh_splits, dhacc, grad_student_weight, vc > 0,
+                        accumulate_grad_weight || rb > 0, s);
+  };
+  const int nparts = (int)(p.n_vc * p.vsplits);
+  auto reduce = [&](int64_t rb0, int64_t rcount) -> flce_status {
+    for (int k = 0; k < 2; ++k) {
+      dst_reduce_kernel<<<(unsigned)cdiv(rcount, 64), 256, 0, s>>>(
+          k ? part_b : part_a, nparts, (int)p.R, (int)rb0, (int)rcount, k ? Bbuf : Abuf);
+      FLCE_TRY(launched("dst_reduce"));
+    }
+    return FLCE_OK;
+  };
+
+  for (int64_t rb = 0; rb < p.n_rb; ++rb) {
+    const int64_t rb0 = rb * p.R;
+    const int64_t rcount = std::min<int64_t>(p.R, T - rb0);
+    if (rcount <= 0) break;
+    const int64_t tiles_n = cdiv(rcount, kTile);
+    if (grads) FLCE_TRY(launch_ht(student_hidden, ht, Ds, p.R, rb0, rcount, s));
+    for (int64_t vc = 0; vc < p.n_vc; ++vc) {
+      float *pa = part_a + (size_t)vc * p.vsplits * p.R;
+      float *pb = part_b + (size_t)vc * p.vsplits * p.R;
+      // teacher: p_t block (and, for KL, partial sums of A)
+      FLCE_TRY(tile_pass(kRoleTeacher, rb0, tiles_n, vc, pa, nullptr));
+      if (!jsd) {
+        // student: partial sums of B and the gradient block
+        FLCE_TRY(tile_pass(kRoleStudentKL, rb0, tiles_n, vc, pb, nullptr));
+        if (grads) FLCE_TRY(dh_dw(rb, rcount, vc));
+      } else {
+        // student: partial sums of the divergence (A) and of gbar (B)
+        FLCE_TRY(tile_pass(kRoleJsdStats, rb0, tiles_n, vc, pa, pb));
+      }
+    }
+    FLCE_TRY(reduce(rb0, rcount));
+    if (jsd && grads) {
+      // the gradient needs each token's complete gbar: a second pass over the chunks
+      for (int64_t vc = 0; vc < p.n_vc; ++vc) {
+        FLCE_TRY(tile_pass(kRoleTeacher, rb0, tiles_n, vc, part_a, nullptr));
+        FLCE_TRY(tile_pass(kRoleJsdGrad, rb0, tiles_n, vc, nullptr, nullptr));
+        FLCE_TRY(dh_dw(rb, rcount, vc));
+      }
+    }
+    if (grads)
+      FLCE_TRY(launch_dh_out(dhacc, grad_student_hidden, Ds, p.R, p.dh_splits, rb0, rcount, s));
+  }
+
+  DstCombineParams c;
+  c.jsd = jsd ? 1 : 0;
+  c.A = Abuf;
+  c.B = Bbuf;
+  c.lse_s = lse_s;
+  c.lse_t = lse_t;
+  c.labels = labels;
+  c.ignore_index = ignore_index;
+  c.T = (int)T;
+  c.kl = kl_out;
+  c.blk_sum = (double *)(ws + p.off_bs);
+  c.blk_cnt = (int *)(ws + p.off_bc);
+  dst_combine_kernel<<<(unsigned)p.n_cblk, 256, 0, s>>>(c);
+  FLCE_TRY(launched("dst_combine"));
+  if (mean_out) {
+    fwd_mean_kernel<<<1, 256, 0, s>>>(c.blk_sum, c.blk_cnt, (int)p.n_cblk, mean_out);
+    FLCE_TRY(launched("fwd_mean"));
+  }
+  return FLCE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -688,182 +908,26 @@ flce_status flce_distill(const void *student_hidden, const void *student_weight,
                          const float *grad_mean, void *grad_student_hidden,
                          float *grad_student_weight, int accumulate_grad_weight,
                          void *workspace, size_t workspace_bytes, void *stream) {
-  g_last_error[0] = 0;
-  DistillPlan p;
-  FLCE_TRY(make_distill_plan(T, Ds, Dt, V, chunk_rows, p));
-  Xform xf;
-  bool cap;
-  FLCE_TRY(make_xform(transform, xf, cap));
-  if (grad_out && grad_mean)
-    return fail(FLCE_ERR_ARG, "give at most one of grad_out and grad_mean");
-  const bool grads = grad_out || grad_mean;
-  if (grads && !grad_student_weight)
-    return fail(FLCE_ERR_ARG, "a gradient was requested but grad_student_weight is NULL");
-  if (grad_student_weight && !aligned(grad_student_weight, 16))
-    return fail(FLCE_ERR_ARG, "grad_student_weight not 16-byte aligned");
-  if (T > 0) {
-    if (!student_hidden || !student_weight || !teacher_hidden || !teacher_weight || !workspace ||
-        (grads && !grad_student_hidden))
-      return fail(FLCE_ERR_ARG, "a required pointer is NULL");
-    if (!aligned(student_hidden, 16) || !aligned(student_weight, 16) ||
-        !aligned(teacher_hidden, 16) || !aligned(teacher_weight, 16) ||
-        !aligned(workspace, 16) || (labels && !aligned(labels, 8)) ||
-        (kl_out && !aligned(kl_out, 4)) || (mean_out && !aligned(mean_out, 4)) ||
-        (grad_out && !aligned(grad_out, 4)) || (grad_mean && !aligned(grad_mean, 4)) ||
-        (grads && !aligned(grad_student_hidden, 16)))
-      return fail(FLCE_ERR_ARG, "misaligned pointer");
-    if (workspace_bytes < p.total)
-      return fail(FLCE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
-                  p.total);
-  }
-  FLCE_TRY(check_device());
-  hipStream_t s = (hipStream_t)stream;
-  if (T == 0) {
-    if (mean_out) FLCE_TRY(fill(mean_out, 1, 0.f, s));
-    if (grads && !accumulate_grad_weight) FLCE_TRY(fill(grad_student_weight, V * Ds, 0.f, s));
-    return FLCE_OK;
-  }
+  return distill_run(false, 0.f, student_hidden, student_weight, Ds, teacher_hidden,
+                     teacher_weight, Dt, labels, ignore_index, T, V, chunk_rows, transform,
+                     kl_out, mean_out, grad_out, grad_mean, grad_student_hidden,
+                     grad_student_weight, accumulate_grad_weight, workspace, workspace_bytes,
+                     stream);
+}
 
-  char *ws = (char *)workspace;
-  float *lse_s = (float *)(ws + p.off_lse_s), *lse_t = (float *)(ws + p.off_lse_t);
-  float *l2s = (float *)(ws + p.off_l2s), *l2t = (float *)(ws + p.off_l2t);
-  float *cbuf = (float *)(ws + p.off_c);
-  float *Abuf = (float *)(ws + p.off_A), *Bbuf = (float *)(ws + p.off_B);
-  float *Pbuf = (float *)(ws + p.off_P);
-  uint16_t *G = (uint16_t *)Pbuf;  // the student's gradient replaces p_t in place
-  float *part_a = (float *)(ws + p.off_pa), *part_b = (float *)(ws + p.off_pb);
-  float *dhacc = (float *)(ws + p.off_dh);
-  uint16_t *ht = (uint16_t *)(ws + p.off_ht);
-
-  // Log-sum-exp of each head: the fused forward kernel without labels.
-  for (int head = 0; head < 2; ++head) {
-    FwdLseParams a;
-    a.hidden = (const uint16_t *)(head ? student_hidden : teacher_hidden);
-    a.weight = (const uint16_t *)(head ? student_weight : teacher_weight);
-    a.labels = nullptr;
-    a.ignore_index = ignore_index;
-    a.T = (int)T;
-    a.D = (int)(head ? Ds : Dt);
-    a.V = (int)V;
-    a.n_tt = (int)p.n_tt;
-    a.n_vt = (int)p.n_vt;
-    a.splits = (int)p.splits;
-    a.T_pad = (int)p.T_pad;
-    a.xf = xf;
-    a.part_m = (float *)(ws + p.off_pm);
-    a.part_s = (float *)(ws + p.off_ps);
-    a.zlab = (float *)(ws + p.off_zl);
-    if (cap)
-      fwd_lse_kernel<true><<<(unsigned)(p.n_tt * p.splits), kThreads, 0, s>>>(a);
-    else
-      fwd_lse_kernel<false><<<(unsigned)(p.n_tt * p.splits), kThreads, 0, s>>>(a);
-    FLCE_TRY(launched("fwd_lse"));
-    DstLseParams l;
-    l.part_m = a.part_m;
-    l.part_s = a.part_s;
-    l.T = (int)T;
-    l.splits = (int)p.splits;
-    l.T_pad = (int)p.T_pad;
-    l.n = (int)p.Tb;
-    l.lanes = (int)combine_lanes(p.splits);
-    l.lse = head ? lse_s : lse_t;
-    l.lse2 = head ? l2s : l2t;
-    dst_lse_kernel<<<(unsigned)cdiv(p.Tb, 256 / l.lanes), 256, 0, s>>>(l);
-    FLCE_TRY(launched("dst_lse"));
-  }
-
-  DstPrepParams pr;
-  pr.labels = labels;
-  pr.grad_out = grad_out;
-  pr.grad_mean = grad_mean;
-  pr.ignore_index = ignore_index;
-  pr.T = grads ? (int)T : 0;  // no gradient: c = 0 everywhere
-  pr.n = (int)p.Tb;
-  pr.c = cbuf;
-  dst_prep_kernel<<<1, 1024, 0, s>>>(pr);
-  FLCE_TRY(launched("dst_prep"));
-
-  for (int64_t rb = 0; rb < p.n_rb; ++rb) {
-    const int64_t rb0 = rb * p.R;
-    const int64_t rcount = std::min<int64_t>(p.R, T - rb0);
-    if (rcount <= 0) break;
-    const int64_t tiles_n = cdiv(rcount, kTile);
-    if (grads) FLCE_TRY(launch_ht(student_hidden, ht, Ds, p.R, rb0, rcount, s));
-    for (int64_t vc = 0; vc < p.n_vc; ++vc) {
-      const int64_t vc0 = vc * p.Vc;
-      const int64_t vcount = std::min<int64_t>(p.Vc, V - vc0);
-      DstTileParams d;
-      d.lse2 = l2t;
-      d.c = cbuf;
-      d.T = (int)T;
-      d.V = (int)V;
-      d.rb0 = (int)rb0;
-      d.vc0 = (int)vc0;
-      d.n_vt = (int)cdiv(vcount, kTile);
-      d.tiles_n = (int)tiles_n;
-      d.vsplits = (int)p.vsplits;
-      d.R = (int)p.R;
-      d.xf = xf;
-      d.P = Pbuf;
-      d.Pp = (int)p.Vc;
-      d.G = G;  // over P, grouped
-      d.Gp = (int)(2 * p.Vc);
-      const unsigned grid = (unsigned)(tiles_n * p.vsplits);
-      // teacher: p_t block and partial sums of A
-      d.hidden = (const uint16_t *)teacher_hidden;
-      d.weight = (const uint16_t *)teacher_weight;
-      d.D = (int)Dt;
-      d.part = part_a + (size_t)vc * p.vsplits * p.R;
-      if (cap)
-        dst_tile_kernel<true, true><<<grid, kThreads, 0, s>>>(d);
-      else
-        dst_tile_kernel<true, false><<<grid, kThreads, 0, s>>>(d);
-      FLCE_TRY(launched("dst_tile teacher"));
-      // student: partial sums of B and the gradient block
-      d.hidden = (const uint16_t *)student_hidden;
-      d.weight = (const uint16_t *)student_weight;
-      d.D = (int)Ds;
-      d.lse2 = l2s;
-      d.part = part_b + (size_t)vc * p.vsplits * p.R;
-      if (cap)
-        dst_tile_kernel<false, true><<<grid, kThreads, 0, s>>>(d);
-      else
-        dst_tile_kernel<false, false><<<grid, kThreads, 0, s>>>(d);
-      FLCE_TRY(launched("dst_tile student"));
-      if (grads)
-        FLCE_TRY(launch_dh_dw(G, (int)(2 * p.Vc), p.Vc, true, student_weight, ht, Ds, V, p.R,
-                              rcount, vc0, vcount, p.dh_splits, dhacc, grad_student_weight,
-                              vc > 0, accumulate_grad_weight || rb > 0, s));
-    }
-    const int nparts = (int)(p.n_vc * p.vsplits);
-    dst_reduce_kernel<<<(unsigned)cdiv(rcount, 64), 256, 0, s>>>(part_a, nparts, (int)p.R,
-                                                                 (int)rb0, (int)rcount, Abuf);
-    FLCE_TRY(launched("dst_reduce"));
-    dst_reduce_kernel<<<(unsigned)cdiv(rcount, 64), 256, 0, s>>>(part_b, nparts, (int)p.R,
-                                                                 (int)rb0, (int)rcount, Bbuf);
-    FLCE_TRY(launched("dst_reduce"));
-    if (grads)
-      FLCE_TRY(launch_dh_out(dhacc, grad_student_hidden, Ds, p.R, p.dh_splits, rb0, rcount, s));
-  }
-
-  DstCombineParams c;
-  c.A = Abuf;
-  c.B = Bbuf;
-  c.lse_s = lse_s;
-  c.lse_t = lse_t;
-  c.labels = labels;
-  c.ignore_index = ignore_index;
-  c.T = (int)T;
-  c.kl = kl_out;
-  c.blk_sum = (double *)(ws + p.off_bs);
-  c.blk_cnt = (int *)(ws + p.off_bc);
-  dst_combine_kernel<<<(unsigned)p.n_cblk, 256, 0, s>>>(c);
-  FLCE_TRY(launched("dst_combine"));
-  if (mean_out) {
-    fwd_mean_kernel<<<1, 256, 0, s>>>(c.blk_sum, c.blk_cnt, (int)p.n_cblk, mean_out);
-    FLCE_TRY(launched("fwd_mean"));
-  }
-  return FLCE_OK;
+flce_status flce_distill_jsd(const void *student_hidden, const void *student_weight, int64_t Ds,
+                             const void *teacher_hidden, const void *teacher_weight, int64_t Dt,
+                             const int64_t *labels, int64_t ignore_index, int64_t T, int64_t V,
+                             int64_t chunk_rows, const flce_logit_transform *transform,
+                             float beta, float *jsd_out, float *mean_out, const float *grad_out,
+                             const float *grad_mean, void *grad_student_hidden,
+                             float *grad_student_weight, int accumulate_grad_weight,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  return distill_run(true, beta, student_hidden, student_weight, Ds, teacher_hidden,
+                     teacher_weight, Dt, labels, ignore_index, T, V, chunk_rows, transform,
+                     jsd_out, mean_out, grad_out, grad_mean, grad_student_hidden,
+                     grad_student_weight, accumulate_grad_weight, workspace, workspace_bytes,
+                     stream);
 }
 
 }  // extern "C"

@@ -12,6 +12,15 @@
 // and dKL/dz_s' = p_s - p_t, so the student's backward is the cross-entropy
 // backward with the one-hot target replaced by p_t.
 //
+// The generalized Jensen-Shannon divergence (the same article names a fused
+// linear JSD loss), with weight beta and M = beta p_t + (1 - beta) p_s:
+//     JSD = beta KL(p_t || M) + (1 - beta) KL(p_s || M),
+//     dJSD/dz_s' = p_s (g - gbar),  g = (1 - beta) log(p_s / M),  gbar = sum_v p_s g,
+// needs the row sum gbar before any gradient value exists, so its schedule
+// has one more block pass: per row block, teacher + student passes over every
+// vocabulary chunk form the divergence and gbar (as partial sums), then
+// teacher + student passes write G for the dH and dW kernels.
+//
 // Schedule (one call): the two log-sum-exps come from the fused forward
 // kernel without labels; then, per block of rows and vocabulary chunk, the
 // teacher kernel recomputes its logits and writes p_t in fp32 (with partial
@@ -98,10 +107,20 @@ __global__ void __launch_bounds__(1024) dst_prep_kernel(DstPrepParams p) {
   }
 }
 
+// What a block pass of dst_tile_kernel computes.
+enum DstRole {
+  kRoleTeacher = 0,   // p_t -> P, partial sums of p_t z_t'
+  kRoleStudentKL = 1, // partial sums of p_t z_s', G = c (p_s - p_t) dz'/dz over P
+  kRoleJsdStats = 2,  // partial sums of the JSD terms and of p_s g (gbar)
+  kRoleJsdGrad = 3,   // G = c p_s (g - gbar) dz'/dz over P
+};
+
 struct DstTileParams {
   const uint16_t *hidden, *weight;  // this head's [T, D] and [V, D], bf16
   const float *lse2;                // [Tb] this head's lse * log2(e), +inf past T
   const float *c;                   // [Tb] student: upstream scale (0: no gradient)
+  const float *gbar2;               // [Tb] JSD gradient pass: gbar / ln 2 per token
+  float beta;                       // JSD weight of the teacher in M
   int T, D, V;
   int rb0, vc0;                     // first token / vocabulary row of this block
   int n_vt;                         // vocabulary tiles of the chunk that hold rows < V
@@ -113,14 +132,22 @@ struct DstTileParams {
   uint16_t *G;                      // student gradient, bf16 (zeros when c = 0), written over
   int Gp;                           // P: the same bytes, Gp = 2 Pp, grouped columns
   float *part;                      // [vsplits, R] this launch's per-token partial sums
+  float *part2;                     // JSD statistics pass: partial sums of p_s g / ln 2
 };
 
 // One head's logit tiles of a block, walking vocabulary tiles per token tile
 // as the recompute kernel of the cross-entropy backward does.
-//   teacher (kTeacher): P = p_t = 2^(z_t' log2 e - lse2_t) -> fp32 block,
-//                       partial sums of p_t z_t' (A);
-//   student:            reads p_t, partial sums of p_t z_s' (B), and
-//                       G = c (p_s - p_t) dz_s'/dz_s -> bf16, over p_t.
+//   teacher:           P = p_t = 2^(z_t' log2 e - lse2_t) -> fp32 block,
+//                      partial sums of p_t z_t' (A);
+//   student, KL:       reads p_t, partial sums of p_t z_s' (B), and
+//                      G = c (p_s - p_t) dz_s'/dz_s -> bf16, over p_t;
+//   student, JSD:      reads p_t; in log2 units (l = log2 of a probability),
+//                      g2 = (1 - beta) (l_s - l_M); statistics pass: partial
+//                      sums of beta p_t (l_t - l_M) + p_s g2 (the divergence /
+//                      ln 2) and of p_s g2 (gbar / ln 2); gradient pass:
+//                      G = c ln2 p_s (g2 - gbar2) dz_s'/dz_s over p_t.
+//                      Probabilities below FLT_MIN count as 0 (their terms
+//                      vanish; the hardware logarithm flushes denormals).
 // A student wave reads the p_t values of one token row (its 128 columns) and
 // then writes that row's G into the first half of the same bytes: each G store
 // overlaps only p_t values of the same or earlier blocks of the row, which the
@@ -128,9 +155,13 @@ struct DstTileParams {
 // Rows past the vocabulary have z = -inf: p = 0 there and the products are
 // taken as 0.  Every workgroup writes its partial-sum slot (zeros when its
 // vocabulary range is empty), so the reduction reads no stale values.
-template <bool kTeacher, bool kCap>
+template <int kRole, bool kCap>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(1, 1))) dst_tile_kernel(DstTileParams p) {
+  constexpr bool kTeacher = kRole == kRoleTeacher;
+  constexpr bool kJsd = kRole == kRoleJsdStats || kRole == kRoleJsdGrad;
+  constexpr bool kWritesG = kRole == kRoleStudentKL || kRole == kRoleJsdGrad;
+  constexpr bool kSums = kRole != kRoleJsdGrad;  // writes per-token partial sums
   __shared__ __attribute__((aligned(16))) char smem_raw[kPipeBytes];
   lds_t *smem = (lds_t *)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -142,18 +173,21 @@ __global__ void __launch_bounds__(kThreads)
   const int vt1 = (int)((int64_t)(sp + 1) * p.n_vt / p.vsplits);
   const int t0 = p.rb0 + tn * kTile;
 
-  float psum[8];
+  float psum[8], psum2[8];
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) psum[nb] = 0.f;
+  for (int nb = 0; nb < 8; ++nb) psum[nb] = psum2[nb] = 0.f;
 
   if (t0 < p.T && vt0 < vt1) {
-    float l2[8], cc[8];
+    float l2[8], cc[8], gb[8];
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
       const int t = t0 + wn * 128 + nb * 16 + (lane & 15);  // < rb0 + R <= Tb
       l2[nb] = p.lse2[t];
-      cc[nb] = kTeacher ? 0.f : p.c[t];
+      cc[nb] = kWritesG ? p.c[t] : 0.f;
+      gb[nb] = kRole == kRoleJsdGrad ? p.gbar2[t] : 0.f;
     }
+    const float beta = p.beta, nbeta = 1.f - p.beta;
+    constexpr float kFltMin = 1.17549435e-38f;
     const float ks = p.xf.zscale * kLog2e;           // uncapped: z' log2 e = z ks
     const float dscale = p.xf.zscale * p.xf.inv_temp;  // capped: dz'/dz = dscale (1 - t^2)
 
@@ -203,17 +237,33 @@ __global__ void __launch_bounds__(kThreads)
               zp[e] = z * p.xf.zscale;
               d[e] = p.xf.zscale;
             }
-            pr[e] = fast_exp2(__builtin_fmaf(zp[e], kLog2e, -l2[nb]));
-            // p z' with p = 0 (and z' = -inf) past the vocabulary taken as 0
-            const float w = kTeacher ? pr[e] : pt[mb][e];
-            psum[nb] += z == -kInf ? 0.f : w * zp[e];
+            const float lq2 = __builtin_fmaf(zp[e], kLog2e, -l2[nb]);
+            pr[e] = fast_exp2(lq2);
+            if constexpr (!kJsd) {
+              // p z' with p = 0 (and z' = -inf) past the vocabulary taken as 0
+              const float w = kTeacher ? pr[e] : pt[mb][e];
+              psum[nb] += z == -kInf ? 0.f : w * zp[e];
+            } else {
+              const float pv = pt[mb][e];
+              const bool qn = pr[e] > kFltMin, pn = pv > kFltMin;
+              const float lm2 = fast_log2(beta * pv + nbeta * pr[e]);  // finite if qn or pn
+              const float g2 = nbeta * (lq2 - lm2);
+              if constexpr (kRole == kRoleJsdStats) {
+                const float qg = qn ? pr[e] * g2 : 0.f;
+                psum[nb] += (pn ? beta * pv * (fast_log2(pv) - lm2) : 0.f) + qg;
+                psum2[nb] += qg;
+              } else {
+                pr[e] = qn ? pr[e] * (g2 - gb[nb]) : 0.f;  // p_s (g2 - gbar2)
+              }
+            }
           }
           if constexpr (kTeacher) {
             *(f32x4 *)(prow + acc_row(mb, 0, lane)) = f32x4{pr[0], pr[1], pr[2], pr[3]};
-          } else {
+          } else if constexpr (kWritesG) {
             float g[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) g[e] = cc[nb] * (pr[e] - pt[mb][e]) * d[e];
+            for (int e = 0; e < 4; ++e)
+              g[e] = kJsd ? cc[nb] * kLn2 * pr[e] * d[e] : cc[nb] * (pr[e] - pt[mb][e]) * d[e];
             u32x2 w;
             w[0] = pack_bf16(g[0], g[1]);
             w[1] = pack_bf16(g[2], g[3]);
@@ -224,21 +274,30 @@ __global__ void __launch_bounds__(kThreads)
     }
   }
 
-  // Sum the four lanes holding one token (l, l ^ 16, l ^ 32, l ^ 48), then the
-  // two waves (wm), in the (idle) ring; one value per token of the tile.
-  float *xch = (float *)smem_raw;  // [wn][nb][16]
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    psum[nb] += __shfl_xor(psum[nb], 16);
-    psum[nb] += __shfl_xor(psum[nb], 32);
-    if (wm == 1 && lane < 16) xch[(wn * 8 + nb) * 16 + lane] = psum[nb];
-  }
-  __syncthreads();
-  if (wm == 0 && lane < 16) {
+  if constexpr (kSums) {
+    // Sum the four lanes holding one token (l, l ^ 16, l ^ 32, l ^ 48), then the
+    // two waves (wm), in the (idle) ring; one value per token of the tile.
+    float *xch = (float *)smem_raw;  // [2 sums][wn][nb][16]
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-      const int tl = tn * kTile + wn * 128 + nb * 16 + lane;
-      p.part[(size_t)sp * p.R + tl] = psum[nb] + xch[(wn * 8 + nb) * 16 + lane];
+      psum[nb] += __shfl_xor(psum[nb], 16);
+      psum[nb] += __shfl_xor(psum[nb], 32);
+      if (wm == 1 && lane < 16) xch[(wn * 8 + nb) * 16 + lane] = psum[nb];
+      if constexpr (kRole == kRoleJsdStats) {
+        psum2[nb] += __shfl_xor(psum2[nb], 16);
+        psum2[nb] += __shfl_xor(psum2[nb], 32);
+        if (wm == 1 && lane < 16) xch[256 + (wn * 8 + nb) * 16 + lane] = psum2[nb];
+      }
+    }
+    __syncthreads();
+    if (wm == 0 && lane < 16) {
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const int tl = tn * kTile + wn * 128 + nb * 16 + lane;
+        p.part[(size_t)sp * p.R + tl] = psum[nb] + xch[(wn * 8 + nb) * 16 + lane];
+        if constexpr (kRole == kRoleJsdStats)
+          p.part2[(size_t)sp * p.R + tl] = psum2[nb] + xch[256 + (wn * 8 + nb) * 16 + lane];
+      }
     }
   }
 }
@@ -282,10 +341,11 @@ __global__ void __launch_bounds__(256)
   if (g == 0 && t < rcount) out[rb0 + t] = ((ssum[0][lane] + ssum[1][lane]) + ssum[2][lane]) + ssum[3][lane];
 }
 
-// kl_t = A - lse_t - B + lse_s for kept tokens, 0 for masked ones; block sums
-// for the mean (fwd_mean_kernel finishes it).
+// kl_t = A - lse_t - B + lse_s (JSD: ln 2 * A) for kept tokens, 0 for masked
+// ones; block sums for the mean (fwd_mean_kernel finishes it).
 struct DstCombineParams {
   const float *A, *B, *lse_s, *lse_t;
+  int jsd;                // 1: kl_t = ln 2 * A_t (A holds the JSD sum / ln 2)
   const int64_t *labels;  // mask, or null
   int64_t ignore_index;
   int T;
@@ -303,7 +363,7 @@ __global__ void __launch_bounds__(256) dst_combine_kernel(DstCombineParams p) {
   if (t < p.T) {
     float k = 0.f;
     if (!p.labels || p.labels[t] != p.ignore_index) {
-      k = (p.A[t] - p.lse_t[t]) - (p.B[t] - p.lse_s[t]);
+      k = p.jsd ? kLn2 * p.A[t] : (p.A[t] - p.lse_t[t]) - (p.B[t] - p.lse_s[t]);
       contrib = (double)k;
       cnt = 1;
     }

@@ -31,7 +31,7 @@ STATUS = {0: "FLCE_OK", 1: "FLCE_ERR_ARG", 2: "FLCE_ERR_SHAPE", 3: "FLCE_ERR_WOR
 EXPORTS = ("flce_workspace_bytes", "flce_forward", "flce_backward", "flce_describe_plan",
            "flce_status_string", "flce_last_error", "flce_distill_workspace_bytes",
            "flce_distill", "flce_chunk_rows_for", "flce_tune", "flce_policy_workspace_bytes",
-           "flce_grpo_loss", "flce_dpo_loss", "flce_kto_loss")
+           "flce_grpo_loss", "flce_dpo_loss", "flce_kto_loss", "flce_distill_jsd")
 
 
 class LogitTransform(ctypes.Structure):
@@ -66,6 +66,10 @@ def _load() -> ctypes.CDLL:
     lib.flce_distill.argtypes = [vp, vp, i64, vp, vp, i64, vp, i64, i64, i64, i64, xp,
                                  f32p, f32p, f32p, f32p, vp, f32p, ctypes.c_int, vp, sz, vp]
     lib.flce_distill.restype = ctypes.c_int
+    lib.flce_distill_jsd.argtypes = [vp, vp, i64, vp, vp, i64, vp, i64, i64, i64, i64, xp,
+                                     ctypes.c_float, f32p, f32p, f32p, f32p, vp, f32p,
+                                     ctypes.c_int, vp, sz, vp]
+    lib.flce_distill_jsd.restype = ctypes.c_int
     lib.flce_chunk_rows_for.argtypes = [i64, i64]
     lib.flce_chunk_rows_for.restype = i64
     lib.flce_tune.argtypes = [i64, i64, i64, i64, sz, ctypes.POINTER(ctypes.c_int64),
@@ -402,10 +406,13 @@ def distill(student_hidden, student_weight, teacher_hidden, teacher_weight,
             grad_hidden: Optional[torch.Tensor] = None,
             grad_weight: Optional[torch.Tensor] = None, accumulate: bool = False,
             workspace: Optional[torch.Tensor] = None, kl: Optional[torch.Tensor] = None,
-            mean: Optional[torch.Tensor] = None):
-    """(kl [T], mean [], dHs or None, dWs or None): per-token KL(teacher || student),
-    its mean over kept tokens and, when grad_out or grad_mean is given, the
-    student's gradients (one call; the teacher gets none)."""
+            mean: Optional[torch.Tensor] = None, divergence: str = "kl", beta: float = 0.5):
+    """(kl [T], mean [], dHs or None, dWs or None): per-token KL(teacher || student)
+    (``divergence="jsd"``: the generalized JSD with weight ``beta``), its mean over
+    kept tokens and, when grad_out or grad_mean is given, the student's gradients
+    (one call; the teacher gets none)."""
+    if divergence not in ("kl", "jsd"):
+        raise ValueError(f"divergence {divergence!r} is neither 'kl' nor 'jsd'")
     for t in (student_hidden, student_weight, teacher_hidden, teacher_weight):
         if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_cuda or not t.is_contiguous():
             raise ValueError("hidden states and lm_heads must be contiguous 2-D bf16 on the GPU")
@@ -443,13 +450,16 @@ def distill(student_hidden, student_weight, teacher_hidden, teacher_weight,
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _check_workspace(workspace, need, dev)
-    _check(lib.flce_distill(_ptr(student_hidden), _ptr(student_weight), Ds, _ptr(teacher_hidden),
-                            _ptr(teacher_weight), Dt, _ptr(labels), ignore_index, T, V,
-                            chunk_rows, make_transform(**(transform or {})), _ptr(kl),
-                            _ptr(mean), _ptr(grad_out), _ptr(grad_mean),
-                            _ptr(grad_hidden) if grads else None,
-                            _ptr(grad_weight) if grads else None, 1 if accumulate else 0,
-                            _ptr(workspace), workspace.numel(), _stream(dev)))
+    head = (_ptr(student_hidden), _ptr(student_weight), Ds, _ptr(teacher_hidden),
+            _ptr(teacher_weight), Dt, _ptr(labels), ignore_index, T, V, chunk_rows,
+            make_transform(**(transform or {})))
+    tail = (_ptr(kl), _ptr(mean), _ptr(grad_out), _ptr(grad_mean),
+            _ptr(grad_hidden) if grads else None, _ptr(grad_weight) if grads else None,
+            1 if accumulate else 0, _ptr(workspace), workspace.numel(), _stream(dev))
+    if divergence == "kl":
+        _check(lib.flce_distill(*head, *tail))
+    else:
+        _check(lib.flce_distill_jsd(*head, float(beta), *tail))
     return kl, mean, (grad_hidden if grads else None), (grad_weight if grads else None)
 
 

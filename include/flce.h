@@ -188,6 +188,30 @@ flce_status flce_distill(const void *student_hidden, const void *student_weight,
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The same call with the generalized Jensen-Shannon divergence in place of the
+ * KL (the TRL v1.13 article names a fused linear JSD loss among the losses
+ * built on the chunked LM head, without defining it; this is the textbook
+ * skewed form): with weight beta in (0, 1) and M = beta p_t + (1 - beta) p_s,
+ *     jsd_t = beta KL(p_t || M) + (1 - beta) KL(p_s || M)
+ * (beta = 1/2: the symmetric JSD, at most ln 2), and the student's gradient
+ *     G_tv = c_t p_s,tv (g_tv - sum_u p_s,tu g_tu) dz'_tv/dz_tv,
+ *     g = (1 - beta) log(p_s / M).
+ * jsd_out [T] replaces kl_out; every other argument, the workspace size
+ * (flce_distill_workspace_bytes) and the error conventions are those of
+ * flce_distill.  beta outside (0, 1) gives FLCE_ERR_ARG.  The gradient needs
+ * each token's full-vocabulary sum before any G value exists, so with a
+ * gradient the call recomputes both heads' logits once more than the KL does.
+ */
+flce_status flce_distill_jsd(const void *student_hidden, const void *student_weight, int64_t Ds,
+                             const void *teacher_hidden, const void *teacher_weight, int64_t Dt,
+                             const int64_t *labels, int64_t ignore_index, int64_t T, int64_t V,
+                             int64_t chunk_rows, const flce_logit_transform *transform,
+                             float beta, float *jsd_out, float *mean_out, const float *grad_out,
+                             const float *grad_mean, void *grad_student_hidden,
+                             float *grad_student_weight, int accumulate_grad_weight,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Policy-optimisation losses on the selective log-softmax.  The TRL v1.13
  * article (section on the other v1.13 changes) names fused linear GRPO, DPO
  * and KTO losses built on the chunked LM head, and the Unsloth GRPO

@@ -95,31 +95,41 @@ def make(name: str) -> str:
     return path
 
 
-DISTILL = ("distill_qwen3",)
+DISTILL = ("distill_qwen3", "distill_qwen3_jsd")
+# name -> (workload, divergence, beta)
+DISTILL_VARIANTS = {"distill_qwen3": ("distill_qwen3", "kl", 0.5),
+                    "distill_qwen3_jsd": ("distill_qwen3", "jsd", 0.5)}
 
 
 def make_distill(name: str) -> str:
-    """Distillation workload: sampled per-token KL and log-sum-exps, the mean,
-    the student's dH rows of the sampled tokens and dW rows of sampled vocabulary
-    entries (those need both log-sum-exps of every token)."""
-    w = synth.DISTILL_WORKLOADS[name]
+    """Distillation workload: sampled per-token divergence (KL, or the JSD with its
+    weight beta) and log-sum-exps, the mean, the student's dH rows of the sampled
+    tokens and dW rows of sampled vocabulary entries (those need both log-sum-exps
+    of every token, and for the JSD each token's gbar)."""
+    base, divergence, beta = DISTILL_VARIANTS[name]
+    kw = dict(divergence=divergence, beta=beta)
+    w = synth.DISTILL_WORKLOADS[base]
     t0 = time.time()
     x = synth.make_distill_inputs(w)
     rng = np.random.default_rng(w.seed + 77)
-    f = dst.forward(x.s_hidden, x.s_weight, x.t_hidden, x.t_weight, x.labels)
+    f = dst.forward(x.s_hidden, x.s_weight, x.t_hidden, x.t_weight, x.labels, **kw)
     tokens = sample_tokens(w, x.labels, rng)
     picks = {0, 255, 256, w.V - 1, w.V - 2}
     while len(picks) < 12:
         picks.add(int(rng.integers(0, w.V)))
     vocab = np.array(sorted(picks), dtype=np.int64)
     c = dst.token_scale(x.labels, w.T, grad_mean=1.0)
-    dh = dst.grad_hidden_rows(x.s_hidden, x.s_weight, x.t_hidden, x.t_weight, tokens, c[tokens])
+    dh = dst.grad_hidden_rows(x.s_hidden, x.s_weight, x.t_hidden, x.t_weight, tokens, c[tokens],
+                              **kw)
+    gbar = (dst.jsd_gbar(x.s_hidden, x.s_weight, x.t_hidden, x.t_weight, beta=beta)
+            if divergence == "jsd" else None)
     dw = dst.grad_weight_rows(x.s_hidden, x.s_weight, x.t_hidden, x.t_weight, vocab, c,
-                              f.lse_s, f.lse_t)
+                              f.lse_s, f.lse_t, gbar=gbar, **kw)
     path = os.path.join(HERE, f"{name}.npz")
     np.savez(path, tokens=tokens, kl=f.kl[tokens], lse_s=f.lse_s[tokens], lse_t=f.lse_t[tokens],
              mean=np.float64(f.mean), n_valid=np.int64(f.n_valid), vocab=vocab,
-             dh=dh.astype(np.float32), dw=dw.astype(np.float32), seed=np.int64(w.seed))
+             dh=dh.astype(np.float32), dw=dw.astype(np.float32), seed=np.int64(w.seed),
+             workload=np.str_(base), divergence=np.str_(divergence), beta=np.float64(beta))
     print(f"{name}: {time.time() - t0:.0f} s -> {path}", flush=True)
     return path
 

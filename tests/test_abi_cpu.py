@@ -238,3 +238,23 @@ def test_policy_workspace_bytes(flce):
         base = flce.lib.flce_workspace_bytes(T, D, V, cr)
         got = pb(T, D, V, cr, n)
         assert base + 12 * T + 16 * n <= got <= base + 12 * T + 16 * n + 7 * 256, (T, got, base)
+
+
+def test_distill_jsd_rejects_before_launch(flce):
+    def call(beta, **over):
+        a = dict(sh=16, sw=16, Ds=64, th=16, tw=16, Dt=96, labels=None, ign=-100, T=4, V=100,
+                 cr=16, xf=None, kl=4, mean=None, gout=None, gmean=None, gh=None, gw=None, acc=0,
+                 ws=16, wsb=1 << 30, stream=None)
+        a.update(over)
+        return flce.lib.flce_distill_jsd(a["sh"], a["sw"], a["Ds"], a["th"], a["tw"], a["Dt"],
+                                         a["labels"], a["ign"], a["T"], a["V"], a["cr"], a["xf"],
+                                         beta, a["kl"], a["mean"], a["gout"], a["gmean"], a["gh"],
+                                         a["gw"], a["acc"], a["ws"], a["wsb"], a["stream"])
+
+    for beta in (0.0, 1.0, -0.5, 1.5, float("nan")):
+        assert call(beta) == 1, beta                  # the weight must lie in (0, 1)
+    assert call(0.5, T=-1) == 2
+    assert call(0.5, Ds=60) == 4
+    assert call(0.5, gmean=4, gh=16) == 1            # gradient without grad_student_weight
+    assert call(0.5, tw=8) == 1                      # misaligned
+    assert call(0.5, wsb=16) == 3

@@ -1,4 +1,4 @@
-"""Distillation on the HIP path vs the CPU oracle, element by element.
+"""Distillation (KL and the generalized JSD) on the HIP path vs the CPU oracle, element by element.
 
 Per-token KL and the mean within 2e-3 absolute; the student's dH and dW within
 1e-2 relative Frobenius error (G is rounded to bf16 before the backward GEMMs,
@@ -48,7 +48,8 @@ def _tensors(x, dev):
             gu.bf16_tensor(x.t_hidden, dev), gu.bf16_tensor(x.t_weight, dev))
 
 
-def _run(x, *, mask=True, transform=None, grads=True, accumulate_into=None):
+def _run(x, *, mask=True, transform=None, grads=True, accumulate_into=None, divergence="kl",
+         beta=0.5):
     from chunked_lm_head_amd import flce
 
     dev = gu.device()
@@ -67,7 +68,8 @@ def _run(x, *, mask=True, transform=None, grads=True, accumulate_into=None):
         kw["accumulate"] = True
     kl, mean, dh, dw = flce.distill(sh, sw, th, tw, labels,
                                     chunk_rows=x.workload.chunk_rows,
-                                    transform=gu.binding_transform(transform), **kw)
+                                    transform=gu.binding_transform(transform),
+                                    divergence=divergence, beta=beta, **kw)
     torch.cuda.synchronize()
     r = dict(kl=kl.cpu().numpy(), mean=float(mean.cpu()))
     if grads:
@@ -76,16 +78,17 @@ def _run(x, *, mask=True, transform=None, grads=True, accumulate_into=None):
     return r
 
 
-def _oracle(x, *, mask=True, transform=None):
+def _oracle(x, *, mask=True, transform=None, divergence="kl", beta=0.5):
     tr = None if transform is None else fo.LogitTransform(*transform)
     labels = x.labels if mask else None
-    f = d.forward(x.s_hidden, x.s_weight, x.t_hidden, x.t_weight, labels, transform=tr)
+    kw = dict(transform=tr, divergence=divergence, beta=beta)
+    f = d.forward(x.s_hidden, x.s_weight, x.t_hidden, x.t_weight, labels, **kw)
     if x.grad_out is not None:
         dh, dw = d.backward(x.s_hidden, x.s_weight, x.t_hidden, x.t_weight, labels,
-                            grad_out=x.grad_out, transform=tr)
+                            grad_out=x.grad_out, **kw)
     else:
         dh, dw = d.backward(x.s_hidden, x.s_weight, x.t_hidden, x.t_weight, labels,
-                            grad_mean=1.0, transform=tr)
+                            grad_mean=1.0, **kw)
     return f, dh, dw
 
 
@@ -107,6 +110,47 @@ def test_distill_parity(case):
         m = x.labels == IGN
         assert np.all(r["kl"][m] == 0.0)
         assert np.all(r["dh"][m] == 0.0)
+
+
+JSD_CASES = [
+    # (case of CASES, beta)
+    ("tiny", 0.5), ("ragged", 0.5), ("per_token_grad", 0.1), ("many_blocks", 0.9),
+    ("wide", 0.5), ("no_mask", 0.3), ("softcap_temperature", 0.5), ("scaled", 0.7),
+]
+
+
+@pytest.mark.parametrize("name,beta", JSD_CASES, ids=lambda v: str(v))
+def test_jsd_parity(name, beta):
+    case = [c for c in CASES if c[0] == name][0]
+    _, shape, transform, mask = case
+    x = _inputs(name, shape)
+    w = x.workload
+    print(f"case jsd {name} beta {beta}: T={w.T} Ds={w.Hs} Dt={w.Ht} V={w.V} transform "
+          f"{transform}", flush=True)
+    r = _run(x, mask=mask, transform=transform, divergence="jsd", beta=beta)
+    f, dh, dw = _oracle(x, mask=mask, transform=transform, divergence="jsd", beta=beta)
+    e = (gu.max_abs(r["kl"], f.kl), abs(r["mean"] - f.mean), gu.rel_fro(r["dh"], dh),
+         gu.rel_fro(r["dw"], dw))
+    print(f"  |d jsd| {e[0]:.2e} |d mean| {e[1]:.2e} dH rel {e[2]:.2e} dW rel {e[3]:.2e}",
+          flush=True)
+    assert e[0] <= gu.OUT_TOL and e[1] <= gu.OUT_TOL, e
+    assert e[2] <= gu.GRAD_TOL and e[3] <= gu.GRAD_TOL, e
+    if mask:
+        m = x.labels == IGN
+        assert np.all(r["kl"][m] == 0.0) and np.all(r["dh"][m] == 0.0)
+
+
+def test_jsd_forward_only_matches_and_identical_heads_vanish():
+    x = _inputs("jfo", (300, 256, 384, 5000, 64, 0.05, "mean", None, None))
+    full = _run(x, divergence="jsd", beta=0.4)
+    only = _run(x, grads=False, divergence="jsd", beta=0.4)
+    assert np.array_equal(full["kl"], only["kl"]) and full["mean"] == only["mean"]
+    y = _inputs("jsame", (300, 256, 256, 5000, 64, 0.05, "mean", None, None))
+    y.t_hidden, y.t_weight = y.s_hidden, y.s_weight
+    r = _run(y, divergence="jsd", beta=0.5)
+    # p_t = p_s bit for bit; beta p + (1 - beta) p rounds to p within an ulp
+    assert np.abs(r["kl"]).max() <= 1e-6, np.abs(r["kl"]).max()
+    assert np.abs(r["dw"]).max() <= 1e-6, np.abs(r["dw"]).max()
 
 
 def test_identical_heads_give_exact_zero():

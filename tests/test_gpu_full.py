@@ -10,6 +10,7 @@ are checked on the complete outputs:
   * ignored tokens and tokens with zero upstream grad have exactly zero dH rows
     (and ignored tokens output exactly 0).
 """
+import math
 import os
 
 import numpy as np
@@ -126,23 +127,28 @@ def test_long_context_memory_is_one_chunk_of_logits():
     assert peak - io <= wsb + (64 << 20), (peak, io, wsb)
 
 
-def test_distill_full_size_against_oracle_samples():
-    """Distillation at the student-8B / wider-teacher shape: sampled per-token KL and
-    log-sum-exps, the mean, and sampled dH / dW rows of the student (float64 oracle over
+@pytest.mark.parametrize("name", ["distill_qwen3", "distill_qwen3_jsd"])
+def test_distill_full_size_against_oracle_samples(name):
+    """Distillation at the student-8B / wider-teacher shape, KL and JSD: sampled per-token
+    divergence, the mean, and sampled dH / dW rows of the student (float64 oracle over
     all tokens and the full vocabulary, tests/golden/make_golden.py)."""
     from chunked_lm_head_amd import flce
 
-    g = _golden("distill_qwen3")
+    g = _golden(name)
     w = synth.DISTILL_WORKLOADS["distill_qwen3"]
     assert int(g["seed"]) == w.seed
-    print(f"case distill_qwen3: T={w.T} Ds={w.Hs} Dt={w.Ht} V={w.V}", flush=True)
+    divergence = str(g["divergence"]) if "divergence" in g else "kl"
+    beta = float(g["beta"]) if "beta" in g else 0.5
+    print(f"case {name}: T={w.T} Ds={w.Hs} Dt={w.Ht} V={w.V} {divergence} beta {beta}",
+          flush=True)
     x = synth.make_distill_inputs(w)
     dev = gu.device()
     sh, sw = gu.bf16_tensor(x.s_hidden, dev), gu.bf16_tensor(x.s_weight, dev)
     th, tw = gu.bf16_tensor(x.t_hidden, dev), gu.bf16_tensor(x.t_weight, dev)
     y = torch.from_numpy(x.labels).to(dev)
     kl, mean, dh, dw = flce.distill(sh, sw, th, tw, y, chunk_rows=w.chunk_rows,
-                                    grad_mean=torch.ones((), dtype=torch.float32, device=dev))
+                                    grad_mean=torch.ones((), dtype=torch.float32, device=dev),
+                                    divergence=divergence, beta=beta)
     torch.cuda.synchronize()
     tok = torch.from_numpy(g["tokens"]).to(dev)
     voc = torch.from_numpy(g["vocab"]).to(dev)
@@ -150,14 +156,17 @@ def test_distill_full_size_against_oracle_samples():
     e = (gu.max_abs(kl_s, g["kl"]), abs(float(mean.cpu()) - float(g["mean"])),
          gu.rel_fro(dh[tok].float().cpu().numpy(), g["dh"].astype(np.float64)),
          gu.rel_fro(dw[voc].cpu().numpy(), g["dw"].astype(np.float64)))
-    print(f"distill_qwen3: |d kl| {e[0]:.2e} |d mean| {e[1]:.2e} dH rel {e[2]:.2e} "
+    print(f"{name}: |d value| {e[0]:.2e} |d mean| {e[1]:.2e} dH rel {e[2]:.2e} "
           f"dW rel {e[3]:.2e}", flush=True)
     assert e[0] <= gu.OUT_TOL and e[1] <= gu.OUT_TOL, e
     assert e[2] <= gu.GRAD_TOL and e[3] <= gu.GRAD_TOL, e
-    # properties on the complete outputs: KL >= 0 (up to rounding), masked tokens are 0
+    # properties on the complete outputs: the divergence >= 0 (up to rounding; the JSD
+    # also <= ln 2 at beta = 1/2), masked tokens are 0
     m = y == synth.IGNORE_INDEX
     assert bool((kl[m] == 0).all()) and bool((dh[m] == 0).all())
     assert float(kl[~m].min()) > -1e-3
+    if divergence == "jsd" and beta == 0.5:
+        assert float(kl.max()) <= math.log(2.0) + 1e-3
     lhs = float((dh.double() * sh.double()).sum())
     rhs = float((dw.double() * sw.double()).sum())
     assert abs(lhs - rhs) <= 1e-2 * max(abs(lhs), abs(rhs), 1e-30), (lhs, rhs)
