@@ -464,7 +464,8 @@ def distill(student_hidden, student_weight, teacher_hidden, teacher_weight,
 
 
 class _ChunkedDistillKL(torch.autograd.Function):
-    """Mean (``reduction="mean"``) or per-token (``"none"``) KL(teacher || student).
+    """Mean (``reduction="mean"``) or per-token (``"none"``) KL(teacher || student), or
+    the generalized JSD.
 
     The mean's gradients are computed in the forward call (c = 1 / N_kept), which
     saves a second recompute, and scaled by the upstream scalar in the backward
@@ -474,8 +475,9 @@ class _ChunkedDistillKL(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, s_hidden, s_weight, t_hidden, t_weight, labels, ignore_index, chunk_rows,
-                reduction, transform):
-        kw = dict(ignore_index=ignore_index, chunk_rows=chunk_rows, transform=transform)
+                reduction, transform, divergence="kl", beta=0.5):
+        kw = dict(ignore_index=ignore_index, chunk_rows=chunk_rows, transform=transform,
+                  divergence=divergence, beta=beta)
         need = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
         if reduction == "mean" and need:
             one = torch.ones((), dtype=torch.float32, device=s_hidden.device)
@@ -492,7 +494,7 @@ class _ChunkedDistillKL(torch.autograd.Function):
     def backward(ctx, grad):
         reduction, kw, need = ctx.cfg
         if not need:
-            return (None,) * 9
+            return (None,) * 11
         if reduction == "mean":
             dh, dw = ctx.saved_tensors
             g = grad.float()
@@ -502,20 +504,21 @@ class _ChunkedDistillKL(torch.autograd.Function):
             s_hidden, s_weight, t_hidden, t_weight, labels = ctx.saved_tensors
             _, _, dh, dw = distill(s_hidden, s_weight, t_hidden, t_weight, labels,
                                    grad_out=grad.float().contiguous(), **kw)
-        return dh, dw.to(torch.bfloat16), None, None, None, None, None, None, None
+        return dh, dw.to(torch.bfloat16), None, None, None, None, None, None, None, None, None
 
 
 def chunked_distill_kl(student_hidden, student_weight, teacher_hidden, teacher_weight,
                        labels=None, *, ignore_index=-100, chunk_rows=256, reduction="mean",
                        logit_scale_multiply=0.0, logit_scale_divide=0.0, logit_softcapping=0.0,
-                       temperature=1.0):
+                       temperature=1.0, divergence="kl", beta=0.5):
     """Autograd-aware KL(teacher || student) of two LM heads, chunked (gradients reach
-    the student's hidden states and lm_head only)."""
+    the student's hidden states and lm_head only); ``divergence="jsd"`` takes the
+    generalized Jensen-Shannon divergence with weight ``beta`` instead."""
     xf = _transform_kwargs(logit_scale_multiply, logit_scale_divide, logit_softcapping,
                            temperature)
     return _ChunkedDistillKL.apply(student_hidden, student_weight, teacher_hidden,
                                    teacher_weight, labels, ignore_index, chunk_rows, reduction,
-                                   xf)
+                                   xf, divergence, beta)
 
 
 # ---------------------------------------------------------------------------

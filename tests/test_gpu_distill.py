@@ -200,6 +200,27 @@ def test_autograd_wrapper():
         assert gu.rel_fro(b.grad.float().cpu().numpy(), odw) <= gu.GRAD_TOL
 
 
+def test_autograd_wrapper_jsd():
+    from chunked_lm_head_amd import flce
+
+    x = _inputs("agj", (260, 128, 192, 2000, 64, 0.1, "none", 0.3, 0.3))
+    dev = gu.device()
+    sh, sw, th, tw = _tensors(x, dev)
+    labels = torch.from_numpy(x.labels).to(dev)
+    f, _, _ = _oracle(x, divergence="jsd", beta=0.3)
+    odh, odw = d.backward(x.s_hidden, x.s_weight, x.t_hidden, x.t_weight, x.labels,
+                          grad_mean=2.5, divergence="jsd", beta=0.3)
+    a = sh.clone().requires_grad_()
+    b = sw.clone().requires_grad_()
+    out = flce.chunked_distill_kl(a, b, th, tw, labels, chunk_rows=64, divergence="jsd",
+                                  beta=0.3)
+    (out * 2.5).backward()
+    torch.cuda.synchronize()
+    assert abs(float(out.detach().cpu()) - f.mean) <= gu.OUT_TOL
+    assert gu.rel_fro(a.grad.float().cpu().numpy(), odh) <= gu.GRAD_TOL
+    assert gu.rel_fro(b.grad.float().cpu().numpy(), odw) <= gu.GRAD_TOL
+
+
 def test_empty_batch():
     from chunked_lm_head_amd import flce
 
