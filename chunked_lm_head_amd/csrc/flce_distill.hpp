@@ -212,15 +212,28 @@ __global__ void __launch_bounds__(kThreads)
         pipe_prologue(A, B, smem, wave);
       }
       const int col = vw - p.vc0;  // column of this wave's first vocabulary row in the block
+      const int tl0 = t0 - p.rb0 + wn * 128 + (lane & 15);  // row nb = 0 in the block
+      // Students read p_t one token row (nb) ahead: row nb + 1 is in flight while
+      // row nb is processed.
+      f32x4 ptb[2][8];
+      if constexpr (!kTeacher) {
+        const float *prow0 = p.P + (size_t)tl0 * p.Pp + col;
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) ptb[0][mb] = *(const f32x4 *)(prow0 + acc_row(mb, 0, lane));
+      }
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
-        const int tl = t0 - p.rb0 + wn * 128 + nb * 16 + (lane & 15);  // row in the block
+        const int tl = tl0 + nb * 16;  // row in the block
         float *prow = p.P + (size_t)tl * p.Pp + col;
-        f32x4 pt[8];
+        f32x4 *pt = ptb[nb & 1];
         if constexpr (!kTeacher) {
+          if (nb + 1 < 8) {
 #pragma unroll
-          for (int mb = 0; mb < 8; ++mb) pt[mb] = *(const f32x4 *)(prow + acc_row(mb, 0, lane));
-          // G is written over these bytes below: keep every read of the row first
+            for (int mb = 0; mb < 8; ++mb)
+              ptb[(nb + 1) & 1][mb] = *(const f32x4 *)(prow + 16 * p.Pp + acc_row(mb, 0, lane));
+          }
+          // G of row nb is written over that row's p_t below: every read of rows nb
+          // and nb + 1 is issued first
           __asm__ volatile("" ::: "memory");
         }
 #pragma unroll
