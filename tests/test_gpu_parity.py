@@ -86,6 +86,27 @@ def test_chunk_rows_invariance_and_determinism():
     assert again["mean"] == runs[16]["mean"]
 
 
+def test_token_permutation():
+    """Permuting the tokens permutes out, lse and the dH rows and leaves dW and the mean
+    unchanged, up to fp32 reordering (the row blocks, token tiles and their ragged tail all
+    change membership)."""
+    import dataclasses
+    w = synth.custom("perm", T=700, H=192, V=3000, ignore_frac=0.05, seed=21)
+    x = synth.make_inputs(w)
+    g = np.random.default_rng(2).standard_normal(700).astype(np.float32)
+    perm = np.random.default_rng(3).permutation(700)
+    xp = dataclasses.replace(x, hidden=np.ascontiguousarray(x.hidden[perm]),
+                             labels=np.ascontiguousarray(x.labels[perm]))
+    for kw in (dict(), dict(grad_out=g)):
+        a = gu.run(x, chunk_rows=64, **kw)
+        b = gu.run(xp, chunk_rows=64, **({"grad_out": g[perm]} if kw else {}))
+        assert gu.max_abs(b["out"], a["out"][perm]) <= 1e-5
+        assert gu.max_abs(b["lse"], a["lse"][perm]) <= 1e-5
+        assert abs(b["mean"] - a["mean"]) <= 1e-5
+        assert gu.rel_fro(b["dh"], a["dh"][perm]) <= 4e-3  # bf16 dH: at most last-bit flips
+        assert gu.rel_fro(b["dw"], a["dw"]) <= 5e-5
+
+
 def test_logprob_is_minus_nll_and_grad_duality():
     w = synth.custom("dual", T=200, H=128, V=2000, ignore_frac=0.05, seed=5)
     x = synth.make_inputs(w)
