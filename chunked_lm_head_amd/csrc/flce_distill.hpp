@@ -188,7 +188,6 @@ __global__ void __launch_bounds__(kThreads)
     }
     const float beta = p.beta, nbeta = 1.f - p.beta;
     constexpr float kFltMin = 1.17549435e-38f;
-    const float ks = p.xf.zscale * kLog2e;           // uncapped: z' log2 e = z ks
     const float dscale = p.xf.zscale * p.xf.inv_temp;  // capped: dz'/dz = dscale (1 - t^2)
 
     OperandK B;
