@@ -1,5 +1,4 @@
 """Plant plausible mistakes in copies of the oracle; some pin must catch each one."""
-import importlib.util
 import os
 import sys
 import types
