@@ -26,6 +26,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 
 #include "flce.h"
@@ -261,24 +262,24 @@ flce_status make_distill_plan(int64_t T, int64_t Ds, int64_t Dt, int64_t V, int6
   return FLCE_OK;
 }
 
+// The current device must be a gfx950.  The answer is cached per device; calls
+// from several threads may fill the cache at once and store the same value.
 flce_status check_device() {
-  static int cache[64];  // 0 unknown, 1 ok, 2 unsupported
+  static std::atomic<int> cache[64];  // 0 unknown, 1 ok, 2 unsupported
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(FLCE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
   if (dev < 0 || dev >= 64) return fail(FLCE_ERR_UNSUPPORTED, "device index %d", dev);
-  if (cache[dev] == 0) {
+  int known = cache[dev].load(std::memory_order_relaxed);
+  if (known == 0) {
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess)
       return fail(FLCE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
-    cache[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
-    if (cache[dev] == 2) {
-      snprintf(g_last_error, sizeof(g_last_error), "device %d is %s, not gfx950", dev,
-               prop.gcnArchName);
-    }
+    known = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    cache[dev].store(known, std::memory_order_relaxed);
   }
-  if (cache[dev] != 1) return FLCE_ERR_UNSUPPORTED;
+  if (known != 1) return fail(FLCE_ERR_UNSUPPORTED, "device %d is not a gfx950", dev);
   return FLCE_OK;
 }
 
