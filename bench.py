@@ -13,6 +13,7 @@ float64 CPU oracle on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -40,6 +41,9 @@ def parse():
     ap.add_argument("--beta", type=float, default=0.5,
                     help="JSD weight of the teacher in the mixture (--divergence jsd)")
     ap.add_argument("--chunk-rows", type=int, default=None)
+    ap.add_argument("--token-shard", type=int, default=1, metavar="N",
+                    help="run one GPU's share of a token-parallel split over N GPUs: the "
+                         "cross-entropy workload with T / N of its tokens")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--cpu-sample-vocab", type=int, default=1 << 30)
@@ -141,6 +145,13 @@ def main():
         policy_main(args)
         return
     w = synth.WORKLOADS[args.workload]
+    if args.token_shard != 1:
+        n = args.token_shard
+        if n < 1 or w.T % n or (w.seq_len and (w.T // n) % w.seq_len):
+            raise SystemExit(f"--token-shard {n} does not split {w.name}'s {w.T} tokens into "
+                             "equal shards of whole sequences")
+        w = dataclasses.replace(w, T=w.T // n,
+                                ignore_count=int(round(w.ignore_count / n)))
     chunk_rows = args.chunk_rows or w.chunk_rows
     xf_vals = dict(scale_multiply=args.logit_scale_multiply, scale_divide=args.logit_scale_divide,
                    softcap=args.logit_softcapping, temperature=args.temperature)
@@ -215,7 +226,8 @@ def main():
 
     traffic = None
     # the counters were taken without a softcap (the capped forward is another instantiation)
-    if os.path.exists(args.traffic_json) and args.logit_softcapping == 0.0:
+    if (os.path.exists(args.traffic_json) and args.logit_softcapping == 0.0
+            and args.token_shard == 1):
         try:
             tj = json.load(open(args.traffic_json))
             rec = tj.get(args.workload, {}).get("fwd_lse_kernel")
@@ -258,6 +270,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "tokens": T, "hidden": D, "vocab": V,
+                   **({"token_shard": f"1/{args.token_shard}"} if args.token_shard != 1
+                      else {}),
                    "chunk_rows": chunk_rows, "mode": w.mode, "reduction": w.reduction,
                    "ignored_tokens": w.ignore_count,
                    **({"logit_transform": xf_vals} if has_xf else {})},
