@@ -46,8 +46,11 @@
  *    and are left out of the mean's denominator.
  *  - Results are deterministic: repeated calls with the same inputs give the
  *    same bits (no floating-point atomics).
- *  - The one host pointer is the optional logit transform (read during the
- *    call, not retained).
+ *  - The host pointers are the optional logit transform and the policy
+ *    losses' parameter struct (read during the call, not retained).
+ *  - A call only launches kernels on `stream` (no allocation, memset, copy or
+ *    synchronisation), so it may be recorded into a HIP graph by stream
+ *    capture; a replay repeats the work with the captured pointers and sizes.
  */
 #ifndef FLCE_H
 #define FLCE_H
