@@ -138,6 +138,8 @@ def main():
         gemm_ceiling(synth.WORKLOADS[args.workload])
         return
 
+    if args.token_shard != 1 and args.workload not in synth.WORKLOADS:
+        raise SystemExit("--token-shard applies to the cross-entropy workloads only")
     if args.workload in synth.DISTILL_WORKLOADS:
         distill_main(args)
         return
