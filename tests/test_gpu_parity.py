@@ -107,6 +107,35 @@ def test_token_permutation():
         assert gu.rel_fro(b["dw"], a["dw"]) <= 5e-5
 
 
+def test_million_entry_vocabulary():
+    """V = 1,000,003 (a ragged last tile, several vocabulary chunks of ~250k rows, 1,024
+    forward splits per token tile, split-K dH over 256 partial sums) with a small D.  The
+    oracle covers sampled tokens: the upstream gradient is zero except on 12 of them, so dW
+    is exactly the oracle's dW of those 12 tokens and every other dH row is exactly zero."""
+    w = synth.custom("huge_vocab", T=300, H=64, V=1_000_003, chunk_rows=64, ignore_frac=0.05,
+                     mode="logprob", reduction="none", seed=77)
+    x = synth.make_inputs(w)
+    print(f"case huge_vocab: T={w.T} D={w.H} V={w.V}", flush=True)
+    rng = np.random.default_rng(8)
+    valid = np.nonzero(x.labels != IGN)[0]
+    rows = np.sort(rng.choice(valid, 12, replace=False))
+    g = np.zeros(w.T, dtype=np.float32)
+    g[rows] = rng.standard_normal(12).astype(np.float32)
+    r = gu.run(x, grad_out=g)
+    assert np.all(np.isfinite(r["out"])) and np.all(np.isfinite(r["lse"]))
+    probe = np.sort(np.concatenate([rows, rng.choice(np.setdiff1d(np.arange(w.T), rows), 12,
+                                                     replace=False)]))
+    out, lse = o.forward_rows(x.hidden, x.weight, x.labels, probe, IGN, "logprob")
+    assert gu.max_abs(r["out"][probe], out) <= gu.OUT_TOL
+    assert gu.max_abs(r["lse"][probe], lse) <= gu.OUT_TOL
+    dh, dw = o.backward(x.hidden[rows], x.weight, x.labels[rows], IGN, "logprob",
+                        grad_out=g[rows])
+    assert gu.rel_fro(r["dh"][rows], dh) <= gu.GRAD_TOL
+    others = np.setdiff1d(np.arange(w.T), rows)
+    assert np.all(r["dh"][others] == 0.0)
+    assert gu.rel_fro(r["dw"], dw) <= gu.GRAD_TOL
+
+
 def test_logprob_is_minus_nll_and_grad_duality():
     w = synth.custom("dual", T=200, H=128, V=2000, ignore_frac=0.05, seed=5)
     x = synth.make_inputs(w)
