@@ -28,6 +28,7 @@ SHAPES = [
     ("one_token", 1, 64, 300, 256, 0.0, "nll", "mean"),
     ("wide_d", 130, 1032, 777, 16, 0.1, "logprob", "mean"),
     ("max_d", 300, 65536, 600, 64, 0.05, "nll", "mean"),   # the largest hidden size accepted
+    ("min_d", 90, 8, 1000, 16, 0.1, "logprob", "mean"),    # the smallest: one partial K stage
 ]
 
 
