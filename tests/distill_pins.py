@@ -29,7 +29,7 @@ import numpy as np
 from chunked_lm_head_amd import synth
 from oracle import flce_oracle as fo
 
-from oracle_pins import bf16_exact, py_decode
+from oracle_pins import bf16_exact, py_decode, small_blocks
 
 IGN = -100
 
@@ -317,6 +317,39 @@ def check_jsd_rows_helpers(d):
     assert np.allclose(rw, dw[vr], rtol=1e-12, atol=1e-15)
 
 
+def check_row_blocks(d):
+    """Row blocks are a schedule detail: with one or two rows per block the divergence,
+    both log-sum-exps, the student's gradients and the JSD row sums match the
+    single-block results, and the brute-forced closed forms still hold."""
+    with small_blocks(d.fo, 1):
+        check_uniform_teacher(d)
+        check_onehot_teacher_is_cross_entropy(d)
+    T, Hs, Ht, V = 9, 8, 6, 17
+    x = _case(T, Hs, Ht, V, seed=61, ignore_frac=0.2, reduction="none")
+    args = (x.s_hidden, x.s_weight, x.t_hidden, x.t_weight)
+    tr = fo.LogitTransform(softcap=2.5, temperature=0.9)
+    for kw in (dict(divergence="kl"), dict(divergence="jsd", beta=0.3),
+               dict(divergence="kl", transform=tr), dict(divergence="jsd", beta=0.6,
+                                                         transform=tr)):
+        f1 = d.forward(*args, x.labels, **kw)
+        b1 = d.backward(*args, x.labels, grad_out=x.grad_out, **kw)
+        gb1 = (d.jsd_gbar(*args, beta=kw["beta"], transform=kw.get("transform"))
+               if kw["divergence"] == "jsd" else None)
+        for elems in (1, 2 * V):
+            with small_blocks(d.fo, elems):
+                assert d.fo._rows_per_block(V, T) == max(1, elems // V)
+                f2 = d.forward(*args, x.labels, **kw)
+                b2 = d.backward(*args, x.labels, grad_out=x.grad_out, **kw)
+                gb2 = (d.jsd_gbar(*args, beta=kw["beta"], transform=kw.get("transform"))
+                       if gb1 is not None else None)
+            for a, b in ((f2.kl, f1.kl), (f2.lse_s, f1.lse_s), (f2.lse_t, f1.lse_t),
+                         (b2[0], b1[0]), (b2[1], b1[1])):
+                assert np.allclose(a, b, rtol=1e-13, atol=1e-15), np.abs(a - b).max()
+            assert abs(f2.mean - f1.mean) < 1e-13
+            if gb1 is not None:
+                assert np.allclose(gb2, gb1, rtol=1e-13, atol=1e-15)
+
+
 ALL_CHECKS = [
     check_identical_heads,
     check_uniform_teacher,
@@ -333,4 +366,5 @@ ALL_CHECKS = [
     check_jsd_two_class,
     check_jsd_finite_differences,
     check_jsd_rows_helpers,
+    check_row_blocks,
 ]

@@ -17,6 +17,7 @@ requires that some check here fails for each of them.
 """
 from __future__ import annotations
 
+import contextlib
 import math
 import struct
 
@@ -430,6 +431,57 @@ def check_transform_rows_and_args(o):
         raise AssertionError(f"invalid transform {bad} was accepted")
 
 
+@contextlib.contextmanager
+def small_blocks(o, elems):
+    """The oracle's row blocks forced down to ``elems`` logits each, so that every call
+    below runs its row-blocked loop over several blocks (at least one row per block)."""
+    saved = o._BLOCK_ELEMS
+    o._BLOCK_ELEMS = elems
+    try:
+        yield
+    finally:
+        o._BLOCK_ELEMS = saved
+
+
+def check_row_blocks(o):
+    """Row blocks are a schedule detail: with one or three rows per block the results
+    match the brute force and the single-block results.  The full-size expected values
+    are generated through many blocks, so this is their pin."""
+    with small_blocks(o, 1):
+        check_bruteforce(o)                  # independent facts, one row per block
+        check_ignore_index(o)
+    T, H, V = 11, 8, 13
+    hb, wb, labels = _rand_case(T, H, V, seed=77, w_std=0.6, ignore=(2, 9))
+    g = np.random.default_rng(77).standard_normal(T)
+    tf = o.LogitTransform(scale_multiply=1.5, softcap=3.0, temperature=0.8)
+    for mode in ("nll", "logprob"):
+        for tr in (None, tf):
+            f1 = o.forward(hb, wb, labels, IGN, mode, transform=tr)
+            b1 = o.backward(hb, wb, labels, IGN, mode, grad_out=g, transform=tr)
+            m1 = o.backward(hb, wb, labels, IGN, mode, grad_mean=0.7, lse=f1.lse, transform=tr)
+            for elems in (1, 3 * V):         # 1 row, then 3 rows (ragged last block)
+                with small_blocks(o, elems):
+                    assert o._rows_per_block(V, T) == max(1, elems // V)
+                    f2 = o.forward(hb, wb, labels, IGN, mode, transform=tr)
+                    b2 = o.backward(hb, wb, labels, IGN, mode, grad_out=g, transform=tr)
+                    m2 = o.backward(hb, wb, labels, IGN, mode, grad_mean=0.7, lse=f2.lse,
+                                    transform=tr)
+                assert np.allclose(f2.out, f1.out, rtol=1e-13, atol=1e-15)
+                assert np.allclose(f2.lse, f1.lse, rtol=1e-13, atol=1e-15)
+                assert abs(f2.mean - f1.mean) < 1e-13
+                for a, b in zip(b2 + m2, b1 + m1):
+                    assert np.allclose(a, b, rtol=1e-13, atol=1e-15), np.abs(a - b).max()
+
+
+def check_default_multiplier(o):
+    """The page's default chunk multiplier max(4, context // 4096), evaluated by hand
+    above the floor of 4, where a wrong divisor would show."""
+    hand = {1: 4, 4096: 4, 8192: 4, 16383: 4, 16384: 4, 20480: 5, 24576: 6, 65536: 16,
+            131072: 32, 1048576: 256}
+    for ctx, mult in hand.items():
+        assert o.default_multiplier(ctx) == mult, (ctx, o.default_multiplier(ctx), mult)
+
+
 ALL_CHECKS = [
     check_zero_weight,
     check_two_class,
@@ -448,4 +500,6 @@ ALL_CHECKS = [
     check_softcap_limits,
     check_transform_finite_differences,
     check_transform_rows_and_args,
+    check_row_blocks,
+    check_default_multiplier,
 ]

@@ -40,6 +40,13 @@ MUTANTS = {
     "jsd_grad_without_row_sum": ("g = ps * (gv - gbar) * c[:, None]", "g = ps * gv * c[:, None]"),
     "jsd_grad_weight": ("        gv = (1.0 - beta) * (log_ps - log_m)\n",
                         "        gv = beta * (log_ps - log_m)\n"),
+    # row-blocked loops
+    "block_scale_offset_dropped": ("g = grad_logits(zs, zt, c[r0:r1], dzs, divergence, beta)",
+                                   "g = grad_logits(zs, zt, c[:r1 - r0], dzs, divergence, beta)"),
+    "block_lse_offset_dropped": ("        lse_t[r0:r1] = fo.logsumexp_rows(zt)\n",
+                                 "        lse_t[:r1 - r0] = fo.logsumexp_rows(zt)\n"),
+    "block_gbar_offset_dropped": ("out[r0:r1] = (ps * gv).sum(axis=1)",
+                                  "out[:r1 - r0] = (ps * gv).sum(axis=1)"),
 }
 
 

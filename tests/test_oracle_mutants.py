@@ -38,6 +38,15 @@ MUTANTS = {
                                "            x = self.softcap * t * self.temperature\n"),
     "divide_multiplies": ("            x = x / self.scale_divide\n", "            x = x * self.scale_divide\n"),
     "weight_rows_drop_chain": ("    if dz is not None:\n        g *= dz\n", ""),
+    # row-blocked loops and the page's chunk multiplier
+    "block_label_offset_dropped": ("zy[r0 + rows] = z[rows, labels[r0 + rows]]",
+                                   "zy[rows] = z[rows, labels[r0 + rows]]"),
+    "block_given_lse_offset_dropped": (
+        "l = logsumexp_rows(z) if lse is None else np.asarray(lse[r0:r1], dtype=np.float64)",
+        "l = logsumexp_rows(z) if lse is None else np.asarray(lse[:r1 - r0], dtype=np.float64)"),
+    "block_scale_offset_dropped": ("g = grad_logits(z, l, labels[r0:r1], c[r0:r1], dz)",
+                                   "g = grad_logits(z, l, labels[r0:r1], c[:r1 - r0], dz)"),
+    "multiplier_divisor_2048": ("return max(4, context // 4096)", "return max(4, context // 2048)"),
 }
 
 
