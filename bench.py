@@ -51,10 +51,6 @@ def parse():
                     help="only time the vendor GEMM (torch.mm -> hipBLASLt) at this path's shapes")
     ap.add_argument("--sample-power", action="store_true",
                     help="sample socket power and GFX clocks with amd-smi during the timed steps")
-    ap.add_argument("--lds-rate", action="store_true",
-                    help="only run the LDS read-rate probe (4, 8 and 16 waves per CU)")
-    ap.add_argument("--mfma-ceiling", action="store_true",
-                    help="only run the sustained-MFMA probe (random operands, no memory traffic)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for HBM counters)")
     ap.add_argument("--logit-scale-multiply", type=float, default=0.0,
@@ -128,12 +124,6 @@ def main():
 
     from chunked_lm_head_amd import flce, synth
 
-    if args.mfma_ceiling:
-        mfma_ceiling()
-        return
-    if args.lds_rate:
-        print(json.dumps(_run_probe("lds_rate")), flush=True)
-        return
     if args.gemm_ceiling:
         gemm_ceiling(synth.WORKLOADS[args.workload])
         return
@@ -578,29 +568,6 @@ class PowerSampler:
         return {"samples": len(s), "socket_w_mean": round(sum(watts) / len(watts), 1),
                 "socket_w_max": max(watts), "cap_w": 1400.0,
                 "gfx_clk_mhz_mean": round(sum(clks) / len(clks), 0) if clks else None}
-
-
-def _run_probe(name: str) -> dict:
-    """Runs chunked_lm_head_amd/<name> (a measurement program built with the library) in a
-    child process and returns the JSON object of its last output line."""
-    import subprocess
-
-    exe = os.path.join(ROOT, "chunked_lm_head_amd", name)
-    if not os.path.exists(exe):
-        raise SystemExit(f"{exe} is not built; run __graft_entry__.build() first")
-    proc = subprocess.run([exe], capture_output=True, text=True, timeout=300)
-    if proc.returncode != 0:
-        raise SystemExit(f"{name} failed ({proc.returncode}): {proc.stderr.strip()}")
-    return json.loads(proc.stdout.strip().splitlines()[-1])
-
-
-def mfma_ceiling() -> None:
-    """Runs the sustained-MFMA probe and reports its bf16 rates as fractions of the
-    2.5 PFLOP/s data-sheet peak."""
-    rec = _run_probe("mfma_ceiling")["mfma_ceiling"]
-    for k in ("v_mfma_f32_32x32x16_bf16", "v_mfma_f32_16x16x32_bf16"):
-        rec[k.replace("v_mfma_f32_", "frac_")] = round(rec[k] / PEAK_BF16, 4)
-    print(json.dumps({"mfma_ceiling": rec}), flush=True)
 
 
 def gemm_ceiling(w) -> None:

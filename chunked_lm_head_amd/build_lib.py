@@ -11,10 +11,6 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libflce.so")
-CEILING_SRC = os.path.join(CSRC, "mfma_ceiling.hip")
-CEILING_BIN = os.path.join(PKG, "mfma_ceiling")  # measurement program, not part of the library
-LDS_SRC = os.path.join(CSRC, "lds_rate.hip")
-LDS_BIN = os.path.join(PKG, "lds_rate")          # measurement program, not part of the library
 SOURCES = [os.path.join(CSRC, "flce_api.hip")]  # includes every kernel header of csrc/
 
 HIPCC_FLAGS = [
@@ -50,28 +46,7 @@ def build_library(verbose: bool = False) -> str:
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, LIB)
-    build_ceiling_probe(verbose)
-    build_probe(LDS_SRC, LDS_BIN, verbose)
     return LIB
-
-
-def build_ceiling_probe(verbose: bool = False) -> str:
-    """Compile the sustained-MFMA probe that bench.py --mfma-ceiling runs."""
-    return build_probe(CEILING_SRC, CEILING_BIN, verbose)
-
-
-def build_probe(src: str, out: str, verbose: bool = False) -> str:
-    """Compile one stand-alone measurement program (bench.py runs them on request)."""
-    flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
-    tmp = out + ".tmp"
-    cmd = [hipcc(), *flags, src, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    proc = subprocess.run(cmd, capture_output=True, text=True)
-    if proc.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src} ({proc.returncode}):\n{proc.stderr}")
-    os.replace(tmp, out)
-    return out
 
 
 if __name__ == "__main__":

@@ -346,7 +346,8 @@ flce_status launch_ht(const void *hidden, uint16_t *ht, int64_t D, int64_t R, in
 // dH partial sums and the dW update of one (row block, vocabulary chunk) from
 // its bf16 gradient block G: token rows of pitch Gp, gcols vocabulary columns
 // (a multiple of 256), plain or grouped (written over an fp32 block: Gp =
-// 2 gcols, each 128-column group in the first half of its fp32 bytes).
+// 2 gcols, each 128-column group in the first half of its fp32 bytes).  A
+// NULL dhacc skips dH, a NULL grad_weight skips dW.
 flce_status launch_dh_dw(const uint16_t *G, int Gp, int64_t gcols, bool grouped,
                          const void *weight, const uint16_t *ht, int64_t D, int64_t V, int64_t R,
                          int64_t rcount, int64_t vc0, int64_t vcount, int64_t dh_splits,
@@ -369,11 +370,14 @@ flce_status launch_dh_dw(const uint16_t *G, int Gp, int64_t gcols, bool grouped,
   h.acc = dhacc;
   h.accumulate = acc_dh ? 1 : 0;
   const unsigned dh_grid = (unsigned)(h.tiles_m * h.tiles_n * h.splits);
-  if (grouped)
-    dst_dh_kernel<<<dh_grid, kThreads, 0, s>>>(h);
-  else
-    bwd_dh_kernel<<<dh_grid, kThreads, 0, s>>>(h);
-  FLCE_TRY(launched("bwd_dh"));
+  if (dhacc) {
+    if (grouped)
+      dst_dh_kernel<<<dh_grid, kThreads, 0, s>>>(h);
+    else
+      bwd_dh_kernel<<<dh_grid, kThreads, 0, s>>>(h);
+    FLCE_TRY(launched("bwd_dh"));
+  }
+  if (!grad_weight) return FLCE_OK;
 
   BwdDwParams w;
   w.G = G;
@@ -439,20 +443,21 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
   if (grad_out && grad_mean)
     return fail(FLCE_ERR_ARG, "give at most one of grad_out and grad_mean");
   const bool grads = grad_out || grad_mean;
-  if (grads && !grad_student_weight)
-    return fail(FLCE_ERR_ARG, "a gradient was requested but grad_student_weight is NULL");
+  if (grads && !grad_student_weight && !grad_student_hidden)
+    return fail(FLCE_ERR_ARG,
+                "a gradient was requested but grad_student_hidden and grad_student_weight are "
+                "both NULL");
   if (grad_student_weight && !aligned(grad_student_weight, 16))
     return fail(FLCE_ERR_ARG, "grad_student_weight not 16-byte aligned");
   if (T > 0) {
-    if (!student_hidden || !student_weight || !teacher_hidden || !teacher_weight || !workspace ||
-        (grads && !grad_student_hidden))
+    if (!student_hidden || !student_weight || !teacher_hidden || !teacher_weight || !workspace)
       return fail(FLCE_ERR_ARG, "a required pointer is NULL");
     if (!aligned(student_hidden, 16) || !aligned(student_weight, 16) ||
         !aligned(teacher_hidden, 16) || !aligned(teacher_weight, 16) ||
         !aligned(workspace, 16) || (labels && !aligned(labels, 8)) ||
         (kl_out && !aligned(kl_out, 4)) || (mean_out && !aligned(mean_out, 4)) ||
         (grad_out && !aligned(grad_out, 4)) || (grad_mean && !aligned(grad_mean, 4)) ||
-        (grads && !aligned(grad_student_hidden, 16)))
+        (grad_student_hidden && !aligned(grad_student_hidden, 16)))
       return fail(FLCE_ERR_ARG, "misaligned pointer");
     if (workspace_bytes < p.total)
       return fail(FLCE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
@@ -462,9 +467,11 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
   hipStream_t s = (hipStream_t)stream;
   if (T == 0) {
     if (mean_out) FLCE_TRY(fill(mean_out, 1, 0.f, s));
-    if (grads && !accumulate_grad_weight) FLCE_TRY(fill(grad_student_weight, V * Ds, 0.f, s));
+    if (grads && grad_student_weight && !accumulate_grad_weight)
+      FLCE_TRY(fill(grad_student_weight, V * Ds, 0.f, s));
     return FLCE_OK;
   }
+  const bool want_dh = grads && grad_student_hidden, want_dw = grads && grad_student_weight;
 
   char *ws = (char *)workspace;
   float *lse_s = (float *)(ws + p.off_lse_s), *lse_t = (float *)(ws + p.off_lse_t);
@@ -571,7 +578,8 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
     const int64_t vc0 = vc * p.Vc;
     const int64_t vcount = std::min<int64_t>(p.Vc, V - vc0);
     return launch_dh_dw(G, (int)(2 * p.Vc), p.Vc, true, student_weight, ht, Ds, V, p.R, rcount,
-                        vc0, vcount, p.dh_splits, dhacc, grad_student_weight, vc > 0,
+                        vc0, vcount, p.dh_splits, want_dh ? dhacc : nullptr,
+                        want_dw ? grad_student_weight : nullptr, vc > 0,
                         accumulate_grad_weight || rb > 0, s);
   };
   const int nparts = (int)(p.n_vc * p.vsplits);
@@ -589,7 +597,7 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
     const int64_t rcount = std::min<int64_t>(p.R, T - rb0);
     if (rcount <= 0) break;
     const int64_t tiles_n = cdiv(rcount, kTile);
-    if (grads) FLCE_TRY(launch_ht(student_hidden, ht, Ds, p.R, rb0, rcount, s));
+    if (want_dw) FLCE_TRY(launch_ht(student_hidden, ht, Ds, p.R, rb0, rcount, s));
     for (int64_t vc = 0; vc < p.n_vc; ++vc) {
       float *pa = part_a + (size_t)vc * p.vsplits * p.R;
       float *pb = part_b + (size_t)vc * p.vsplits * p.R;
@@ -613,7 +621,7 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
         FLCE_TRY(dh_dw(rb, rcount, vc));
       }
     }
-    if (grads)
+    if (want_dh)
       FLCE_TRY(launch_dh_out(dhacc, grad_student_hidden, Ds, p.R, p.dh_splits, rb0, rcount, s));
   }
 
@@ -767,13 +775,16 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
   FLCE_TRY(make_xform(transform, xf, cap));
   if ((grad_out == nullptr) == (grad_mean == nullptr))
     return fail(FLCE_ERR_ARG, "exactly one of grad_out and grad_mean must be given");
-  if (!grad_weight) return fail(FLCE_ERR_ARG, "grad_weight is NULL");
-  if (!aligned(grad_weight, 16)) return fail(FLCE_ERR_ARG, "grad_weight not 16-byte aligned");
+  if (!grad_weight && !grad_hidden)
+    return fail(FLCE_ERR_ARG, "grad_hidden and grad_weight are both NULL: nothing to compute");
+  if (grad_weight && !aligned(grad_weight, 16))
+    return fail(FLCE_ERR_ARG, "grad_weight not 16-byte aligned");
   if (T > 0) {
-    if (!hidden || !weight || !labels || !lse || !grad_hidden || !workspace)
+    if (!hidden || !weight || !labels || !lse || !workspace)
       return fail(FLCE_ERR_ARG, "a required pointer is NULL");
     if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(labels, 8) ||
-        !aligned(lse, 4) || !aligned(grad_hidden, 16) || !aligned(workspace, 16) ||
+        !aligned(lse, 4) || (grad_hidden && !aligned(grad_hidden, 16)) ||
+        !aligned(workspace, 16) ||
         (grad_out && !aligned(grad_out, 4)) || (grad_mean && !aligned(grad_mean, 4)))
       return fail(FLCE_ERR_ARG, "misaligned pointer");
     if (workspace_bytes < p.total)
@@ -782,7 +793,8 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
   }
   FLCE_TRY(check_device());
   hipStream_t s = (hipStream_t)stream;
-  if (T == 0) return accumulate_grad_weight ? FLCE_OK : fill(grad_weight, V * D, 0.f, s);
+  if (T == 0)
+    return (accumulate_grad_weight || !grad_weight) ? FLCE_OK : fill(grad_weight, V * D, 0.f, s);
 
   char *ws = (char *)workspace;
   float *cbuf = (float *)(ws + p.off_c);
@@ -810,7 +822,7 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
     const int64_t rb0 = rb * p.R;
     const int64_t rcount = std::min<int64_t>(p.R, T - rb0);
     if (rcount <= 0) break;
-    FLCE_TRY(launch_ht(hidden, ht, D, p.R, rb0, rcount, s));
+    if (grad_weight) FLCE_TRY(launch_ht(hidden, ht, D, p.R, rb0, rcount, s));
     for (int64_t vc = 0; vc < p.n_vc; ++vc) {
       const int64_t vc0 = vc * p.Vc;
       const int64_t vcount = std::min<int64_t>(p.Vc, V - vc0);
@@ -843,10 +855,11 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
       FLCE_TRY(launched("bwd_grad"));
 
       FLCE_TRY(launch_dh_dw(G, (int)p.Vc, p.Vc, false, weight, ht, D, V, p.R, rcount, vc0, vcount,
-                            p.dh_splits, dhacc, grad_weight, vc > 0,
+                            p.dh_splits, grad_hidden ? dhacc : nullptr, grad_weight, vc > 0,
                             accumulate_grad_weight || rb > 0, s));
     }
-    FLCE_TRY(launch_dh_out(dhacc, grad_hidden, D, p.R, p.dh_splits, rb0, rcount, s));
+    if (grad_hidden)
+      FLCE_TRY(launch_dh_out(dhacc, grad_hidden, D, p.R, p.dh_splits, rb0, rcount, s));
   }
   return FLCE_OK;
 }
@@ -1008,20 +1021,21 @@ flce_status policy_loss(int kind, const PolicyInputs &in, const flce_policy_para
   }
   const bool grads = grad_loss != nullptr;
   if (!loss_out) return fail(FLCE_ERR_ARG, "loss_out is NULL");
-  if (grads && !grad_weight)
-    return fail(FLCE_ERR_ARG, "a gradient was requested but grad_weight is NULL");
+  if (grads && !grad_weight && !grad_hidden)
+    return fail(FLCE_ERR_ARG,
+                "a gradient was requested but grad_hidden and grad_weight are both NULL");
   if (grad_weight && !aligned(grad_weight, 16))
     return fail(FLCE_ERR_ARG, "grad_weight not 16-byte aligned");
   if (!aligned(loss_out, 4) || (grad_loss && !aligned(grad_loss, 4)))
     return fail(FLCE_ERR_ARG, "misaligned pointer");
   if (T > 0) {
     const bool need_seq = kind != kPolicyGrpo;
-    if (!hidden || !weight || !labels || !workspace || (grads && !grad_hidden) ||
+    if (!hidden || !weight || !labels || !workspace ||
         (kind == kPolicyGrpo && !in.advantages) || (need_seq && !in.ref_seq) ||
         (kind == kPolicyKto && !in.desirable))
       return fail(FLCE_ERR_ARG, "a required pointer is NULL");
     if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(labels, 8) ||
-        !aligned(workspace, 16) || (grads && !aligned(grad_hidden, 16)) ||
+        !aligned(workspace, 16) || (grad_hidden && !aligned(grad_hidden, 16)) ||
         (logp_out && !aligned(logp_out, 4)) || (in.advantages && !aligned(in.advantages, 4)) ||
         (in.old_logp && !aligned(in.old_logp, 4)) || (in.ref_logp && !aligned(in.ref_logp, 4)) ||
         (in.ref_seq && !aligned(in.ref_seq, 4)) || (in.kl_ref && !aligned(in.kl_ref, 4)))
@@ -1034,7 +1048,7 @@ flce_status policy_loss(int kind, const PolicyInputs &in, const flce_policy_para
   hipStream_t s = (hipStream_t)stream;
   if (T == 0) {
     FLCE_TRY(fill(loss_out, 1, 0.f, s));
-    if (grads && !accumulate_grad_weight) FLCE_TRY(fill(grad_weight, V * D, 0.f, s));
+    if (grads && grad_weight && !accumulate_grad_weight) FLCE_TRY(fill(grad_weight, V * D, 0.f, s));
     return FLCE_OK;
   }
 

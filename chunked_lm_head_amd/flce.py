@@ -245,8 +245,12 @@ def backward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor,
              chunk_rows: int = 256, mode: str = "nll", transform: Optional[dict] = None,
              grad_hidden: Optional[torch.Tensor] = None,
              grad_weight: Optional[torch.Tensor] = None, accumulate: bool = False,
-             workspace: Optional[torch.Tensor] = None):
-    """(dH [T, D] bf16, dW [V, D] fp32) of the loss given dL/d out (per token) or dL/d mean."""
+             workspace: Optional[torch.Tensor] = None, need_hidden: bool = True,
+             need_weight: bool = True):
+    """(dH [T, D] bf16, dW [V, D] fp32) of the loss given dL/d out (per token) or dL/d mean.
+
+    ``need_hidden=False`` / ``need_weight=False`` skip that gradient (returned as None;
+    e.g. a frozen lm_head skips the dW products)."""
     _validate(hidden, weight, labels)
     T, D = hidden.shape
     V = weight.shape[0]
@@ -258,14 +262,22 @@ def backward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor,
         _check_buffer("grad_out", grad_out, torch.float32, (T,), dev)
     if grad_mean is not None:
         _check_buffer("grad_mean", grad_mean, torch.float32, (), dev)
-    if grad_hidden is None:
+    if not (need_hidden or need_weight):
+        raise ValueError("nothing to compute: need_hidden and need_weight are both False")
+    if not need_hidden:
+        grad_hidden = None
+    elif grad_hidden is None:
         grad_hidden = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
-    if grad_weight is None:
+    if not need_weight:
+        grad_weight = None
+    elif grad_weight is None:
         if accumulate:
             raise ValueError("accumulate needs an existing grad_weight")
         grad_weight = torch.empty((V, D), dtype=torch.float32, device=dev)
-    _check_buffer("grad_hidden", grad_hidden, torch.bfloat16, (T, D), dev)
-    _check_buffer("grad_weight", grad_weight, torch.float32, (V, D), dev)
+    if grad_hidden is not None:
+        _check_buffer("grad_hidden", grad_hidden, torch.bfloat16, (T, D), dev)
+    if grad_weight is not None:
+        _check_buffer("grad_weight", grad_weight, torch.float32, (V, D), dev)
     if workspace is None:
         workspace = alloc_workspace(T, D, V, chunk_rows, dev)
     _check_workspace(workspace, workspace_bytes(T, D, V, chunk_rows), dev)
@@ -315,11 +327,16 @@ class _ChunkedLinearCE(torch.autograd.Function):
             del ctx.hidden_host
         else:
             hidden, weight, labels, lse = ctx.saved_tensors
+        need_h, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        if not (need_h or need_w):
+            return (None,) * 9
         g = grad.float().contiguous()
         kw = dict(grad_mean=g.reshape(())) if reduction == "mean" else dict(grad_out=g)
         dh, dw = backward(hidden, weight, labels, lse, ignore_index=ignore_index,
-                          chunk_rows=chunk_rows, mode=mode, transform=transform, **kw)
-        return dh, dw.to(weight.dtype), None, None, None, None, None, None, None
+                          chunk_rows=chunk_rows, mode=mode, transform=transform,
+                          need_hidden=need_h, need_weight=need_w, **kw)
+        return (dh, None if dw is None else dw.to(weight.dtype), None, None, None, None, None,
+                None, None)
 
 
 def _transform_kwargs(logit_scale_multiply, logit_scale_divide, logit_softcapping, temperature):
@@ -406,11 +423,12 @@ def distill(student_hidden, student_weight, teacher_hidden, teacher_weight,
             grad_hidden: Optional[torch.Tensor] = None,
             grad_weight: Optional[torch.Tensor] = None, accumulate: bool = False,
             workspace: Optional[torch.Tensor] = None, kl: Optional[torch.Tensor] = None,
-            mean: Optional[torch.Tensor] = None, divergence: str = "kl", beta: float = 0.5):
+            mean: Optional[torch.Tensor] = None, divergence: str = "kl", beta: float = 0.5,
+            need_hidden: bool = True, need_weight: bool = True):
     """(kl [T], mean [], dHs or None, dWs or None): per-token KL(teacher || student)
     (``divergence="jsd"``: the generalized JSD with weight ``beta``), its mean over
     kept tokens and, when grad_out or grad_mean is given, the student's gradients
-    (one call; the teacher gets none)."""
+    (one call; the teacher gets none; ``need_hidden`` / ``need_weight`` False skip one)."""
     if divergence not in ("kl", "jsd"):
         raise ValueError(f"divergence {divergence!r} is neither 'kl' nor 'jsd'")
     for t in (student_hidden, student_weight, teacher_hidden, teacher_weight):
@@ -438,14 +456,24 @@ def distill(student_hidden, student_weight, teacher_hidden, teacher_weight,
     _check_buffer("kl", kl, torch.float32, (T,), dev)
     _check_buffer("mean", mean, torch.float32, (), dev)
     if grads:
-        if grad_hidden is None:
+        if not (need_hidden or need_weight):
+            raise ValueError("nothing to compute: need_hidden and need_weight are both False")
+        if not need_hidden:
+            grad_hidden = None
+        elif grad_hidden is None:
             grad_hidden = torch.empty((T, Ds), dtype=torch.bfloat16, device=dev)
-        if grad_weight is None:
+        if not need_weight:
+            grad_weight = None
+        elif grad_weight is None:
             if accumulate:
                 raise ValueError("accumulate needs an existing grad_weight")
             grad_weight = torch.empty((V, Ds), dtype=torch.float32, device=dev)
-        _check_buffer("grad_hidden", grad_hidden, torch.bfloat16, (T, Ds), dev)
-        _check_buffer("grad_weight", grad_weight, torch.float32, (V, Ds), dev)
+        if grad_hidden is not None:
+            _check_buffer("grad_hidden", grad_hidden, torch.bfloat16, (T, Ds), dev)
+        if grad_weight is not None:
+            _check_buffer("grad_weight", grad_weight, torch.float32, (V, Ds), dev)
+    else:
+        grad_hidden = grad_weight = None
     need = distill_workspace_bytes(T, Ds, Dt, V, chunk_rows)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -453,58 +481,48 @@ def distill(student_hidden, student_weight, teacher_hidden, teacher_weight,
     head = (_ptr(student_hidden), _ptr(student_weight), Ds, _ptr(teacher_hidden),
             _ptr(teacher_weight), Dt, _ptr(labels), ignore_index, T, V, chunk_rows,
             make_transform(**(transform or {})))
-    tail = (_ptr(kl), _ptr(mean), _ptr(grad_out), _ptr(grad_mean),
-            _ptr(grad_hidden) if grads else None, _ptr(grad_weight) if grads else None,
-            1 if accumulate else 0, _ptr(workspace), workspace.numel(), _stream(dev))
+    tail = (_ptr(kl), _ptr(mean), _ptr(grad_out), _ptr(grad_mean), _ptr(grad_hidden),
+            _ptr(grad_weight), 1 if accumulate else 0, _ptr(workspace), workspace.numel(),
+            _stream(dev))
     if divergence == "kl":
         _check(lib.flce_distill(*head, *tail))
     else:
         _check(lib.flce_distill_jsd(*head, float(beta), *tail))
-    return kl, mean, (grad_hidden if grads else None), (grad_weight if grads else None)
+    return kl, mean, grad_hidden, grad_weight
 
 
 class _ChunkedDistillKL(torch.autograd.Function):
     """Mean (``reduction="mean"``) or per-token (``"none"``) KL(teacher || student), or
     the generalized JSD.
 
-    The mean's gradients are computed in the forward call (c = 1 / N_kept), which
-    saves a second recompute, and scaled by the upstream scalar in the backward
-    (two elementwise products in PyTorch; dH is rounded to bf16 once more);
-    per-token reduction calls the library again in the backward with the
-    upstream gradient (recompute)."""
+    The forward call computes the divergence only; the backward calls the library
+    again with the upstream gradient (dL/d mean as ``grad_mean``, or dL/d kl_t as
+    ``grad_out``), which recomputes both heads' logits and applies it in the
+    kernels, so the student's gradients are rounded once."""
 
     @staticmethod
     def forward(ctx, s_hidden, s_weight, t_hidden, t_weight, labels, ignore_index, chunk_rows,
                 reduction, transform, divergence="kl", beta=0.5):
         kw = dict(ignore_index=ignore_index, chunk_rows=chunk_rows, transform=transform,
                   divergence=divergence, beta=beta)
-        need = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
-        if reduction == "mean" and need:
-            one = torch.ones((), dtype=torch.float32, device=s_hidden.device)
-            kl, mean, dh, dw = distill(s_hidden, s_weight, t_hidden, t_weight, labels,
-                                       grad_mean=one, **kw)
-            ctx.save_for_backward(dh, dw)
-        else:
-            kl, mean, _, _ = distill(s_hidden, s_weight, t_hidden, t_weight, labels, **kw)
-            ctx.save_for_backward(s_hidden, s_weight, t_hidden, t_weight, labels)
-        ctx.cfg = (reduction, kw, need)
+        kl, mean, _, _ = distill(s_hidden, s_weight, t_hidden, t_weight, labels, **kw)
+        ctx.save_for_backward(s_hidden, s_weight, t_hidden, t_weight, labels)
+        ctx.cfg = (reduction, kw)
         return mean if reduction == "mean" else kl
 
     @staticmethod
     def backward(ctx, grad):
-        reduction, kw, need = ctx.cfg
-        if not need:
+        reduction, kw = ctx.cfg
+        need_h, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        if not (need_h or need_w):
             return (None,) * 11
-        if reduction == "mean":
-            dh, dw = ctx.saved_tensors
-            g = grad.float()
-            dh = (dh.float() * g).to(torch.bfloat16)
-            dw = dw * g
-        else:
-            s_hidden, s_weight, t_hidden, t_weight, labels = ctx.saved_tensors
-            _, _, dh, dw = distill(s_hidden, s_weight, t_hidden, t_weight, labels,
-                                   grad_out=grad.float().contiguous(), **kw)
-        return dh, dw.to(torch.bfloat16), None, None, None, None, None, None, None, None, None
+        s_hidden, s_weight, t_hidden, t_weight, labels = ctx.saved_tensors
+        g = grad.float().contiguous()
+        gkw = dict(grad_mean=g.reshape(())) if reduction == "mean" else dict(grad_out=g)
+        _, _, dh, dw = distill(s_hidden, s_weight, t_hidden, t_weight, labels,
+                               need_hidden=need_h, need_weight=need_w, **gkw, **kw)
+        return (dh, None if dw is None else dw.to(s_weight.dtype), None, None, None, None, None,
+                None, None, None, None)
 
 
 def chunked_distill_kl(student_hidden, student_weight, teacher_hidden, teacher_weight,
@@ -543,7 +561,8 @@ def _f32_input(name, t, shape, dev, optional=True):
 
 
 def _policy(kind, hidden, weight, labels, n_seq, extra, params, *, ignore_index, chunk_rows,
-            transform, grad_loss, grad_hidden, grad_weight, accumulate, workspace, loss, logp):
+            transform, grad_loss, grad_hidden, grad_weight, accumulate, workspace, loss, logp,
+            need_hidden=True, need_weight=True):
     _validate(hidden, weight, labels)
     T, D = hidden.shape
     V = weight.shape[0]
@@ -555,14 +574,24 @@ def _policy(kind, hidden, weight, labels, n_seq, extra, params, *, ignore_index,
     grads = grad_loss is not None
     if grads:
         _check_buffer("grad_loss", grad_loss, torch.float32, (), dev)
-        if grad_hidden is None:
+        if not (need_hidden or need_weight):
+            raise ValueError("nothing to compute: need_hidden and need_weight are both False")
+        if not need_hidden:
+            grad_hidden = None
+        elif grad_hidden is None:
             grad_hidden = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
-        if grad_weight is None:
+        if not need_weight:
+            grad_weight = None
+        elif grad_weight is None:
             if accumulate:
                 raise ValueError("accumulate needs an existing grad_weight")
             grad_weight = torch.empty((V, D), dtype=torch.float32, device=dev)
-        _check_buffer("grad_hidden", grad_hidden, torch.bfloat16, (T, D), dev)
-        _check_buffer("grad_weight", grad_weight, torch.float32, (V, D), dev)
+        if grad_hidden is not None:
+            _check_buffer("grad_hidden", grad_hidden, torch.bfloat16, (T, D), dev)
+        if grad_weight is not None:
+            _check_buffer("grad_weight", grad_weight, torch.float32, (V, D), dev)
+    else:
+        grad_hidden = grad_weight = None
     need = policy_workspace_bytes(T, D, V, chunk_rows, n_seq)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -570,17 +599,16 @@ def _policy(kind, hidden, weight, labels, n_seq, extra, params, *, ignore_index,
     fn = {"grpo": lib.flce_grpo_loss, "dpo": lib.flce_dpo_loss, "kto": lib.flce_kto_loss}[kind]
     _check(fn(_ptr(hidden), _ptr(weight), _ptr(labels), ignore_index, T, D, V, chunk_rows,
               make_transform(**(transform or {})), n_seq, *extra, ctypes.byref(params),
-              _ptr(loss), _ptr(logp), _ptr(grad_loss),
-              _ptr(grad_hidden) if grads else None, _ptr(grad_weight) if grads else None,
+              _ptr(loss), _ptr(logp), _ptr(grad_loss), _ptr(grad_hidden), _ptr(grad_weight),
               1 if accumulate else 0, _ptr(workspace), workspace.numel(), _stream(dev)))
-    return loss, logp, (grad_hidden if grads else None), (grad_weight if grads else None)
+    return loss, logp, grad_hidden, grad_weight
 
 
 def grpo_loss(hidden, weight, labels, n_seq: int, advantages, *, old_logp=None, ref_logp=None,
               beta: float = 0.0, eps_low: float = 0.2, eps_high: float = 0.2,
               ignore_index: int = -100, chunk_rows: int = 256, transform=None,
               grad_loss=None, grad_hidden=None, grad_weight=None, accumulate=False,
-              workspace=None, loss=None, logp=None):
+              workspace=None, loss=None, logp=None, need_hidden=True, need_weight=True):
     """GRPO loss over n_seq sequences of the flattened batch (``flce_grpo_loss``):
     (loss [], logp [T] or None, dH or None, dW or None)."""
     T = hidden.shape[0]
@@ -592,13 +620,14 @@ def grpo_loss(hidden, weight, labels, n_seq: int, advantages, *, old_logp=None, 
     return _policy("grpo", hidden, weight, labels, n_seq, extra, prm, ignore_index=ignore_index,
                    chunk_rows=chunk_rows, transform=transform, grad_loss=grad_loss,
                    grad_hidden=grad_hidden, grad_weight=grad_weight, accumulate=accumulate,
-                   workspace=workspace, loss=loss, logp=logp)
+                   workspace=workspace, loss=loss, logp=logp, need_hidden=need_hidden,
+                   need_weight=need_weight)
 
 
 def dpo_loss(hidden, weight, labels, n_seq: int, ref_seq_logp, *, beta: float = 0.1,
              ignore_index: int = -100, chunk_rows: int = 256, transform=None, grad_loss=None,
              grad_hidden=None, grad_weight=None, accumulate=False, workspace=None, loss=None,
-             logp=None):
+             logp=None, need_hidden=True, need_weight=True):
     """DPO loss; sequences [0, n_seq/2) chosen, [n_seq/2, n_seq) rejected (``flce_dpo_loss``)."""
     dev = hidden.device
     extra = (_ptr(_f32_input("ref_seq_logp", ref_seq_logp, (n_seq,), dev, optional=False)),)
@@ -606,14 +635,15 @@ def dpo_loss(hidden, weight, labels, n_seq: int, ref_seq_logp, *, beta: float = 
     return _policy("dpo", hidden, weight, labels, n_seq, extra, prm, ignore_index=ignore_index,
                    chunk_rows=chunk_rows, transform=transform, grad_loss=grad_loss,
                    grad_hidden=grad_hidden, grad_weight=grad_weight, accumulate=accumulate,
-                   workspace=workspace, loss=loss, logp=logp)
+                   workspace=workspace, loss=loss, logp=logp, need_hidden=need_hidden,
+                   need_weight=need_weight)
 
 
 def kto_loss(hidden, weight, labels, n_seq: int, ref_seq_logp, desirable, *, kl_ref=None,
              beta: float = 0.1, desirable_weight: float = 1.0, undesirable_weight: float = 1.0,
              ignore_index: int = -100, chunk_rows: int = 256, transform=None, grad_loss=None,
              grad_hidden=None, grad_weight=None, accumulate=False, workspace=None, loss=None,
-             logp=None):
+             logp=None, need_hidden=True, need_weight=True):
     """KTO loss with the reference point kl_ref (device scalar, clamped at 0; None = 0)
     (``flce_kto_loss``)."""
     dev = hidden.device
@@ -624,49 +654,52 @@ def kto_loss(hidden, weight, labels, n_seq: int, ref_seq_logp, desirable, *, kl_
     return _policy("kto", hidden, weight, labels, n_seq, extra, prm, ignore_index=ignore_index,
                    chunk_rows=chunk_rows, transform=transform, grad_loss=grad_loss,
                    grad_hidden=grad_hidden, grad_weight=grad_weight, accumulate=accumulate,
-                   workspace=workspace, loss=loss, logp=logp)
+                   workspace=workspace, loss=loss, logp=logp, need_hidden=need_hidden,
+                   need_weight=need_weight)
 
 
 class _PolicyLossFn(torch.autograd.Function):
     """A policy loss as a scalar of the policy's hidden states and lm_head.
 
-    The library call computes the loss and, with an upstream scalar of 1, its
-    gradients in one pass (the log-prob forward, the loss kernels and the
-    recomputing backward); the backward multiplies them by the upstream scalar
-    (two elementwise products in PyTorch; dH is rounded to bf16 once more)."""
+    The forward call computes the loss only; the backward calls the library again
+    with the upstream scalar as ``grad_loss`` (the log-prob forward, the loss
+    kernels and the recomputing backward), so the kernels apply it and dH is
+    rounded once."""
 
     @staticmethod
     def forward(ctx, hidden, weight, call):
-        need = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
-        one = torch.ones((), dtype=torch.float32, device=hidden.device)
-        loss, _, dh, dw = call(hidden, weight, one if need else None)
-        if need:
-            ctx.save_for_backward(dh, dw)
-        ctx.need = need
+        loss, _, _, _ = call(hidden, weight, None, True, True)
+        ctx.save_for_backward(hidden, weight)
+        ctx.call = call
         return loss
 
     @staticmethod
     def backward(ctx, grad):
-        if not ctx.need:
+        need_h, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        if not (need_h or need_w):
             return None, None, None
-        dh, dw = ctx.saved_tensors
-        g = grad.float()
-        return (dh.float() * g).to(torch.bfloat16), (dw * g).to(torch.bfloat16), None
+        hidden, weight = ctx.saved_tensors
+        _, _, dh, dw = ctx.call(hidden, weight, grad.float().reshape(()).contiguous(), need_h,
+                                need_w)
+        return dh, None if dw is None else dw.to(weight.dtype), None
 
 
 def grpo_loss_fn(hidden, weight, labels, n_seq: int, advantages, **kw):
     """Autograd-aware ``grpo_loss`` (keyword arguments as there, without the gradient ones)."""
-    return _PolicyLossFn.apply(hidden, weight, lambda h, w, gl: grpo_loss(
-        h.detach(), w.detach(), labels, n_seq, advantages, grad_loss=gl, **kw))
+    return _PolicyLossFn.apply(hidden, weight, lambda h, w, gl, nh, nw: grpo_loss(
+        h.detach(), w.detach(), labels, n_seq, advantages, grad_loss=gl, need_hidden=nh,
+        need_weight=nw, **kw))
 
 
 def dpo_loss_fn(hidden, weight, labels, n_seq: int, ref_seq_logp, **kw):
     """Autograd-aware ``dpo_loss``."""
-    return _PolicyLossFn.apply(hidden, weight, lambda h, w, gl: dpo_loss(
-        h.detach(), w.detach(), labels, n_seq, ref_seq_logp, grad_loss=gl, **kw))
+    return _PolicyLossFn.apply(hidden, weight, lambda h, w, gl, nh, nw: dpo_loss(
+        h.detach(), w.detach(), labels, n_seq, ref_seq_logp, grad_loss=gl, need_hidden=nh,
+        need_weight=nw, **kw))
 
 
 def kto_loss_fn(hidden, weight, labels, n_seq: int, ref_seq_logp, desirable, **kw):
     """Autograd-aware ``kto_loss``."""
-    return _PolicyLossFn.apply(hidden, weight, lambda h, w, gl: kto_loss(
-        h.detach(), w.detach(), labels, n_seq, ref_seq_logp, desirable, grad_loss=gl, **kw))
+    return _PolicyLossFn.apply(hidden, weight, lambda h, w, gl, nh, nw: kto_loss(
+        h.detach(), w.detach(), labels, n_seq, ref_seq_logp, desirable, grad_loss=gl,
+        need_hidden=nh, need_weight=nw, **kw))

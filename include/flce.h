@@ -99,12 +99,14 @@ typedef struct flce_logit_transform {
 
 /*
  * Bytes of device workspace that flce_forward and flce_backward need for this
- * shape (one size serves both).  It is bounded by the logit memory of one
- * chunk, chunk_rows x V x 4 bytes (the fp32 chunk logits of the pages'
- * Equation 3), plus terms linear in T and in D, and does not grow with T x V:
- * the backward stages the softmax gradient of a block of rows in bf16 within
- * that bound.  The minimum is one 256 x 256 bf16 tile.  Returns 0 when the
- * arguments are invalid (same rules as the entry points) or overflow.
+ * shape (one size serves both).  It does not grow with T x V.  The backward
+ * stages the softmax gradient of a block of R rows x Vc vocabulary entries in
+ * bf16, R * Vc * 2 <= chunk_rows * V * 4 bytes (the fp32 logits of one chunk,
+ * the pages' Equation 3; at least one 256 x 256 tile), next to the fp32 dH
+ * sums of the row block (R * D * 4 per split of the vocabulary chunk), a bf16
+ * copy of the row block's hidden states transposed (R * D * 2) and O(T)
+ * per-token values; R <= 8192.  Returns 0 when the arguments are invalid
+ * (same rules as the entry points) or overflow.
  */
 size_t flce_workspace_bytes(int64_t T, int64_t D, int64_t V, int64_t chunk_rows);
 
@@ -137,9 +139,11 @@ flce_status flce_forward(const void *hidden, const void *weight, const int64_t *
  * s = +1 for FLCE_MODE_NLL and -1 for FLCE_MODE_LOGPROB, c_t = 0 for ignored
  * (and out-of-range) labels, N_valid = number of tokens whose label is not
  * ignore_index (c_t = 0 for all t if N_valid == 0).  Exactly one of grad_out
- * and grad_mean must be non-NULL.  lse must be the forward's output for the
- * same inputs and transform.  T == 0 is valid: grad_weight is zeroed unless
- * accumulating.
+ * and grad_mean must be non-NULL.  Either gradient output may be NULL: a NULL
+ * grad_hidden skips the dH products, a NULL grad_weight skips the dW products
+ * (a frozen lm_head); both NULL is FLCE_ERR_ARG.  lse must be the forward's
+ * output for the same inputs and transform.  T == 0 is valid: grad_weight (if
+ * given) is zeroed unless accumulating.
  */
 flce_status flce_backward(const void *hidden, const void *weight, const int64_t *labels,
                           const float *lse, int64_t T, int64_t D, int64_t V,
@@ -170,8 +174,9 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
  * keeps every token.  Outputs (each optional): kl_out [T] fp32, *mean_out =
  * mean of kl over kept tokens (0 if none).  Gradients are computed when
  * grad_out (dL/d kl_t, [T]) or grad_mean (dL/d mean, device scalar) is given
- * (at most one): c_t = grad_out[t], or *grad_mean / N_kept; grad_student_hidden
- * and grad_student_weight must then be non-NULL.  The forward values and the
+ * (at most one): c_t = grad_out[t], or *grad_mean / N_kept; at least one of
+ * grad_student_hidden and grad_student_weight must then be non-NULL (a NULL one
+ * is not computed).  The forward values and the
  * gradients come from one call: the logits of both heads are recomputed per
  * block (the two log-sum-exps first), nothing of size T x V is stored, and
  * the workspace is bounded like that of the cross-entropy path.  T == 0 is
@@ -251,7 +256,8 @@ flce_status flce_distill_jsd(const void *student_hidden, const void *student_wei
  * the per-token log-probs, 0 off the completions).  If grad_loss (device scalar
  * dTotal/dL) is given, grad_hidden [T x D] bf16 and grad_weight [V x D] fp32
  * (added if accumulate_grad_weight) receive grad_loss * dL/dH and dL/dW through
- * the log-prob backward (recompute), with grad_out_t = grad_loss * dL/dlogp_t.
+ * the log-prob backward (recompute), with grad_out_t = grad_loss * dL/dlogp_t;
+ * either may be NULL (not computed), not both.
  * At a clipping kink GRPO takes the unclipped derivative.  Errors: n_seq must
  * divide T (FLCE_ERR_SHAPE), DPO needs an even n_seq, parameters out of range
  * give FLCE_ERR_ARG; otherwise the conventions of flce_forward (T == 0 gives

@@ -71,8 +71,9 @@ def test_backward_rejects_before_launch(flce):
     assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, None, None, None, 16, 16, 0, 16, 1 << 30, None) == 1
     # both given
     assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, None, 4, 4, 16, 16, 0, 16, 1 << 30, None) == 1
-    # grad_weight missing
-    assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, None, 4, None, 16, None, 0, 16, 1 << 30, None) == 1
+    # neither gradient output given (either alone is allowed: the other is skipped)
+    assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, None, 4, None, None, None, 0, 16, 1 << 30, None) == 1
+    assert b"both NULL" in flce.lib.flce_last_error()
     # tiny workspace
     assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, None, 4, None, 16, 16, 0, 16, 8, None) == 3
 
@@ -153,8 +154,8 @@ def test_distill_rejects_before_launch(flce):
     assert _dst(flce, Ds=60) == 4                    # student hidden not a multiple of 8
     assert _dst(flce, Dt=12) == 4                    # teacher hidden not a multiple of 8
     assert _dst(flce, gout=4, gmean=4, gh=16, gw=16) == 1   # both upstream grads
-    assert _dst(flce, gmean=4, gh=16) == 1           # gradient without grad_student_weight
-    assert _dst(flce, gmean=4, gw=16) == 1           # gradient without grad_student_hidden
+    assert _dst(flce, gmean=4) == 1                  # gradient with neither output
+    assert b"both NULL" in flce.lib.flce_last_error()
     assert _dst(flce, th=0) == 1
     assert _dst(flce, tw=8) == 1                     # misaligned
     assert _dst(flce, wsb=16) == 3
@@ -206,8 +207,8 @@ def test_policy_rejects_before_launch(flce, kind):
     assert _pol(flce, kind, D=60) == 4
     assert _pol(flce, kind, prm=None) == 1
     assert _pol(flce, kind, loss=None) == 1
-    assert _pol(flce, kind, gl=4, gh=16) == 1        # gradient without grad_weight
-    assert _pol(flce, kind, gl=4, gw=16) == 1        # gradient without grad_hidden
+    assert _pol(flce, kind, gl=4) == 1               # gradient with neither output
+    assert b"both NULL" in flce.lib.flce_last_error()
     assert _pol(flce, kind, h=None) == 1
     assert _pol(flce, kind, h=8) == 1                # misaligned
     assert _pol(flce, kind, wsb=16) == 3
@@ -255,6 +256,6 @@ def test_distill_jsd_rejects_before_launch(flce):
         assert call(beta) == 1, beta                  # the weight must lie in (0, 1)
     assert call(0.5, T=-1) == 2
     assert call(0.5, Ds=60) == 4
-    assert call(0.5, gmean=4, gh=16) == 1            # gradient without grad_student_weight
+    assert call(0.5, gmean=4) == 1                   # gradient with neither output
     assert call(0.5, tw=8) == 1                      # misaligned
     assert call(0.5, wsb=16) == 3
