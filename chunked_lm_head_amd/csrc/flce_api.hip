@@ -56,6 +56,7 @@ constexpr int64_t kDhTargetWG = 512;
 constexpr int64_t kCUs = 256;  // compute units of an MI355X (8 XCDs of 32)
 constexpr int64_t kDhPartialCap = (int64_t)128 << 20;  // bytes of split-K partial sums
 constexpr int64_t kI32Bytes = ((int64_t)1 << 31) - 1;
+constexpr size_t kScratchBytes = FLCE_FORWARD_SCRATCH_BYTES;  // flce_forward_noalloc's array
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -646,71 +647,35 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
   return FLCE_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t flce_workspace_bytes(int64_t T, int64_t D, int64_t V, int64_t chunk_rows) {
-  Plan p;
-  if (make_plan(T, D, V, chunk_rows, p) != FLCE_OK) return 0;
-  return p.total;
-}
-
-flce_status flce_describe_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows,
-                               int64_t *info) {
-  if (!info) return fail(FLCE_ERR_ARG, "info is NULL");
-  Plan p;
-  FLCE_TRY(make_plan(T, D, V, chunk_rows, p));
-  const int64_t v[12] = {p.n_tt, p.n_vt, p.splits, p.R, p.n_rb, p.Vc, p.n_vc, p.dh_splits,
-                         (int64_t)p.fwd_bytes, (int64_t)p.bwd_bytes, (int64_t)p.gtile_bytes,
-                         (int64_t)p.chunk_bound};
-  memcpy(info, v, sizeof(v));
-  return FLCE_OK;
-}
-
-const char *flce_status_string(int status) {
-  switch (status) {
-    case FLCE_OK: return "ok";
-    case FLCE_ERR_ARG: return "invalid argument (pointer, alignment or mode)";
-    case FLCE_ERR_SHAPE: return "invalid or too large shape";
-    case FLCE_ERR_WORKSPACE: return "workspace too small";
-    case FLCE_ERR_UNSUPPORTED: return "unsupported shape or device";
-    case FLCE_ERR_HIP: return "HIP runtime error";
-    default: return "unknown status";
-  }
-}
-
-const char *flce_last_error(void) { return g_last_error; }
-
-flce_status flce_forward(const void *hidden, const void *weight, const int64_t *labels,
-                         int64_t T, int64_t D, int64_t V, int64_t ignore_index,
-                         int64_t chunk_rows, int mode, const flce_logit_transform *transform,
-                         float *out, float *lse, float *mean_out,
-                         void *workspace, size_t workspace_bytes, void *stream) {
-  g_last_error[0] = 0;
-  Plan p;
+// Argument checks shared by the two forward entry points (everything but the
+// workspace), and the plan and transform they run with.
+flce_status forward_checks(const void *hidden, const void *weight, const int64_t *labels,
+                           int64_t T, int64_t D, int64_t V, int64_t chunk_rows, int mode,
+                           const flce_logit_transform *transform, const float *out,
+                           const float *lse, const float *mean_out, Plan &p, Xform &xf,
+                           bool &cap) {
   FLCE_TRY(make_plan(T, D, V, chunk_rows, p));
   if (mode != FLCE_MODE_NLL && mode != FLCE_MODE_LOGPROB)
     return fail(FLCE_ERR_ARG, "mode %d is neither NLL (0) nor LOGPROB (1)", mode);
-  Xform xf;
-  bool cap;
   FLCE_TRY(make_xform(transform, xf, cap));
   if (T > 0) {
-    if (!hidden || !weight || !labels || !out || !lse || !workspace)
+    if (!hidden || !weight || !labels || !out || !lse)
       return fail(FLCE_ERR_ARG, "a required pointer is NULL");
     if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(labels, 8) ||
-        !aligned(out, 4) || !aligned(lse, 4) || !aligned(workspace, 16) ||
-        (mean_out && !aligned(mean_out, 4)))
+        !aligned(out, 4) || !aligned(lse, 4) || (mean_out && !aligned(mean_out, 4)))
       return fail(FLCE_ERR_ARG, "misaligned pointer (hidden/weight/workspace need 16 bytes)");
-    if (workspace_bytes < p.total)
-      return fail(FLCE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
-                  p.total);
   }
-  FLCE_TRY(check_device());
-  hipStream_t s = (hipStream_t)stream;
+  return FLCE_OK;
+}
+
+// The forward's launches with its partial results at ws (p.fwd_bytes bytes).
+flce_status forward_launch(const Plan &p, const Xform &xf, bool cap, const void *hidden,
+                           const void *weight, const int64_t *labels, int64_t ignore_index,
+                           int mode, float *out, float *lse, float *mean_out, char *ws,
+                           hipStream_t s) {
+  const int64_t T = p.T, D = p.D, V = p.V;
   if (T == 0) return mean_out ? fill(mean_out, 1, 0.f, s) : FLCE_OK;
 
-  char *ws = (char *)workspace;
   FwdLseParams a;
   a.hidden = (const uint16_t *)hidden;
   a.weight = (const uint16_t *)weight;
@@ -756,6 +721,118 @@ flce_status flce_forward(const void *hidden, const void *weight, const int64_t *
     FLCE_TRY(launched("fwd_mean"));
   }
   return FLCE_OK;
+}
+
+}  // namespace
+
+// Scratch of flce_forward_noalloc: the forward's partial results, for callers
+// that cannot allocate.  One copy per GPU, reserved when the library's code is
+// loaded on that GPU and kept until the process ends.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// Device address of `scratch` on the current device.  Host code must never use
+// the array's name as an address (it is a host-side stand-in); the address is
+// asked of the runtime once per device, with that device current, and kept.
+flce_status scratch_address(char **out) {
+  static std::atomic<void *> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FLCE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(FLCE_ERR_UNSUPPORTED, "device index %d", dev);
+  void *ptr = cache[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(FLCE_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    cache[dev].store(ptr, std::memory_order_release);
+  }
+  *out = (char *)ptr;
+  return FLCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t flce_workspace_bytes(int64_t T, int64_t D, int64_t V, int64_t chunk_rows) {
+  Plan p;
+  if (make_plan(T, D, V, chunk_rows, p) != FLCE_OK) return 0;
+  return p.total;
+}
+
+flce_status flce_describe_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows,
+                               int64_t *info) {
+  if (!info) return fail(FLCE_ERR_ARG, "info is NULL");
+  Plan p;
+  FLCE_TRY(make_plan(T, D, V, chunk_rows, p));
+  const int64_t v[12] = {p.n_tt, p.n_vt, p.splits, p.R, p.n_rb, p.Vc, p.n_vc, p.dh_splits,
+                         (int64_t)p.fwd_bytes, (int64_t)p.bwd_bytes, (int64_t)p.gtile_bytes,
+                         (int64_t)p.chunk_bound};
+  memcpy(info, v, sizeof(v));
+  return FLCE_OK;
+}
+
+const char *flce_status_string(int status) {
+  switch (status) {
+    case FLCE_OK: return "ok";
+    case FLCE_ERR_ARG: return "invalid argument (pointer, alignment or mode)";
+    case FLCE_ERR_SHAPE: return "invalid or too large shape";
+    case FLCE_ERR_WORKSPACE: return "workspace too small";
+    case FLCE_ERR_UNSUPPORTED: return "unsupported shape or device";
+    case FLCE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *flce_last_error(void) { return g_last_error; }
+
+flce_status flce_forward(const void *hidden, const void *weight, const int64_t *labels,
+                         int64_t T, int64_t D, int64_t V, int64_t ignore_index,
+                         int64_t chunk_rows, int mode, const flce_logit_transform *transform,
+                         float *out, float *lse, float *mean_out,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+  g_last_error[0] = 0;
+  Plan p;
+  Xform xf;
+  bool cap;
+  FLCE_TRY(forward_checks(hidden, weight, labels, T, D, V, chunk_rows, mode, transform, out,
+                          lse, mean_out, p, xf, cap));
+  if (T > 0) {
+    if (!workspace) return fail(FLCE_ERR_ARG, "a required pointer is NULL");
+    if (!aligned(workspace, 16))
+      return fail(FLCE_ERR_ARG, "misaligned pointer (hidden/weight/workspace need 16 bytes)");
+    if (workspace_bytes < p.total)
+      return fail(FLCE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
+                  p.total);
+  }
+  FLCE_TRY(check_device());
+  return forward_launch(p, xf, cap, hidden, weight, labels, ignore_index, mode, out, lse,
+                        mean_out, (char *)workspace, (hipStream_t)stream);
+}
+
+flce_status flce_forward_noalloc(const void *hidden, const void *weight, const int64_t *labels,
+                                 int64_t T, int64_t D, int64_t V, int64_t ignore_index,
+                                 int64_t chunk_rows, int mode,
+                                 const flce_logit_transform *transform, float *out, float *lse,
+                                 float *mean_out, void *stream) {
+  g_last_error[0] = 0;
+  Plan p;
+  Xform xf;
+  bool cap;
+  FLCE_TRY(forward_checks(hidden, weight, labels, T, D, V, chunk_rows, mode, transform, out,
+                          lse, mean_out, p, xf, cap));
+  if (T > 0 && p.fwd_bytes > kScratchBytes)
+    return fail(FLCE_ERR_WORKSPACE,
+                "the forward needs %zu bytes of scratch for T = %lld, more than the %zu bytes "
+                "of the library's fixed array (use flce_forward with a workspace)",
+                p.fwd_bytes, (long long)T, kScratchBytes);
+  FLCE_TRY(check_device());
+  char *ws = nullptr;
+  if (T > 0) FLCE_TRY(scratch_address(&ws));
+  return forward_launch(p, xf, cap, hidden, weight, labels, ignore_index, mode, out, lse,
+                        mean_out, ws, (hipStream_t)stream);
 }
 
 flce_status flce_backward(const void *hidden, const void *weight, const int64_t *labels,

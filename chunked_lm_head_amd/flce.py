@@ -31,7 +31,8 @@ STATUS = {0: "FLCE_OK", 1: "FLCE_ERR_ARG", 2: "FLCE_ERR_SHAPE", 3: "FLCE_ERR_WOR
 EXPORTS = ("flce_workspace_bytes", "flce_forward", "flce_backward", "flce_describe_plan",
            "flce_status_string", "flce_last_error", "flce_distill_workspace_bytes",
            "flce_distill", "flce_chunk_rows_for", "flce_tune", "flce_policy_workspace_bytes",
-           "flce_grpo_loss", "flce_dpo_loss", "flce_kto_loss", "flce_distill_jsd")
+           "flce_grpo_loss", "flce_dpo_loss", "flce_kto_loss", "flce_distill_jsd",
+           "flce_forward_noalloc")
 
 
 class LogitTransform(ctypes.Structure):
@@ -58,6 +59,9 @@ def _load() -> ctypes.CDLL:
     lib.flce_forward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, xp,
                                  f32p, f32p, f32p, vp, sz, vp]
     lib.flce_forward.restype = ctypes.c_int
+    lib.flce_forward_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, xp,
+                                         f32p, f32p, f32p, vp]
+    lib.flce_forward_noalloc.restype = ctypes.c_int
     lib.flce_backward.argtypes = [vp, vp, vp, f32p, i64, i64, i64, i64, i64, ctypes.c_int,
                                   xp, f32p, f32p, vp, f32p, ctypes.c_int, vp, sz, vp]
     lib.flce_backward.restype = ctypes.c_int
@@ -236,6 +240,28 @@ def forward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor, *,
                             chunk_rows, _MODES[mode], make_transform(**(transform or {})),
                             _ptr(out), _ptr(lse), _ptr(mean),
                             _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out, lse, mean
+
+
+def forward_noalloc(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor, *,
+                    ignore_index: int = -100, chunk_rows: int = 256, mode: str = "nll",
+                    transform: Optional[dict] = None, out: torch.Tensor, lse: torch.Tensor,
+                    mean: Optional[torch.Tensor] = None):
+    """``forward`` through ``flce_forward_noalloc``: no workspace and nothing allocated
+    here either (the caller passes the outputs); the library's fixed per-GPU array holds
+    the partial results, so calls that can overlap on one GPU must not be made."""
+    _validate(hidden, weight, labels)
+    T, D = hidden.shape
+    V = weight.shape[0]
+    dev = hidden.device
+    _check_buffer("out", out, torch.float32, (T,), dev)
+    _check_buffer("lse", lse, torch.float32, (T,), dev)
+    if mean is not None:
+        _check_buffer("mean", mean, torch.float32, (), dev)
+    _check(lib.flce_forward_noalloc(_ptr(hidden), _ptr(weight), _ptr(labels), T, D, V,
+                                    ignore_index, chunk_rows, _MODES[mode],
+                                    make_transform(**(transform or {})), _ptr(out), _ptr(lse),
+                                    _ptr(mean), _stream(dev)))
     return out, lse, mean
 
 

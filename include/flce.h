@@ -128,6 +128,30 @@ flce_status flce_forward(const void *hidden, const void *weight, const int64_t *
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * flce_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation and outputs, with the forward's partial results kept in a
+ * fixed array inside the library instead of a caller workspace.  The array
+ * holds FLCE_FORWARD_SCRATCH_BYTES (16 MiB); the library reserves one per GPU
+ * when its code is loaded there and keeps it until the process ends.  The
+ * forward uses at most about 8 * max(T_pad, 524288) + 4 * T_pad bytes of it
+ * (T_pad = T rounded up to 256; 4.7 MB at 131,072 tokens, 12.6 MB at 1,048,576),
+ * so T up to about 1.39 million tokens fits; beyond the limit the call returns
+ * FLCE_ERR_WORKSPACE and enqueues nothing.
+ * Nothing in the array needs clearing between calls (every value a call reads
+ * was written by that call).  All calls on one GPU share its array: calls that
+ * can overlap on one GPU (two streams, two threads) race, so serialise them.
+ * Same arguments, conventions and errors as flce_forward otherwise.
+ */
+#define FLCE_FORWARD_SCRATCH_BYTES ((size_t)16 << 20)
+
+flce_status flce_forward_noalloc(const void *hidden, const void *weight, const int64_t *labels,
+                                 int64_t T, int64_t D, int64_t V, int64_t ignore_index,
+                                 int64_t chunk_rows, int mode,
+                                 const flce_logit_transform *transform, float *out, float *lse,
+                                 float *mean_out, void *stream);
+
+/*
  * Backward.  Recomputes the logits chunk by chunk and writes
  *   grad_hidden [T x D] bf16  = G W,
  *   grad_weight [V x D] fp32  = G^T H      (added to the existing contents if

@@ -23,6 +23,7 @@ int main(void) {
   printf("tune %d %lld %lld\n", (int)st, (long long)mb, (long long)cr);
   printf("bad_shape %d\n", (int)flce_describe_plan(16, 60, 100, 16, info));
   printf("status %s\n", flce_status_string(FLCE_ERR_WORKSPACE));
+  printf("forward_scratch %zu\n", (size_t)FLCE_FORWARD_SCRATCH_BYTES);
   printf("last_error %s\n", flce_last_error());
   return 0;
 }

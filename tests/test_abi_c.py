@@ -42,3 +42,4 @@ def test_c_caller_matches_the_binding(c_output):
     assert int(c_output["bad_shape"]) == 4          # D not a multiple of 8
     assert c_output["status"] == "workspace too small"
     assert "multiple of 8" in c_output["last_error"]
+    assert int(c_output["forward_scratch"]) == 16 << 20

@@ -65,6 +65,26 @@ def test_forward_rejects_before_launch(flce):
     assert b"workspace" in flce.lib.flce_last_error()
 
 
+def test_forward_noalloc_rejects_before_launch(flce):
+    f = flce.lib.flce_forward_noalloc
+
+    def call(**over):
+        a = dict(hidden=16, weight=16, labels=8, T=4, D=64, V=100, ign=-100, cr=16, mode=0,
+                 xf=None, out=4, lse=4, mean=None, stream=None)
+        a.update(over)
+        return f(a["hidden"], a["weight"], a["labels"], a["T"], a["D"], a["V"], a["ign"],
+                 a["cr"], a["mode"], a["xf"], a["out"], a["lse"], a["mean"], a["stream"])
+
+    assert call(T=-3) == 2
+    assert call(D=12) == 4
+    assert call(mode=7) == 1
+    assert call(hidden=None) == 1
+    assert call(hidden=8) == 1                      # misaligned
+    # the forward's partial results outgrow the fixed 16 MiB array past ~1.39M tokens
+    assert call(T=1_400_000, D=4096, V=151936) == 3
+    assert b"scratch" in flce.lib.flce_last_error()
+
+
 def test_backward_rejects_before_launch(flce):
     b = flce.lib.flce_backward
     # neither grad given
