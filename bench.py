@@ -5,10 +5,11 @@ whole synthetic batch, inputs resident in HBM, workspace preallocated.  Work
 per step is 8*T*V*D FLOPs: the logit GEMM (2TVD), its recompute in the backward
 (2TVD), dH = G W (2TVD) and dW = G^T H (2TVD).
 
-Prints one JSON line.  ``roofline`` describes the fused forward kernel
-(logit GEMM + online log-sum-exp), the largest single launch of the step,
-timed with HIP events on the stream it runs on; ``cpu_baseline`` times the
-float64 CPU oracle on a bounded sample of the same workload.
+Prints one JSON line.  ``roofline`` describes the GEMM kernel with the most time
+per step (the fused forward, the recompute, dH or dW), timed with the HIP events
+the library records after each kernel on the stream it runs on (instrumented steps
+after the timed ones), and lists all four under ``kernels``; ``cpu_baseline``
+times the float64 CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -216,36 +217,42 @@ def main():
     step_flops = 8.0 * T * V * D
     fwd_flops = 2.0 * T * V * D
 
-    traffic = None
-    # the counters were taken without a softcap (the capped forward is another instantiation)
-    if (os.path.exists(args.traffic_json) and args.logit_softcapping == 0.0
-            and args.token_shard == 1):
-        try:
-            tj = json.load(open(args.traffic_json))
-            rec = tj.get(args.workload, {}).get("fwd_lse_kernel")
-            if rec and rec.get("source_sha") == _kernel_sha():
-                traffic = rec["hbm_bytes_per_launch"]
-        except Exception:
-            traffic = None
-
+    # Per-kernel times of the four GEMM kernels, outside the timed region: the library's
+    # per-launch events over instrumented steps (one event on the stream after each
+    # kernel it launches).  Each GEMM kernel does 2TVD per step.
+    kernels, inst = kernel_breakdown(
+        step, max(3, min(args.steps, 10)),
+        {k: fwd_flops for k in ("fwd_lse", "bwd_grad", "bwd_dh", "bwd_dw")})
+    traffic = load_traffic(args) if (args.logit_softcapping == 0.0
+                                     and args.token_shard == 1) else {}
+    for k, rec in kernels.items():
+        rec["traffic"] = traffic.get(k, {}).get("hbm_bytes_per_launch")
     # The fused forward reads H and W once and writes O(T) values: its algorithmic
     # bytes per launch.  Below the ridge (peak FLOP/s / peak B/s) it is HBM-bound.
     fwd_bytes = 2.0 * T * D + 2.0 * V * D + 8.0 * T + 4.0 * 2 * T
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     if fwd_flops / fwd_bytes < PEAK_BF16 / PEAK_HBM:
-        roofline = {"kernel": "fwd_lse_kernel", "bound": "hbm",
-                    "achieved": round(fwd_bytes / (fwd_avg / 1e3) / 1e9, 1),
+        dom = "fwd_lse"                        # the HBM-bound shape (one token tile)
+        t_fwd = kernels[dom]["ms_per_step"]
+        roofline = {"kernel": dom, "bound": "hbm",
+                    "achieved": round(fwd_bytes / (t_fwd / 1e3) / 1e9, 1),
                     "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                    "frac": round(fwd_bytes / (fwd_avg / 1e3) / PEAK_HBM, 4)}
+                    "frac": round(fwd_bytes / (t_fwd / 1e3) / PEAK_HBM, 4),
+                    "algorithmic_bytes_per_launch": fwd_bytes}
     else:
-        roofline = {"kernel": "fwd_lse_kernel", "bound": "mfma",
-                    "achieved": round(fwd_flops / (fwd_avg / 1e3) / 1e12, 2),
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": kernels[dom]["achieved"],
                     "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                    "frac": round(fwd_flops / (fwd_avg / 1e3) / PEAK_BF16, 4)}
+                    "frac": kernels[dom]["frac"]}
     roofline.update({
-        "traffic": traffic,
-        "algorithmic_flops_per_launch": fwd_flops,
-        "algorithmic_bytes_per_launch": fwd_bytes,
-        "note": "event pair brackets flce_forward: the fused kernel plus two O(T) kernels",
+        "traffic": kernels[dom]["traffic"],
+        "algorithmic_flops_per_launch": kernels[dom]["algorithmic_flops_per_launch"],
+        "launches_per_step": kernels[dom]["launches_per_step"],
+        "avg_launch_us": kernels[dom]["avg_launch_us"],
+        "kernels": kernels,
+        "instrumented": inst,
+        "note": "the GEMM kernel with the most time per step; per-launch durations from "
+                "events the library records after each kernel on its stream, over "
+                "instrumented steps run after the timed ones",
     })
 
     line = {
@@ -283,6 +290,58 @@ def main():
         line["cpu_baseline"] = cpu_baseline(x, min(args.cpu_sample_tokens, T),
                                            args.cpu_sample_vocab, xf_vals if has_xf else None)
     print(json.dumps(line), flush=True)
+
+
+def kernel_breakdown(step, steps: int, flops: dict) -> tuple:
+    """Per-kernel times over `steps` calls of step() with the library's per-launch timing
+    on (an event on the stream after every kernel it launches), outside the timed region.
+    flops maps kernel names to algorithmic FLOPs per step; returns ({kernel: launches per
+    step, ms per step, average launch duration, achieved rate and fraction of peak}, the
+    instrumented steps' own time and the sum of all kernels' times per step)."""
+    import torch
+
+    from chunked_lm_head_amd import flce
+
+    cap = 1 << 15
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    flce.timing_begin(cap)
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    rows, n, dropped = flce.timing_end(cap)
+    torch.cuda.synchronize()
+    if dropped or n > cap or any(ms < 0 for _, ms in rows):
+        raise RuntimeError(f"kernel timing incomplete: {n} launches, {dropped} marks dropped")
+    per = {}
+    for k, ms in rows:
+        per.setdefault(k, []).append(ms)
+    kernels = {}
+    for k, f in flops.items():
+        v = per.get(k)
+        if not v:
+            continue
+        t = sum(v) / steps
+        kernels[k] = {"launches_per_step": len(v) / steps, "ms_per_step": round(t, 4),
+                      "avg_launch_us": round(sum(v) / len(v) * 1e3, 1),
+                      "achieved": round(f / (t / 1e3) / 1e12, 2),
+                      "frac": round(f / (t / 1e3) / PEAK_BF16, 4),
+                      "algorithmic_flops_per_launch": f * steps / len(v)}
+    inst = {"steps": steps, "ms_per_step": round(a.elapsed_time(b) / steps, 4),
+            "kernel_ms_per_step": round(sum(ms for _, ms in rows) / steps, 4)}
+    return kernels, inst
+
+
+def load_traffic(args) -> dict:
+    """Per-kernel HBM bytes per launch from profiles/traffic.json, for the kernels whose
+    record was measured on the current kernel sources (a hash of the three files)."""
+    try:
+        tj = json.load(open(args.traffic_json)).get(args.workload, {})
+    except Exception:
+        return {}
+    sha = _kernel_sha()
+    return {k: v for k, v in tj.items() if isinstance(v, dict) and v.get("source_sha") == sha}
 
 
 def distill_main(args) -> None:
@@ -344,6 +403,15 @@ def distill_main(args) -> None:
                   "gradient passes, dH, dW")
         loss = f"mean generalized JSD (beta {args.beta})"
     achieved = flops / (ms / 1e3)
+    # per-kernel FLOPs per step: both log-sum-exp passes, the block passes of each head
+    # (the JSD's gradient needs a second one of each), the student's dH and dW
+    npass = 1 if args.divergence == "kl" else 2
+    kernels, inst = kernel_breakdown(
+        step, max(3, min(args.steps, 10)),
+        {"fwd_lse": 2.0 * T * V * (Dt + Ds), "dst_teacher": npass * 2.0 * T * V * Dt,
+         "dst_student": npass * 2.0 * T * V * Ds, "dst_dh": 2.0 * T * V * Ds,
+         "dst_dw": 2.0 * T * V * Ds})
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     line = {
         "metric": "distillation fwd+bwd tokens/s (student and teacher LM heads)",
         "value": round(T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -354,11 +422,18 @@ def distill_main(args) -> None:
                    "teacher_hidden": Dt, "vocab": V, "chunk_rows": chunk_rows,
                    "masked_tokens": w.ignore_count, "loss": loss},
         "workspace_bytes": int(ws.numel()),
+        "whole_call": {"passes": passes, "achieved": round(achieved / 1e12, 2),
+                       "frac": round(achieved / PEAK_BF16, 4), "flops_per_step": flops},
         "roofline": {
-            "kernel": f"whole distillation call ({passes})",
-            "bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": PEAK_BF16 / 1e12,
-            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4), "traffic": None,
-            "algorithmic_flops_per_launch": flops,
+            "kernel": dom, "bound": "mfma", "achieved": kernels[dom]["achieved"],
+            "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": kernels[dom]["frac"],
+            "traffic": None,
+            "algorithmic_flops_per_launch": kernels[dom]["algorithmic_flops_per_launch"],
+            "launches_per_step": kernels[dom]["launches_per_step"],
+            "avg_launch_us": kernels[dom]["avg_launch_us"],
+            "kernels": kernels, "instrumented": inst,
+            "note": "the GEMM kernel with the most time per step, from the library's "
+                    "per-launch events over instrumented steps after the timed ones",
         },
     }
     print(f"[bench] {args.workload}: inputs drawn in {t_gen:.1f} s; step {ms:.3f} ms",
@@ -445,6 +520,10 @@ def policy_main(args):
     ms = start.elapsed_time(end) / args.steps
     flops = 8.0 * T * V * D
     achieved = flops / (ms / 1e3)
+    kernels, inst = kernel_breakdown(
+        step, max(3, min(args.steps, 10)),
+        {k: 2.0 * T * V * D for k in ("fwd_lse", "bwd_grad", "bwd_dh", "bwd_dw")})
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     line = {
         "metric": f"{args.loss.upper()} loss fwd+bwd tokens/s (fused LM head, selective log-softmax)",
         "value": round(T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -457,12 +536,20 @@ def policy_main(args):
                    "params": prm},
         "loss_value": round(float(loss.cpu()), 6),
         "workspace_bytes": int(ws.numel()),
+        "whole_call": {"achieved": round(achieved / 1e12, 2),
+                       "frac": round(achieved / PEAK_BF16, 4), "flops_per_step": flops,
+                       "note": "log-prob forward, loss kernels, recompute, dH, dW; prompt "
+                               "rows are computed too"},
         "roofline": {
-            "kernel": f"whole flce_{args.loss}_loss call (log-prob forward, loss kernels, "
-                      "recompute, dH, dW; prompt rows are computed too)",
-            "bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": PEAK_BF16 / 1e12,
-            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4), "traffic": None,
-            "algorithmic_flops_per_launch": flops,
+            "kernel": dom, "bound": "mfma", "achieved": kernels[dom]["achieved"],
+            "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": kernels[dom]["frac"],
+            "traffic": None,
+            "algorithmic_flops_per_launch": kernels[dom]["algorithmic_flops_per_launch"],
+            "launches_per_step": kernels[dom]["launches_per_step"],
+            "avg_launch_us": kernels[dom]["avg_launch_us"],
+            "kernels": kernels, "instrumented": inst,
+            "note": "the GEMM kernel with the most time per step, from the library's "
+                    "per-launch events over instrumented steps after the timed ones",
         },
     }
     print(f"[bench] {args.workload} {args.loss}: inputs drawn in {t_gen:.1f} s; step {ms:.3f} ms",

@@ -28,6 +28,8 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <mutex>
+#include <vector>
 
 #include "flce.h"
 #include "flce_distill.hpp"
@@ -284,9 +286,56 @@ flce_status check_device() {
   return FLCE_OK;
 }
 
-flce_status launched(const char *what) {
+const char *kernel_name(int id) {
+  static const char *const names[FLCE_KERNEL_COUNT] = {
+      "?",           "fwd_lse",     "fwd_combine", "fwd_mean",    "bwd_prep",
+      "bwd_ht",      "bwd_grad",    "bwd_dh",      "bwd_dw",      "bwd_dh_out",
+      "fill",        "dst_lse",     "dst_prep",    "dst_teacher", "dst_student",
+      "dst_reduce",  "dst_dh",      "dst_dw",      "dst_combine", "policy"};
+  return id > 0 && id < FLCE_KERNEL_COUNT ? names[id] : "?";
+}
+
+// Per-launch timing (flce_timing_begin / flce_timing_end): while on, an event
+// is recorded on the launching stream after every kernel (tagged with its
+// code) and before each entry point's first launch (tag 0).  The flag is read
+// without the lock on every launch; the marks are taken under it.
+struct Timing {
+  std::mutex mu;
+  std::atomic<bool> on{false};
+  std::vector<hipEvent_t> ev;
+  std::vector<hipStream_t> st;
+  std::vector<int32_t> id;
+  int32_t used = 0, dropped = 0;
+};
+
+Timing &timing() {
+  static Timing t;
+  return t;
+}
+
+void timing_mark(int32_t id, hipStream_t s) {
+  Timing &t = timing();
+  if (!t.on.load(std::memory_order_acquire)) return;
+  std::lock_guard<std::mutex> g(t.mu);
+  if (!t.on.load(std::memory_order_relaxed)) return;
+  if (t.used >= (int32_t)t.ev.size() || hipEventRecord(t.ev[t.used], s) != hipSuccess) {
+    ++t.dropped;
+    return;
+  }
+  t.st[t.used] = s;
+  t.id[t.used] = id;
+  ++t.used;
+}
+
+// Marks the start of an entry point's launches on s.
+void timing_start(hipStream_t s) { timing_mark(0, s); }
+
+// Checks a launch of kernel `id` on s and, with timing on, marks its end.
+flce_status launched(int32_t id, hipStream_t s) {
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(FLCE_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  if (e != hipSuccess)
+    return fail(FLCE_ERR_HIP, "%s launch: %s", kernel_name(id), hipGetErrorString(e));
+  timing_mark(id, s);
   return FLCE_OK;
 }
 
@@ -341,7 +390,7 @@ flce_status launch_ht(const void *hidden, uint16_t *ht, int64_t D, int64_t R, in
   t.rb0 = (int)rb0;
   t.rcount = (int)rcount;
   bwd_ht_kernel<<<dim3((unsigned)cdiv(rcount, 64), (unsigned)cdiv(D, 64)), 256, 0, s>>>(t);
-  return launched("bwd_ht");
+  return launched(FLCE_KERNEL_BWD_HT, s);
 }
 
 // dH partial sums and the dW update of one (row block, vocabulary chunk) from
@@ -376,7 +425,7 @@ flce_status launch_dh_dw(const uint16_t *G, int Gp, int64_t gcols, bool grouped,
       dst_dh_kernel<<<dh_grid, kThreads, 0, s>>>(h);
     else
       bwd_dh_kernel<<<dh_grid, kThreads, 0, s>>>(h);
-    FLCE_TRY(launched("bwd_dh"));
+    FLCE_TRY(launched(grouped ? FLCE_KERNEL_DST_DH : FLCE_KERNEL_BWD_DH, s));
   }
   if (!grad_weight) return FLCE_OK;
 
@@ -397,7 +446,7 @@ flce_status launch_dh_dw(const uint16_t *G, int Gp, int64_t gcols, bool grouped,
     dst_dw_kernel<<<(unsigned)(w.tiles_m * w.tiles_n), kThreads, 0, s>>>(w);
   else
     bwd_dw_kernel<<<(unsigned)(w.tiles_m * w.tiles_n), kThreads, 0, s>>>(w);
-  return launched("bwd_dw");
+  return launched(grouped ? FLCE_KERNEL_DST_DW : FLCE_KERNEL_BWD_DW, s);
 }
 
 // dH rows of a row block: sum of the split-K partials, rounded to bf16.
@@ -413,14 +462,14 @@ flce_status launch_dh_out(const float *dhacc, void *grad_hidden, int64_t D, int6
   o.rcount = (int)rcount;
   const int64_t work = rcount * (D / 8);
   bwd_dh_out_kernel<<<(unsigned)std::min<int64_t>(cdiv(work, 256), 8192), 256, 0, s>>>(o);
-  return launched("bwd_dh_out");
+  return launched(FLCE_KERNEL_BWD_DH_OUT, s);
 }
 
 flce_status fill(float *dst, int64_t n, float v, hipStream_t s) {
   if (n <= 0) return FLCE_OK;
   const int64_t blocks = std::min<int64_t>(cdiv(n, 256), 4096);
   fill_f32_kernel<<<(unsigned)blocks, 256, 0, s>>>(dst, n, v);
-  return launched("fill");
+  return launched(FLCE_KERNEL_FILL, s);
 }
 
 // Forward KL (jsd = false) or the generalized Jensen-Shannon divergence with
@@ -466,6 +515,7 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
   }
   FLCE_TRY(check_device());
   hipStream_t s = (hipStream_t)stream;
+  timing_start(s);
   if (T == 0) {
     if (mean_out) FLCE_TRY(fill(mean_out, 1, 0.f, s));
     if (grads && grad_student_weight && !accumulate_grad_weight)
@@ -507,7 +557,7 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
       fwd_lse_kernel<true><<<(unsigned)(p.n_tt * p.splits), kThreads, 0, s>>>(a);
     else
       fwd_lse_kernel<false><<<(unsigned)(p.n_tt * p.splits), kThreads, 0, s>>>(a);
-    FLCE_TRY(launched("fwd_lse"));
+    FLCE_TRY(launched(FLCE_KERNEL_FWD_LSE, s));
     DstLseParams l;
     l.part_m = a.part_m;
     l.part_s = a.part_s;
@@ -519,7 +569,7 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
     l.lse = head ? lse_s : lse_t;
     l.lse2 = head ? l2s : l2t;
     dst_lse_kernel<<<(unsigned)cdiv(p.Tb, 256 / l.lanes), 256, 0, s>>>(l);
-    FLCE_TRY(launched("dst_lse"));
+    FLCE_TRY(launched(FLCE_KERNEL_DST_LSE, s));
   }
 
   DstPrepParams pr;
@@ -531,7 +581,7 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
   pr.n = (int)p.Tb;
   pr.c = cbuf;
   dst_prep_kernel<<<1, 1024, 0, s>>>(pr);
-  FLCE_TRY(launched("dst_prep"));
+  FLCE_TRY(launched(FLCE_KERNEL_DST_PREP, s));
 
   // One block pass of dst_tile_kernel in the given role over the chunk at vc0.
   auto tile_pass = [&](int role, int64_t rb0, int64_t tiles_n, int64_t vc, float *part,
@@ -573,7 +623,7 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
       default: FLCE_TILE(kRoleJsdGrad); break;
     }
 #undef FLCE_TILE
-    return launched(teacher ? "dst_tile teacher" : "dst_tile student");
+    return launched(teacher ? FLCE_KERNEL_DST_TEACHER : FLCE_KERNEL_DST_STUDENT, s);
   };
   auto dh_dw = [&](int64_t rb, int64_t rcount, int64_t vc) -> flce_status {
     const int64_t vc0 = vc * p.Vc;
@@ -588,7 +638,7 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
     for (int k = 0; k < 2; ++k) {
       dst_reduce_kernel<<<(unsigned)cdiv(rcount, 64), 256, 0, s>>>(
           k ? part_b : part_a, nparts, (int)p.R, (int)rb0, (int)rcount, k ? Bbuf : Abuf);
-      FLCE_TRY(launched("dst_reduce"));
+      FLCE_TRY(launched(FLCE_KERNEL_DST_REDUCE, s));
     }
     return FLCE_OK;
   };
@@ -639,10 +689,10 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
   c.blk_sum = (double *)(ws + p.off_bs);
   c.blk_cnt = (int *)(ws + p.off_bc);
   dst_combine_kernel<<<(unsigned)p.n_cblk, 256, 0, s>>>(c);
-  FLCE_TRY(launched("dst_combine"));
+  FLCE_TRY(launched(FLCE_KERNEL_DST_COMBINE, s));
   if (mean_out) {
     fwd_mean_kernel<<<1, 256, 0, s>>>(c.blk_sum, c.blk_cnt, (int)p.n_cblk, mean_out);
-    FLCE_TRY(launched("fwd_mean"));
+    FLCE_TRY(launched(FLCE_KERNEL_FWD_MEAN, s));
   }
   return FLCE_OK;
 }
@@ -674,6 +724,7 @@ flce_status forward_launch(const Plan &p, const Xform &xf, bool cap, const void 
                            int mode, float *out, float *lse, float *mean_out, char *ws,
                            hipStream_t s) {
   const int64_t T = p.T, D = p.D, V = p.V;
+  timing_start(s);
   if (T == 0) return mean_out ? fill(mean_out, 1, 0.f, s) : FLCE_OK;
 
   FwdLseParams a;
@@ -696,7 +747,7 @@ flce_status forward_launch(const Plan &p, const Xform &xf, bool cap, const void 
     fwd_lse_kernel<true><<<(unsigned)(p.n_tt * p.splits), kThreads, 0, s>>>(a);
   else
     fwd_lse_kernel<false><<<(unsigned)(p.n_tt * p.splits), kThreads, 0, s>>>(a);
-  FLCE_TRY(launched("fwd_lse"));
+  FLCE_TRY(launched(FLCE_KERNEL_FWD_LSE, s));
 
   FwdCombineParams c;
   c.part_m = a.part_m;
@@ -715,10 +766,10 @@ flce_status forward_launch(const Plan &p, const Xform &xf, bool cap, const void 
   c.blk_sum = (double *)(ws + p.off_bs);
   c.blk_cnt = (int *)(ws + p.off_bc);
   fwd_combine_kernel<<<(unsigned)p.n_cblk, 256, 0, s>>>(c);
-  FLCE_TRY(launched("fwd_combine"));
+  FLCE_TRY(launched(FLCE_KERNEL_FWD_COMBINE, s));
   if (mean_out) {
     fwd_mean_kernel<<<1, 256, 0, s>>>(c.blk_sum, c.blk_cnt, (int)p.n_cblk, mean_out);
-    FLCE_TRY(launched("fwd_mean"));
+    FLCE_TRY(launched(FLCE_KERNEL_FWD_MEAN, s));
   }
   return FLCE_OK;
 }
@@ -787,6 +838,69 @@ const char *flce_status_string(int status) {
 }
 
 const char *flce_last_error(void) { return g_last_error; }
+
+const char *flce_kernel_name(int32_t id) { return kernel_name(id); }
+
+flce_status flce_timing_begin(int32_t capacity) {
+  g_last_error[0] = 0;
+  if (capacity < 1 || capacity > (1 << 20))
+    return fail(FLCE_ERR_ARG, "timing capacity %d outside 1 .. 1048576", (int)capacity);
+  Timing &t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (t.on.load(std::memory_order_relaxed)) return fail(FLCE_ERR_ARG, "timing is already on");
+  t.ev.assign((size_t)capacity, nullptr);
+  for (int32_t i = 0; i < capacity; ++i) {
+    const hipError_t e = hipEventCreate(&t.ev[i]);
+    if (e != hipSuccess) {
+      for (int32_t j = 0; j < i; ++j) (void)hipEventDestroy(t.ev[j]);
+      t.ev.clear();
+      return fail(FLCE_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+    }
+  }
+  t.st.assign((size_t)capacity, nullptr);
+  t.id.assign((size_t)capacity, 0);
+  t.used = 0;
+  t.dropped = 0;
+  t.on.store(true, std::memory_order_release);
+  return FLCE_OK;
+}
+
+flce_status flce_timing_end(int32_t *ids, float *ms, int32_t capacity, int32_t *count,
+                            int32_t *dropped) {
+  g_last_error[0] = 0;
+  if (!ids || !ms || !count || capacity < 0)
+    return fail(FLCE_ERR_ARG, "ids, ms and count must not be NULL, capacity >= 0");
+  Timing &t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (!t.on.load(std::memory_order_relaxed)) return fail(FLCE_ERR_ARG, "timing is not on");
+  t.on.store(false, std::memory_order_release);
+  flce_status st = FLCE_OK;
+  for (int32_t i = 0; i < t.used && st == FLCE_OK; ++i) {
+    const hipError_t e = hipEventSynchronize(t.ev[i]);
+    if (e != hipSuccess) st = fail(FLCE_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+  }
+  int32_t n = 0;
+  for (int32_t i = 0; i < t.used && st == FLCE_OK; ++i) {
+    if (t.id[i] == 0) continue;  // an entry point's start mark
+    float v = -1.f;
+    if (i > 0 && t.st[i - 1] == t.st[i]) {
+      const hipError_t e = hipEventElapsedTime(&v, t.ev[i - 1], t.ev[i]);
+      if (e != hipSuccess)
+        st = fail(FLCE_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
+    }
+    if (n < capacity) {
+      ids[n] = t.id[i];
+      ms[n] = v;
+    }
+    ++n;
+  }
+  for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
+  t.ev.clear();
+  *count = n;
+  if (dropped) *dropped = t.dropped;
+  t.used = t.dropped = 0;
+  return st;
+}
 
 flce_status flce_forward(const void *hidden, const void *weight, const int64_t *labels,
                          int64_t T, int64_t D, int64_t V, int64_t ignore_index,
@@ -870,6 +984,7 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
   }
   FLCE_TRY(check_device());
   hipStream_t s = (hipStream_t)stream;
+  timing_start(s);
   if (T == 0)
     return (accumulate_grad_weight || !grad_weight) ? FLCE_OK : fill(grad_weight, V * D, 0.f, s);
 
@@ -893,7 +1008,7 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
   pr.c = cbuf;
   pr.lse2 = l2buf;
   bwd_prep_kernel<<<1, 1024, 0, s>>>(pr);
-  FLCE_TRY(launched("bwd_prep"));
+  FLCE_TRY(launched(FLCE_KERNEL_BWD_PREP, s));
 
   for (int64_t rb = 0; rb < p.n_rb; ++rb) {
     const int64_t rb0 = rb * p.R;
@@ -929,7 +1044,7 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
         bwd_grad_kernel<true><<<grid, kThreads, 0, s>>>(g);
       else
         bwd_grad_kernel<false><<<grid, kThreads, 0, s>>>(g);
-      FLCE_TRY(launched("bwd_grad"));
+      FLCE_TRY(launched(FLCE_KERNEL_BWD_GRAD, s));
 
       FLCE_TRY(launch_dh_dw(G, (int)p.Vc, p.Vc, false, weight, ht, D, V, p.R, rcount, vc0, vcount,
                             p.dh_splits, grad_hidden ? dhacc : nullptr, grad_weight, vc > 0,
@@ -1123,6 +1238,7 @@ flce_status policy_loss(int kind, const PolicyInputs &in, const flce_policy_para
   }
   FLCE_TRY(check_device());
   hipStream_t s = (hipStream_t)stream;
+  timing_start(s);
   if (T == 0) {
     FLCE_TRY(fill(loss_out, 1, 0.f, s));
     if (grads && grad_weight && !accumulate_grad_weight) FLCE_TRY(fill(grad_weight, V * D, 0.f, s));
@@ -1165,7 +1281,7 @@ flce_status policy_loss(int kind, const PolicyInputs &in, const flce_policy_para
     launch_policy_kernels<kPolicyDpo>(pp, grads, s);
   else
     launch_policy_kernels<kPolicyKto>(pp, grads, s);
-  FLCE_TRY(launched("policy loss"));
+  FLCE_TRY(launched(FLCE_KERNEL_POLICY, s));
   if (!grads) return FLCE_OK;
   return flce_backward(hidden, weight, labels, lse, T, D, V, ignore_index, chunk_rows,
                        FLCE_MODE_LOGPROB, transform, pp.c, nullptr, grad_hidden, grad_weight,

@@ -32,7 +32,8 @@ EXPORTS = ("flce_workspace_bytes", "flce_forward", "flce_backward", "flce_descri
            "flce_status_string", "flce_last_error", "flce_distill_workspace_bytes",
            "flce_distill", "flce_chunk_rows_for", "flce_tune", "flce_policy_workspace_bytes",
            "flce_grpo_loss", "flce_dpo_loss", "flce_kto_loss", "flce_distill_jsd",
-           "flce_forward_noalloc")
+           "flce_forward_noalloc", "flce_timing_begin", "flce_timing_end",
+           "flce_kernel_name")
 
 
 class LogitTransform(ctypes.Structure):
@@ -96,6 +97,14 @@ def _load() -> ctypes.CDLL:
     lib.flce_status_string.restype = ctypes.c_char_p
     lib.flce_last_error.argtypes = []
     lib.flce_last_error.restype = ctypes.c_char_p
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.flce_timing_begin.argtypes = [ctypes.c_int32]
+    lib.flce_timing_begin.restype = ctypes.c_int
+    lib.flce_timing_end.argtypes = [i32p, ctypes.POINTER(ctypes.c_float), ctypes.c_int32, i32p,
+                                    i32p]
+    lib.flce_timing_end.restype = ctypes.c_int
+    lib.flce_kernel_name.argtypes = [ctypes.c_int32]
+    lib.flce_kernel_name.restype = ctypes.c_char_p
     return lib
 
 
@@ -152,6 +161,24 @@ def describe_plan(T: int, D: int, V: int, chunk_rows: int = 256) -> dict:
     info = (ctypes.c_int64 * 12)()
     _check(lib.flce_describe_plan(T, D, V, chunk_rows, info))
     return dict(zip(PLAN_KEYS, list(info)))
+
+
+def timing_begin(capacity: int) -> None:
+    """Turn the library's per-launch kernel timing on (``capacity`` HIP events on the
+    current device): every kernel launched until ``timing_end`` is followed by an event
+    on its stream."""
+    _check(lib.flce_timing_begin(capacity))
+
+
+def timing_end(capacity: int) -> tuple:
+    """Turn timing off and return ([(kernel name, ms), ...] in launch order, number of
+    kernels recorded, marks dropped for lack of events); ms is -1 where unknown."""
+    ids = (ctypes.c_int32 * capacity)()
+    ms = (ctypes.c_float * capacity)()
+    n, dropped = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.flce_timing_end(ids, ms, capacity, ctypes.byref(n), ctypes.byref(dropped)))
+    rows = [(lib.flce_kernel_name(ids[i]).decode(), ms[i]) for i in range(min(n.value, capacity))]
+    return rows, n.value, dropped.value
 
 
 def chunk_rows_for(context_length: int, multiplier: int = 0) -> int:

@@ -371,6 +371,61 @@ flce_status flce_tune(int64_t batch, int64_t context_length, int64_t D, int64_t 
 flce_status flce_describe_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows,
                                int64_t *info);
 
+/*
+ * Per-launch kernel timing, a profiling aid (no page defines it; it is how the
+ * time of each GEMM kernel inside one call is measured).  The exceptions to the
+ * conventions above: flce_timing_begin creates HIP events and flce_timing_end
+ * waits for them; while timing is on, the entry points also record events on
+ * their stream (do not turn it on around stream capture).
+ *
+ * flce_timing_begin(capacity): creates `capacity` (1 .. 1,048,576) events on the
+ * current device and turns timing on for the whole process.  From then on each
+ * entry point records one event on its stream before its first launch and one
+ * after every kernel it launches, tagged with that kernel's FLCE_KERNEL_* code,
+ * until the events run out (later marks are dropped and counted).  Timing must
+ * be off (FLCE_ERR_ARG otherwise).
+ *
+ * flce_timing_end(ids, ms, capacity, count, dropped): waits for the recorded
+ * events, turns timing off, destroys the events and writes, in launch order,
+ * one (id, milliseconds) pair per recorded kernel: ids[i] its FLCE_KERNEL_*
+ * code, ms[i] the time between the event before it on the same stream and the
+ * event after it (-1 when the mark before it was recorded on another stream or
+ * none exists).  At most `capacity` pairs are written; *count receives the
+ * number recorded, *dropped (if not NULL) the marks dropped for lack of events.
+ * ids and ms are host arrays.  FLCE_ERR_ARG if timing is off or an argument is
+ * NULL.  Calls on several streams at once interleave their marks; time one
+ * stream at a time.
+ */
+enum {
+  FLCE_KERNEL_FWD_LSE = 1,        /* forward: fused logit GEMM + running log-sum-exp */
+  FLCE_KERNEL_FWD_COMBINE = 2,    /* forward: combine of the vocabulary splits */
+  FLCE_KERNEL_FWD_MEAN = 3,       /* forward: the mean over kept tokens */
+  FLCE_KERNEL_BWD_PREP = 4,       /* backward: per-token scale c_t */
+  FLCE_KERNEL_BWD_HT = 5,         /* backward: H^T of a row block */
+  FLCE_KERNEL_BWD_GRAD = 6,       /* backward: logit recompute + bf16 gradient block G */
+  FLCE_KERNEL_BWD_DH = 7,         /* backward: dH partial sums G W */
+  FLCE_KERNEL_BWD_DW = 8,         /* backward: dW update G^T H */
+  FLCE_KERNEL_BWD_DH_OUT = 9,     /* backward: dH partials summed and rounded to bf16 */
+  FLCE_KERNEL_FILL = 10,          /* a constant fill (T == 0 paths) */
+  FLCE_KERNEL_DST_LSE = 11,       /* distillation: combine of one head's log-sum-exp */
+  FLCE_KERNEL_DST_PREP = 12,      /* distillation: per-token scale */
+  FLCE_KERNEL_DST_TEACHER = 13,   /* distillation: teacher logits -> probabilities */
+  FLCE_KERNEL_DST_STUDENT = 14,   /* distillation: student logits -> sums and G */
+  FLCE_KERNEL_DST_REDUCE = 15,    /* distillation: per-token sums of a row block */
+  FLCE_KERNEL_DST_DH = 16,        /* distillation: dH partial sums */
+  FLCE_KERNEL_DST_DW = 17,        /* distillation: dW update */
+  FLCE_KERNEL_DST_COMBINE = 18,   /* distillation: per-token divergence */
+  FLCE_KERNEL_POLICY = 19,        /* policy losses: the loss kernels (2 or 3 launches) */
+  FLCE_KERNEL_COUNT = 20
+};
+
+flce_status flce_timing_begin(int32_t capacity);
+flce_status flce_timing_end(int32_t *ids, float *ms, int32_t capacity, int32_t *count,
+                            int32_t *dropped);
+
+/* Static name of a FLCE_KERNEL_* code ("?" for other values). */
+const char *flce_kernel_name(int32_t id);
+
 /* Static text for a status code. */
 const char *flce_status_string(int status);
 

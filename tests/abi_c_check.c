@@ -23,7 +23,10 @@ int main(void) {
   printf("tune %d %lld %lld\n", (int)st, (long long)mb, (long long)cr);
   printf("bad_shape %d\n", (int)flce_describe_plan(16, 60, 100, 16, info));
   printf("status %s\n", flce_status_string(FLCE_ERR_WORKSPACE));
+  printf("bad_shape_error %s\n", flce_last_error());
   printf("forward_scratch %zu\n", (size_t)FLCE_FORWARD_SCRATCH_BYTES);
+  printf("kernel %s %s\n", flce_kernel_name(FLCE_KERNEL_BWD_GRAD), flce_kernel_name(FLCE_KERNEL_COUNT));
+  printf("timing_off %d\n", (int)flce_timing_end(NULL, NULL, 0, NULL, NULL));
   printf("last_error %s\n", flce_last_error());
   return 0;
 }

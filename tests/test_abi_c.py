@@ -41,5 +41,8 @@ def test_c_caller_matches_the_binding(c_output):
     assert st == 0 and (mb, cr) == (t["mini_batches"], t["chunk_rows"])
     assert int(c_output["bad_shape"]) == 4          # D not a multiple of 8
     assert c_output["status"] == "workspace too small"
-    assert "multiple of 8" in c_output["last_error"]
+    assert "multiple of 8" in c_output["bad_shape_error"]
+    assert c_output["kernel"] == "bwd_grad ?"
+    assert int(c_output["timing_off"]) == 1         # FLCE_ERR_ARG: NULL outputs
+    assert "NULL" in c_output["last_error"]
     assert int(c_output["forward_scratch"]) == 16 << 20

@@ -98,6 +98,22 @@ def test_backward_rejects_before_launch(flce):
     assert b(16, 16, 8, 4, 4, 64, 100, -100, 16, 0, None, 4, None, 16, 16, 0, 16, 8, None) == 3
 
 
+def test_timing_rejects_before_any_device_call(flce):
+    lib = flce.lib
+    assert lib.flce_timing_begin(0) == 1
+    assert lib.flce_timing_begin(1 << 21) == 1
+    assert b"capacity" in lib.flce_last_error()
+    ids, ms = (ctypes.c_int32 * 4)(), (ctypes.c_float * 4)()
+    n = ctypes.c_int32()
+    assert lib.flce_timing_end(ids, ms, 4, ctypes.byref(n), None) == 1     # timing is off
+    assert b"not on" in lib.flce_last_error()
+    assert lib.flce_timing_end(None, ms, 4, ctypes.byref(n), None) == 1
+    names = [lib.flce_kernel_name(i).decode() for i in range(1, 20)]
+    assert len(set(names)) == 19 and "?" not in names
+    assert lib.flce_kernel_name(0) == b"?" and lib.flce_kernel_name(20) == b"?"
+    assert names[5:8] == ["bwd_grad", "bwd_dh", "bwd_dw"]
+
+
 BAD_TRANSFORMS = [
     (-1.0, 0.0, 0.0, 1.0),            # negative multiply
     (0.0, -2.0, 0.0, 1.0),            # negative divide
