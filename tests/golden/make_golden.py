@@ -7,7 +7,11 @@ float64 oracle computes, over ALL tokens and the FULL vocabulary:
   * the grad_weight rows of a sample of vocabulary entries (these need the
     lse of every token, hence the full forward).
 The samples include the first and last tokens and vocabulary rows, tile
-boundaries, the ragged tail, ignored tokens and labels of sampled tokens.
+boundaries, the ragged tail, ignored tokens and labels of sampled tokens, and the
+tokens on both sides of every multiple of 8,192 (the backward's row blocks).  The
+vocabulary rows on both sides of every multiple of 4,096 (and of 7,936 where
+V = 128,000) cover the backward's vocabulary chunks, all multiples of 256 rows: their
+dW rows are kept for the first 512 hidden columns (``vocab_edge``, ``dw_edge``).
 
 Variants with a logit transform (the chunked call's multiply / divide /
 softcap / temperature keywords on the Unsloth GRPO page) reuse a workload's
@@ -47,6 +51,8 @@ def sample_tokens(w: synth.Workload, labels: np.ndarray, rng) -> np.ndarray:
     T = w.T
     picks = {0, 1, 255, 256, T // 2, T - 1, T - 2}
     picks |= {T - 1 - int(i) for i in range(0, min(T, 300), 37)}     # ragged / last tile
+    for k in range(8192, T, 8192):                                    # row-block edges
+        picks |= {k - 1, k}
     ign = np.nonzero(labels == synth.IGNORE_INDEX)[0]
     picks |= set(int(i) for i in ign[:3])
     if getattr(w, "prompt_len", 0):
@@ -63,6 +69,20 @@ def sample_vocab(w: synth.Workload, labels: np.ndarray, tokens: np.ndarray, rng)
     picks |= set(int(x) for x in used[:4])
     while len(picks) < 12:
         picks.add(int(rng.integers(0, V)))
+    return np.array(sorted(picks), dtype=np.int64)
+
+
+EDGE_COLS = 512
+
+
+def vocab_edges(V: int) -> np.ndarray:
+    """Vocabulary rows on both sides of each multiple of 4,096, and of 7,936 when
+    V = 128,000: the edges of every vocabulary chunk the backward can use here."""
+    steps = (4096, 7936) if V == 128000 else (4096,)
+    picks = set()
+    for m in steps:
+        for k in range(m, V, m):
+            picks |= {k - 1, k}
     return np.array(sorted(picks), dtype=np.int64)
 
 
@@ -83,11 +103,15 @@ def make(name: str) -> str:
     dh = o.grad_hidden_rows(x.hidden, x.weight, x.labels, tokens, c[tokens], synth.IGNORE_INDEX,
                             transform=tr)
     dw = o.grad_weight_rows(x.hidden, x.weight, x.labels, vocab, c, f.lse, transform=tr)
+    edges = vocab_edges(w.V)
+    dw_edge = o.grad_weight_rows(x.hidden, x.weight, x.labels, edges, c, f.lse,
+                                 transform=tr)[:, :EDGE_COLS]
     tv = o.LogitTransform(**xf)
     path = os.path.join(HERE, f"{name}.npz")
     np.savez(path, tokens=tokens, out=f.out[tokens], lse=f.lse[tokens], mean=np.float64(f.mean),
              n_valid=np.int64(f.n_valid), vocab=vocab, dh=dh.astype(np.float32),
              dw=dw.astype(np.float32), dw_norm_rows=np.linalg.norm(dw, axis=1),
+             vocab_edge=edges, dw_edge=dw_edge.astype(np.float32),
              seed=np.int64(w.seed), workload=np.str_(base),
              transform=np.array([tv.scale_multiply, tv.scale_divide, tv.softcap,
                                  tv.temperature], dtype=np.float64))
@@ -125,11 +149,15 @@ def make_distill(name: str) -> str:
             if divergence == "jsd" else None)
     dw = dst.grad_weight_rows(x.s_hidden, x.s_weight, x.t_hidden, x.t_weight, vocab, c,
                               f.lse_s, f.lse_t, gbar=gbar, **kw)
+    edges = vocab_edges(w.V)
+    dw_edge = dst.grad_weight_rows(x.s_hidden, x.s_weight, x.t_hidden, x.t_weight, edges, c,
+                                   f.lse_s, f.lse_t, gbar=gbar, **kw)[:, :EDGE_COLS]
     path = os.path.join(HERE, f"{name}.npz")
     np.savez(path, tokens=tokens, kl=f.kl[tokens], lse_s=f.lse_s[tokens], lse_t=f.lse_t[tokens],
              mean=np.float64(f.mean), n_valid=np.int64(f.n_valid), vocab=vocab,
              dh=dh.astype(np.float32), dw=dw.astype(np.float32), seed=np.int64(w.seed),
-             workload=np.str_(base), divergence=np.str_(divergence), beta=np.float64(beta))
+             workload=np.str_(base), divergence=np.str_(divergence), beta=np.float64(beta),
+             vocab_edge=edges, dw_edge=dw_edge.astype(np.float32))
     print(f"{name}: {time.time() - t0:.0f} s -> {path}", flush=True)
     return path
 
@@ -188,6 +216,7 @@ def make_policy(name: str) -> str:
                         seq_len=w.seq_len, prompt_len=w.prompt_len)
     tokens = sample_tokens(tw, x.labels, rng)
     vocab = sample_vocab(tw, x.labels, tokens, rng)
+    edges = vocab_edges(w.V)
     out = dict(tokens=tokens, vocab=vocab, logp=lp[tokens], seed=np.int64(w.seed), old=old,
                ref=ref, ref_dpo=ref_dpo, ref_kto=ref_kto, grad_loss=np.float64(GRAD_LOSS),
                **{k: np.float64(v) for k, v in P.items()})
@@ -198,6 +227,9 @@ def make_policy(name: str) -> str:
                                             synth.IGNORE_INDEX).astype(np.float32)
         out[f"{k}_dw"] = o.grad_weight_rows(x.hidden, x.weight, x.labels, vocab, c,
                                             f.lse).astype(np.float32)
+        out[f"{k}_dw_edge"] = o.grad_weight_rows(x.hidden, x.weight, x.labels, edges, c,
+                                                 f.lse)[:, :EDGE_COLS].astype(np.float32)
+    out["vocab_edge"] = edges
     path = os.path.join(HERE, f"{name}.npz")
     np.savez(path, **out)
     print(f"{name}: {time.time() - t0:.0f} s -> {path}", flush=True)
