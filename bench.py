@@ -225,20 +225,37 @@ def main():
         {k: fwd_flops for k in ("fwd_lse", "bwd_grad", "bwd_dh", "bwd_dw")})
     traffic = load_traffic(args) if (args.logit_softcapping == 0.0
                                      and args.token_shard == 1) else {}
+    # Algorithmic HBM bytes per step of each GEMM kernel (each operand and output once per
+    # launch that needs it; the plan's row blocks n_rb and vocabulary chunks n_vc):
+    #   forward:   H and W once, labels, two fp32 values per token out;
+    #   recompute: per (row block, chunk) its H rows and W rows, the bf16 G block written;
+    #   dH:        G read, W rows per row block, fp32 dH sums written (read back after
+    #              the first chunk);
+    #   dW:        G read, H^T per chunk, fp32 dW written (read back after the first block).
+    plan = flce.describe_plan(T, D, V, chunk_rows)
+    n_rb, n_vc = plan["row_blocks"], plan["vocab_chunks"]
+    step_bytes = {
+        "fwd_lse": 2.0 * T * D + 2.0 * V * D + 8.0 * T + 8.0 * T,
+        "bwd_grad": 2.0 * n_vc * T * D + 2.0 * n_rb * V * D + 2.0 * T * V,
+        "bwd_dh": 2.0 * T * V + 2.0 * n_rb * V * D + 4.0 * T * D * (2 * n_vc - 1),
+        "bwd_dw": 2.0 * T * V + 2.0 * n_vc * T * D + 4.0 * V * D * (2 * n_rb - 1),
+    }
     for k, rec in kernels.items():
         rec["traffic"] = traffic.get(k, {}).get("hbm_bytes_per_launch")
-    # The fused forward reads H and W once and writes O(T) values: its algorithmic
-    # bytes per launch.  Below the ridge (peak FLOP/s / peak B/s) it is HBM-bound.
-    fwd_bytes = 2.0 * T * D + 2.0 * V * D + 8.0 * T + 4.0 * 2 * T
+        n = rec["launches_per_step"]
+        rec["algorithmic_bytes_per_launch"] = step_bytes[k] / n
+        # below the ridge (peak FLOP/s over peak B/s) a kernel is HBM-bound
+        if fwd_flops / step_bytes[k] < PEAK_BF16 / PEAK_HBM:
+            rate = step_bytes[k] / (rec["ms_per_step"] / 1e3)
+            rec.update(bound="hbm", achieved_gbps=round(rate / 1e9, 1),
+                       frac_hbm=round(rate / PEAK_HBM, 4))
+        else:
+            rec["bound"] = "mfma"
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
-    if fwd_flops / fwd_bytes < PEAK_BF16 / PEAK_HBM:
-        dom = "fwd_lse"                        # the HBM-bound shape (one token tile)
-        t_fwd = kernels[dom]["ms_per_step"]
-        roofline = {"kernel": dom, "bound": "hbm",
-                    "achieved": round(fwd_bytes / (t_fwd / 1e3) / 1e9, 1),
-                    "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                    "frac": round(fwd_bytes / (t_fwd / 1e3) / PEAK_HBM, 4),
-                    "algorithmic_bytes_per_launch": fwd_bytes}
+    if kernels[dom]["bound"] == "hbm":
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": kernels[dom]["achieved_gbps"],
+                    "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": kernels[dom]["frac_hbm"],
+                    "algorithmic_bytes_per_launch": kernels[dom]["algorithmic_bytes_per_launch"]}
     else:
         roofline = {"kernel": dom, "bound": "mfma", "achieved": kernels[dom]["achieved"],
                     "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
