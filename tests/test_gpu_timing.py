@@ -108,3 +108,37 @@ def test_timing_of_distillation_names_its_block_kernels():
     assert names.count("dst_dh") == blocks and names.count("dst_dw") == blocks
     assert names[-2:] == ["dst_combine", "fwd_mean"], names
     assert all(ms > 0 for _, ms in rows)
+
+
+def test_timing_of_a_policy_loss_and_the_allocation_free_forward():
+    from chunked_lm_head_amd import flce
+
+    w = synth.policy_custom("timing_policy", n_seq=2, seq_len=384, prompt_len=64, H=128, V=1900,
+                            seed=84)
+    x = synth.make_policy_inputs(w)
+    dev = gu.device()
+    h, W = gu.bf16_tensor(x.hidden, dev), gu.bf16_tensor(x.weight, dev)
+    y = torch.from_numpy(x.labels).to(dev)
+    adv = torch.from_numpy(x.advantages).to(dev)
+    one = torch.ones((), dtype=torch.float32, device=dev)
+    ref = flce.grpo_loss(h, W, y, w.n_seq, adv, beta=0.0, chunk_rows=w.chunk_rows,
+                         grad_loss=one)
+    out = torch.empty(w.T, dtype=torch.float32, device=dev)
+    lse = torch.empty(w.T, dtype=torch.float32, device=dev)
+    flce.timing_begin(4096)
+    got = flce.grpo_loss(h, W, y, w.n_seq, adv, beta=0.0, chunk_rows=w.chunk_rows,
+                         grad_loss=one)
+    flce.forward_noalloc(h, W, y, chunk_rows=w.chunk_rows, out=out, lse=lse)
+    rows, n, dropped = flce.timing_end(4096)
+    torch.cuda.synchronize()
+    for r, t in zip(ref, got):
+        assert (r is None and t is None) or torch.equal(r, t)
+    names = [k for k, _ in rows]
+    plan = flce.describe_plan(w.T, w.H, w.V, w.chunk_rows)
+    # log-prob forward, the loss kernels, the log-prob backward, then the second forward
+    want = (["fwd_lse", "fwd_combine", "policy", "bwd_prep"]
+            + (["bwd_ht"] + ["bwd_grad", "bwd_dh", "bwd_dw"] * plan["vocab_chunks"]
+               + ["bwd_dh_out"]) * plan["row_blocks"]
+            + ["fwd_lse", "fwd_combine"])
+    assert dropped == 0 and names == want, names
+    assert all(ms > 0 for _, ms in rows)
