@@ -318,7 +318,12 @@ void timing_mark(int32_t id, hipStream_t s) {
   if (!t.on.load(std::memory_order_acquire)) return;
   std::lock_guard<std::mutex> g(t.mu);
   if (!t.on.load(std::memory_order_relaxed)) return;
-  if (t.used >= (int32_t)t.ev.size() || hipEventRecord(t.ev[t.used], s) != hipSuccess) {
+  if (t.used >= (int32_t)t.ev.size()) {
+    ++t.dropped;
+    return;
+  }
+  if (hipEventRecord(t.ev[t.used], s) != hipSuccess) {
+    (void)hipGetLastError();  // a lost mark must not read as the next launch's failure
     ++t.dropped;
     return;
   }
