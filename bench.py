@@ -3,7 +3,9 @@
 One step = flce_forward + flce_backward (mean NLL, upstream grad 1) over the
 whole synthetic batch, inputs resident in HBM, workspace preallocated.  Work
 per step is 8*T*V*D FLOPs: the logit GEMM (2TVD), its recompute in the backward
-(2TVD), dH = G W (2TVD) and dW = G^T H (2TVD).
+(2TVD), dH = G W (2TVD) and dW = G^T H (2TVD).  The backward skips 256-token tiles
+in which no token has a gradient (prompt tokens of a policy loss, a per-token upstream
+gradient that is zero); the FLOPs reported are the ones the kernels execute.
 
 Prints one JSON line.  ``roofline`` describes the GEMM kernel with the most time
 per step (the fused forward, the recompute, dH or dW), timed with the HIP events
@@ -214,15 +216,19 @@ def main():
     step_ms = sorted(f + b for f, b in zip(fwd_ms, bwd_ms))
     median_ms = step_ms[len(step_ms) // 2]
     tokens_per_s = T / (ms / 1e3)
-    step_flops = 8.0 * T * V * D
     fwd_flops = 2.0 * T * V * D
+    plan = flce.describe_plan(T, D, V, chunk_rows)
+    active = x.labels != synth.IGNORE_INDEX
+    if x.grad_out is not None:
+        active &= x.grad_out != 0
+    bwd = backward_flops(active, plan["row_block"], V, D)
+    gemm_flops = {"fwd_lse": fwd_flops, **{k: bwd[k] for k in ("bwd_grad", "bwd_dh", "bwd_dw")}}
+    step_flops = sum(gemm_flops.values())
 
     # Per-kernel times of the four GEMM kernels, outside the timed region: the library's
     # per-launch events over instrumented steps (one event on the stream after each
-    # kernel it launches).  Each GEMM kernel does 2TVD per step.
-    kernels, inst = kernel_breakdown(
-        step, max(3, min(args.steps, 10)),
-        {k: fwd_flops for k in ("fwd_lse", "bwd_grad", "bwd_dh", "bwd_dw")})
+    # kernel it launches).  Each GEMM kernel does 2TVD per step, less the skipped tiles.
+    kernels, inst = kernel_breakdown(step, max(3, min(args.steps, 10)), gemm_flops)
     traffic = load_traffic(args) if (args.logit_softcapping == 0.0
                                      and args.token_shard == 1) else {}
     # Algorithmic HBM bytes per step of each GEMM kernel (each operand and output once per
@@ -232,7 +238,6 @@ def main():
     #   dH:        G read, W rows per row block, fp32 dH sums written (read back after
     #              the first chunk);
     #   dW:        G read, H^T per chunk, fp32 dW written (read back after the first block).
-    plan = flce.describe_plan(T, D, V, chunk_rows)
     n_rb, n_vc = plan["row_blocks"], plan["vocab_chunks"]
     step_bytes = {
         "fwd_lse": 2.0 * T * D + 2.0 * V * D + 8.0 * T + 8.0 * T,
@@ -245,7 +250,7 @@ def main():
         n = rec["launches_per_step"]
         rec["algorithmic_bytes_per_launch"] = step_bytes[k] / n
         # below the ridge (peak FLOP/s over peak B/s) a kernel is HBM-bound
-        if fwd_flops / step_bytes[k] < PEAK_BF16 / PEAK_HBM:
+        if gemm_flops[k] / step_bytes[k] < PEAK_BF16 / PEAK_HBM:
             rate = step_bytes[k] / (rec["ms_per_step"] / 1e3)
             rec.update(bound="hbm", achieved_gbps=round(rate / 1e9, 1),
                        frac_hbm=round(rate / PEAK_HBM, 4))
@@ -292,6 +297,8 @@ def main():
                    "ignored_tokens": w.ignore_count,
                    **({"logit_transform": xf_vals} if has_xf else {})},
         "mfma_frac_of_step": round(step_flops / (ms / 1e3) / PEAK_BF16, 4),
+        "executed_flops_per_step": step_flops,
+        "skipped_token_tiles": f"{bwd['skipped_token_tiles']} of {bwd['token_tiles']}",
         "ms_per_step_median": round(median_ms, 4),
         "fwd_ms": round(fwd_avg, 4),
         "bwd_ms": round(bwd_avg, 4),
@@ -307,6 +314,31 @@ def main():
         line["cpu_baseline"] = cpu_baseline(x, min(args.cpu_sample_tokens, T),
                                            args.cpu_sample_vocab, xf_vals if has_xf else None)
     print(json.dumps(line), flush=True)
+
+
+def backward_flops(active, row_block: int, V: int, D: int) -> dict:
+    """FLOPs per step that the three backward GEMM kernels execute, given which tokens
+    carry a gradient (a label that is not ignored and a non-zero upstream gradient).  A
+    256-token tile without any such token is skipped by the recompute and by dH; dW runs
+    its token loop, per row block, from the first to the last tile with a gradient.  With
+    every tile active each kernel does 2TVD."""
+    import numpy as np
+
+    T = int(active.shape[0])
+    n_t = -(-T // 256)
+    pad = np.zeros(n_t * 256, dtype=bool)
+    pad[:T] = active
+    tile_any = pad.reshape(n_t, 256).any(axis=1)
+    tile_tokens = np.minimum(256, T - 256 * np.arange(n_t))
+    gd = int(tile_tokens[tile_any].sum())
+    dw = 0
+    per_rb = row_block // 256
+    for b in range(0, n_t, per_rb):
+        idx = np.nonzero(tile_any[b:b + per_rb])[0]
+        if idx.size:
+            dw += min(T, (b + idx[-1] + 1) * 256) - (b + idx[0]) * 256
+    return {"bwd_grad": 2.0 * V * D * gd, "bwd_dh": 2.0 * V * D * gd, "bwd_dw": 2.0 * V * D * dw,
+            "skipped_token_tiles": int(n_t - tile_any.sum()), "token_tiles": int(n_t)}
 
 
 def kernel_breakdown(step, steps: int, flops: dict) -> tuple:
@@ -535,11 +567,14 @@ def policy_main(args):
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    flops = 8.0 * T * V * D
+    # prompt tokens carry no label and so no gradient: the backward skips their tiles
+    bwd = backward_flops(x.labels != synth.IGNORE_INDEX,
+                         flce.describe_plan(T, D, V, chunk_rows)["row_block"], V, D)
+    gemm_flops = {"fwd_lse": 2.0 * T * V * D,
+                  **{k: bwd[k] for k in ("bwd_grad", "bwd_dh", "bwd_dw")}}
+    flops = sum(gemm_flops.values())
     achieved = flops / (ms / 1e3)
-    kernels, inst = kernel_breakdown(
-        step, max(3, min(args.steps, 10)),
-        {k: 2.0 * T * V * D for k in ("fwd_lse", "bwd_grad", "bwd_dh", "bwd_dw")})
+    kernels, inst = kernel_breakdown(step, max(3, min(args.steps, 10)), gemm_flops)
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     line = {
         "metric": f"{args.loss.upper()} loss fwd+bwd tokens/s (fused LM head, selective log-softmax)",
@@ -555,8 +590,11 @@ def policy_main(args):
         "workspace_bytes": int(ws.numel()),
         "whole_call": {"achieved": round(achieved / 1e12, 2),
                        "frac": round(achieved / PEAK_BF16, 4), "flops_per_step": flops,
-                       "note": "log-prob forward, loss kernels, recompute, dH, dW; prompt "
-                               "rows are computed too"},
+                       "skipped_token_tiles": f"{bwd['skipped_token_tiles']} of "
+                                              f"{bwd['token_tiles']}",
+                       "note": "log-prob forward, loss kernels, recompute, dH, dW: FLOPs "
+                               "executed (the forward computes the prompt rows, the backward "
+                               "skips token tiles without gradient)"},
         "roofline": {
             "kernel": dom, "bound": "mfma", "achieved": kernels[dom]["achieved"],
             "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": kernels[dom]["frac"],

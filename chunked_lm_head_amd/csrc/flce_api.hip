@@ -53,6 +53,8 @@ flce_status fail(flce_status s, const char *fmt, ...) {
 constexpr int64_t kMaxD = 1 << 16;
 constexpr int64_t kMaxTV = (int64_t)1 << 30;  // T and V each
 constexpr int64_t kRowBlockMax = 8192;
+// one bit per 256-token tile of a row block in a 32-bit mask (bwd_prep_kernel)
+static_assert(kRowBlockMax / kTile <= 32, "row block tiles exceed the tile mask");
 constexpr int64_t kFwdTargetWG = 2048;
 constexpr int64_t kDhTargetWG = 512;
 constexpr int64_t kCUs = 256;  // compute units of an MI355X (8 XCDs of 32)
@@ -69,7 +71,7 @@ struct Plan {
   int64_t R, n_rb, Vc, n_vc, dh_splits, Tb;   // backward; Tb = n_rb * R
   int64_t comb_lanes, n_cblk;  // forward combine: lanes per token, blocks
   size_t off_pm, off_ps, off_zl, off_bs, off_bc, fwd_bytes;
-  size_t off_c, off_l2, off_G, off_dh, off_ht, bwd_bytes;
+  size_t off_c, off_l2, off_mask, off_G, off_dh, off_ht, bwd_bytes;
   size_t gtile_bytes, chunk_bound;
   size_t total;
 };
@@ -167,6 +169,7 @@ flce_status make_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows, Plan 
   off = 0;
   p.off_c = off;  off = align256(off + (size_t)p.Tb * 4);
   p.off_l2 = off; off = align256(off + (size_t)p.Tb * 4);
+  p.off_mask = off; off = align256(off + (size_t)p.n_rb * 4);
   p.off_G = off;  off = align256(off + (size_t)p.R * p.Vc * 2);
   p.off_dh = off; off = align256(off + (size_t)p.dh_splits * p.R * p.D * 4);
   p.off_ht = off; off = align256(off + (size_t)p.R * p.D * 2);
@@ -402,12 +405,13 @@ flce_status launch_ht(const void *hidden, uint16_t *ht, int64_t D, int64_t R, in
 // its bf16 gradient block G: token rows of pitch Gp, gcols vocabulary columns
 // (a multiple of 256), plain or grouped (written over an fp32 block: Gp =
 // 2 gcols, each 128-column group in the first half of its fp32 bytes).  A
-// NULL dhacc skips dH, a NULL grad_weight skips dW.
+// NULL dhacc skips dH, a NULL grad_weight skips dW.  rb_mask (or NULL: no
+// skipping) marks the row block's token tiles that carry a gradient.
 flce_status launch_dh_dw(const uint16_t *G, int Gp, int64_t gcols, bool grouped,
                          const void *weight, const uint16_t *ht, int64_t D, int64_t V, int64_t R,
                          int64_t rcount, int64_t vc0, int64_t vcount, int64_t dh_splits,
                          float *dhacc, float *grad_weight, bool acc_dh, bool acc_dw,
-                         hipStream_t s) {
+                         const uint32_t *rb_mask, hipStream_t s) {
   const int tiles_h = (int)cdiv(D, kTile);
   BwdDhParams h;
   h.G = G;
@@ -424,6 +428,7 @@ flce_status launch_dh_dw(const uint16_t *G, int Gp, int64_t gcols, bool grouped,
   h.splits = (int)dh_splits;
   h.acc = dhacc;
   h.accumulate = acc_dh ? 1 : 0;
+  h.rb_mask = rb_mask;
   const unsigned dh_grid = (unsigned)(h.tiles_m * h.tiles_n * h.splits);
   if (dhacc) {
     if (grouped)
@@ -447,6 +452,7 @@ flce_status launch_dh_dw(const uint16_t *G, int Gp, int64_t gcols, bool grouped,
   w.tiles_n = tiles_h;
   w.dW = grad_weight;
   w.accumulate = acc_dw ? 1 : 0;
+  w.rb_mask = rb_mask;
   if (grouped)
     dst_dw_kernel<<<(unsigned)(w.tiles_m * w.tiles_n), kThreads, 0, s>>>(w);
   else
@@ -636,7 +642,7 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
     return launch_dh_dw(G, (int)(2 * p.Vc), p.Vc, true, student_weight, ht, Ds, V, p.R, rcount,
                         vc0, vcount, p.dh_splits, want_dh ? dhacc : nullptr,
                         want_dw ? grad_student_weight : nullptr, vc > 0,
-                        accumulate_grad_weight || rb > 0, s);
+                        accumulate_grad_weight || rb > 0, nullptr, s);
   };
   const int nparts = (int)(p.n_vc * p.vsplits);
   auto reduce = [&](int64_t rb0, int64_t rcount) -> flce_status {
@@ -996,6 +1002,7 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
   char *ws = (char *)workspace;
   float *cbuf = (float *)(ws + p.off_c);
   float *l2buf = (float *)(ws + p.off_l2);
+  uint32_t *rb_mask = (uint32_t *)(ws + p.off_mask);
   uint16_t *G = (uint16_t *)(ws + p.off_G);
   float *dhacc = (float *)(ws + p.off_dh);
   uint16_t *ht = (uint16_t *)(ws + p.off_ht);
@@ -1012,6 +1019,8 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
   pr.mode = mode;
   pr.c = cbuf;
   pr.lse2 = l2buf;
+  pr.tiles_rb = (int)(p.R / kTile);
+  pr.rb_mask = rb_mask;
   bwd_prep_kernel<<<1, 1024, 0, s>>>(pr);
   FLCE_TRY(launched(FLCE_KERNEL_BWD_PREP, s));
 
@@ -1044,6 +1053,7 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
       g.xf = xf;
       g.G = G;
       g.Gp = (int)p.Vc;
+      g.rb_mask = rb_mask + rb;
       const unsigned grid = (unsigned)(g.tiles_n * g.vsplits);
       if (cap)
         bwd_grad_kernel<true><<<grid, kThreads, 0, s>>>(g);
@@ -1053,7 +1063,7 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
 
       FLCE_TRY(launch_dh_dw(G, (int)p.Vc, p.Vc, false, weight, ht, D, V, p.R, rcount, vc0, vcount,
                             p.dh_splits, grad_hidden ? dhacc : nullptr, grad_weight, vc > 0,
-                            accumulate_grad_weight || rb > 0, s));
+                            accumulate_grad_weight || rb > 0, rb_mask + rb, s));
     }
     if (grad_hidden)
       FLCE_TRY(launch_dh_out(dhacc, grad_hidden, D, p.R, p.dh_splits, rb0, rcount, s));

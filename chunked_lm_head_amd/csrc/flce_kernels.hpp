@@ -341,6 +341,9 @@ struct BwdPrepParams {
   int T, V, T_pad, mode;
   float *c;     // [T_pad] per-token scale (0 where the row has no gradient)
   float *lse2;  // [T_pad] lse * log2(e); +inf where c == 0 so softmax terms vanish
+  int tiles_rb;        // 256-token tiles per row block (<= 32)
+  uint32_t *rb_mask;   // [T_pad / (256 tiles_rb)]: bit i set if tile i of the row block
+                       // holds a token with c != 0
 };
 
 __global__ void __launch_bounds__(1024) bwd_prep_kernel(BwdPrepParams p) {
@@ -354,6 +357,8 @@ __global__ void __launch_bounds__(1024) bwd_prep_kernel(BwdPrepParams p) {
     __syncthreads();
   }
   const int n_valid = scnt[0];
+  const int n_tiles = p.T_pad / kTile;
+  for (int b = threadIdx.x; b * p.tiles_rb < n_tiles; b += 1024) p.rb_mask[b] = 0u;
   const float sign = p.mode == 0 ? 1.f : -1.f;
   float gm = 0.f;
   if (!p.grad_out && n_valid > 0) gm = p.grad_mean[0] / (float)n_valid;
@@ -370,6 +375,18 @@ __global__ void __launch_bounds__(1024) bwd_prep_kernel(BwdPrepParams p) {
     p.c[t] = c;
     p.lse2[t] = l2;
   }
+  // Which token tiles carry any gradient, one bit per tile and a mask per row block:
+  // the backward GEMMs skip the others (their G rows are zero, so their dH rows are
+  // zero and they add nothing to dW).
+  // One wave per tile: each lane tests four of its 256 values.
+  __syncthreads();  // the block's writes of c and of the cleared masks are visible to it
+  const int lane = threadIdx.x & 63;
+  for (int tt = threadIdx.x >> 6; tt < n_tiles; tt += 1024 / 64) {
+    const f32x4 v = *(const f32x4 *)(p.c + (size_t)tt * kTile + lane * 4);
+    const bool nz = (v[0] != 0.f) | (v[1] != 0.f) | (v[2] != 0.f) | (v[3] != 0.f);
+    if (__builtin_amdgcn_ballot_w64(nz) != 0 && lane == 0)
+      atomicOr(p.rb_mask + tt / p.tiles_rb, 1u << (tt % p.tiles_rb));
+  }
 }
 
 struct BwdGradParams {
@@ -384,6 +401,7 @@ struct BwdGradParams {
   Xform xf;              // logit transform; G is the gradient with respect to the raw logits
   uint16_t *G;           // [R, Gp] bf16, row = token - rb0, col = vocab - vc0
   int Gp;
+  const uint32_t *rb_mask;  // this row block's tiles with a gradient (bwd_prep_kernel)
 };
 
 // G tiles of one row block and vocabulary chunk.  A workgroup keeps one
@@ -409,6 +427,7 @@ __global__ void __launch_bounds__(kThreads)
   const int vt1 = (int)((int64_t)(sp + 1) * p.n_vt / p.vsplits);
   const int t0 = p.rb0 + tn * kTile;
   if (t0 >= p.T || vt0 >= vt1) return;
+  const uint32_t mask = *p.rb_mask;  // read beside the per-token values below
 
   // Per-token values of this lane's 8 token columns, loaded before any DMA.
   float cc[8], l2[8];
@@ -434,6 +453,17 @@ __global__ void __launch_bounds__(kThreads)
   A.init(p.weight + (size_t)v0 * p.D, p.D, min(kTile, p.V - v0), p.D, wave, lane);
   wait_vmcnt<0>();
   __syncthreads();
+  if (!((mask >> tn) & 1u)) {
+    // No token of the tile has a gradient: its G rows are zeros (what the full
+    // computation writes for c = 0), without the GEMM.
+    const int per_row = (vt1 - vt0) * (kTile / 8);  // 16-byte chunks of a row's range
+    uint16_t *g0 = p.G + (size_t)(t0 - p.rb0) * p.Gp + vt0 * kTile;
+    for (int i = threadIdx.x; i < kTile * per_row; i += kThreads) {
+      const int r = i / per_row, ch = i - r * per_row;
+      *(u32x4 *)(g0 + (size_t)r * p.Gp + ch * 8) = u32x4{0u, 0u, 0u, 0u};
+    }
+    return;
+  }
   pipe_prologue(A, B, smem, wave);
   Acc acc;
   for (int vt = vt0; vt < vt1; ++vt) {
@@ -550,6 +580,7 @@ struct BwdDhParams {
   int tiles_m, tiles_n, splits;
   float *acc;            // [splits, R, D] fp32
   int accumulate;
+  const uint32_t *rb_mask;  // this row block's tiles with a gradient, or null (no skipping)
 };
 
 // One dH tile (split s of K): A = G rows, plain (OperandK) or grouped in
@@ -564,7 +595,7 @@ __device__ __forceinline__ void dh_tile(const BwdDhParams &p, lds_t *smem) {
   const int s = L / per_split;
   int tm, tn;
   grouped_tile(L - s * per_split, p.tiles_m, p.tiles_n, 8, tm, tn);
-
+  const uint32_t mask = p.rb_mask ? *p.rb_mask : ~0u;
   const int ktiles = (p.Kc + kBK - 1) / kBK;
   const int kbeg = (int)((int64_t)s * ktiles / p.splits) * kBK;
   const int kend = min(p.Kc, (int)((int64_t)(s + 1) * ktiles / p.splits) * kBK);
@@ -580,7 +611,25 @@ __device__ __forceinline__ void dh_tile(const BwdDhParams &p, lds_t *smem) {
          min(kend, p.vcount) - kbeg, wave, lane);
   Acc acc;
   acc.zero();
-  tile_mainloop(A, B, (kend - kbeg + kKS - 1) / kKS, smem, acc, wave, lane);
+  const int nk = (kend - kbeg + kKS - 1) / kKS;
+  // The first stages are issued before the row block's mask is looked at, so that its
+  // read overlaps their loads.
+  if (nk > 0) pipe_prologue(A, B, smem, wave);
+  if (!((mask >> tm) & 1u)) {
+    // A token tile without gradient: its dH rows are zero.  The first chunk writes the
+    // zeros, later chunks (accumulating) have nothing to add.
+    wait_vmcnt<0>();  // the issued loads still write LDS: let them land first
+    if (!p.accumulate) {
+      const int cols = min(kTile, p.D - h0);
+      float *t = p.acc + ((size_t)s * p.R + (size_t)tm * kTile) * p.D + h0;
+      for (int i = threadIdx.x; i < kTile * (cols / 4); i += kThreads) {
+        const int r = i / (cols / 4), c4 = i - r * (cols / 4);
+        *(f32x4 *)(t + (size_t)r * p.D + c4 * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    return;
+  }
+  if (nk > 0) pipe_run(A, B, nk, smem, acc, wave, lane);
 
   // rows [tm*256, tm*256 + 256) of split s, all inside the R x D slice
   const float *tile = p.acc + ((size_t)s * p.R + (size_t)tm * kTile) * p.D;
@@ -641,6 +690,7 @@ struct BwdDwParams {
   int tiles_m, tiles_n;
   float *dW;             // [V, D] fp32
   int accumulate;
+  const uint32_t *rb_mask;  // this row block's tiles with a gradient, or null (no skipping)
 };
 
 // One dW tile: A = G^T, plain (OperandMN) or grouped (OperandMNG).
@@ -655,14 +705,41 @@ __device__ __forceinline__ void dw_tile(const BwdDwParams &p, lds_t *smem) {
   if (v0 >= p.V) return;  // the whole tile lies past the vocabulary
   const int h0 = tn * kTile;
 
-  OA A;            // G^T: G[k = token][m = vocabulary]
-  A.init(p.G + (OA::kGrouped ? grouped_col(tm * kTile) : tm * kTile), p.Gp, kTile, p.rcount,
-         wave, lane);
-  OperandK B;      // H^T[h0 + n][k = token], K-contiguous; zeros past rcount
-  B.init(p.ht + (size_t)h0 * p.R, p.R, min(kTile, p.D - h0), (p.rcount + 7) & ~7, wave, lane);
+  const uint32_t mask = p.rb_mask ? *p.rb_mask : ~0u;
+
+  // G^T: G[k = token][m = vocabulary]; H^T[h0 + n][k = token], K-contiguous, zeros past
+  // rcount.  K (tokens) [kbeg, kend) starts as the whole row block.
+  const uint16_t *g_col = p.G + (OA::kGrouped ? grouped_col(tm * kTile) : tm * kTile);
+  const uint16_t *ht_row = p.ht + (size_t)h0 * p.R;
+  const int hrows = min(kTile, p.D - h0);
+  OA A;
+  A.init(g_col, p.Gp, kTile, p.rcount, wave, lane);
+  OperandK B;
+  B.init(ht_row, p.R, hrows, (p.rcount + 7) & ~7, wave, lane);
   Acc acc;
   acc.zero();
-  tile_mainloop(A, B, (p.rcount + kKS - 1) / kKS, smem, acc, wave, lane);
+  int nk = (p.rcount + kKS - 1) / kKS;
+  if (nk > 0) pipe_prologue(A, B, smem, wave);
+  // K runs from the first to the last token tile with a gradient: the G rows outside
+  // add exact zeros (inside, the recompute wrote zeros for tiles without gradient).
+  // The mask is looked at after the first stages are issued, so that its read overlaps
+  // their loads; a narrower range drains them and starts again.
+  const int nt = (p.rcount + kTile - 1) / kTile;
+  const uint32_t m = mask & (nt >= 32 ? ~0u : (1u << nt) - 1u);
+  const int kbeg = m ? __builtin_ctz(m) * kTile : 0;
+  const int kend = m ? min(p.rcount, (32 - __builtin_clz(m)) * kTile) : 0;
+  if (kbeg != 0 || kend != p.rcount) {
+    wait_vmcnt<0>();  // the issued loads still write LDS: let them land first
+    __syncthreads();
+    nk = (kend - kbeg + kKS - 1) / kKS;
+    if (nk <= 0 && p.accumulate) return;  // nothing to add to dW
+    if (nk > 0) {
+      A.init(g_col + (size_t)kbeg * p.Gp, p.Gp, kTile, kend - kbeg, wave, lane);
+      B.init(ht_row + kbeg, p.R, hrows, ((kend + 7) & ~7) - kbeg, wave, lane);
+      pipe_prologue(A, B, smem, wave);
+    }
+  }
+  if (nk > 0) pipe_run(A, B, nk, smem, acc, wave, lane);
 
   // rows [v0, min(V, v0 + 256)) of dW
   const uint32_t rows = (uint32_t)min(kTile, p.V - v0);

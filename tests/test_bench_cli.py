@@ -31,3 +31,50 @@ def test_bad_token_shards_are_refused(args, msg):
     r = _bench(*args)
     assert r.returncode != 0
     assert msg in r.stderr
+
+
+def _bench_module():
+    sys.path.insert(0, ROOT)
+    import bench
+    return bench
+
+
+def test_backward_flops_count_the_tiles_that_run():
+    """Executed backward FLOPs when token tiles without gradient are skipped: counted here
+    token by token (a token's tile runs if any token of its 256 has a gradient; dW's
+    token loop spans, per row block, the first to the last such tile)."""
+    import numpy as np
+
+    bench = _bench_module()
+    V, D = 1000, 64
+    rng = np.random.default_rng(5)
+    cases = [
+        (np.ones(2600, bool), 2816),                               # all active
+        (np.zeros(700, bool), 768),                                # nothing active
+        (np.ones(2600, bool), 256),                                # one-tile row blocks
+    ]
+    a = np.ones(2600, bool)
+    for t in (0, 1, 5, 10):                                        # holes incl. ragged tail
+        a[t * 256:(t + 1) * 256] = False
+    cases.append((a, 2816))
+    b = rng.random(5000) < 0.002                                   # sparse: most tiles empty
+    cases += [(b, 1024), (b, 4096)]
+    for active, R in cases:
+        T = active.shape[0]
+        got = bench.backward_flops(active, R, V, D)
+        tile_on = [active[(t // 256) * 256:(t // 256 + 1) * 256].any() for t in range(T)]
+        gd = sum(tile_on)
+        dw = 0
+        for r0 in range(0, T, R):
+            on = [t for t in range(r0, min(T, r0 + R)) if tile_on[t]]
+            if on:
+                dw += min(T, (on[-1] // 256 + 1) * 256) - (on[0] // 256) * 256
+        assert got["bwd_grad"] == got["bwd_dh"] == 2.0 * V * D * gd
+        assert got["bwd_dw"] == 2.0 * V * D * dw
+        assert got["token_tiles"] == -(-T // 256)
+        if active.all():
+            assert got["bwd_grad"] == got["bwd_dw"] == 2.0 * T * V * D
+    # the holes case by hand: 7 full tiles run; dW spans tiles 2..9
+    got = bench.backward_flops(a, 2816, V, D)
+    assert got["bwd_grad"] == 2.0 * V * D * 7 * 256 and got["bwd_dw"] == 2.0 * V * D * 2048
+    assert got["skipped_token_tiles"] == 4
