@@ -1,0 +1,81 @@
+"""HIP path vs the CPU oracle on seeded random shapes: sizes, chunking, ignored fractions,
+modes, reductions (per-token upstream gradients with zeroed prompt spans, which makes whole
+256-token tiles gradient-free), weight scales and logit transforms drawn together, so that
+combinations the hand-picked cases do not name are covered too.  Same tolerances as the
+other parity tests: per-token output, lse and mean within 2e-3 absolute, dH and dW within
+1e-2 relative Frobenius error; ignored tokens give exactly zero output and dH rows."""
+import numpy as np
+import pytest
+
+from chunked_lm_head_amd import synth
+from oracle import flce_oracle as o
+
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+IGN = synth.IGNORE_INDEX
+N_CASES = 24
+MAX_WORK = 6e9        # T * V * D, so that the float64 oracle takes about a second per case
+
+
+def _log_uniform(rng, lo, hi):
+    return int(round(np.exp(rng.uniform(np.log(lo), np.log(hi)))))
+
+
+def _cases():
+    rng = np.random.default_rng(20261202)
+    out = []
+    while len(out) < N_CASES:
+        # most cases span several 256-wide tiles in both T and V, with ragged tails
+        T = _log_uniform(rng, 1, 6000) if rng.random() < 0.3 else int(rng.integers(257, 6000))
+        V = _log_uniform(rng, 1, 12000) if rng.random() < 0.3 else int(rng.integers(257, 12000))
+        D = 8 * _log_uniform(rng, 1, 160)
+        if T * V * D > MAX_WORK:
+            continue
+        cr = int(rng.choice([1, 7, 16, 64, 256, 1024, 4096]))
+        ign = float(rng.choice([0.0, 0.05, 0.5, 1.0], p=[0.4, 0.3, 0.2, 0.1]))
+        mode = str(rng.choice(["nll", "logprob"]))
+        red = str(rng.choice(["mean", "none"]))
+        w_std = [None, 0.02, 1.0][int(rng.integers(3))]
+        tr = None
+        if rng.random() < 0.3:
+            tr = (float(rng.choice([0.0, 1.7])), float(rng.choice([0.0, 2.3])),
+                  float(rng.choice([0.0, 2.0, 30.0])), float(rng.choice([1.0, 0.6, 1.5])))
+        out.append((f"r{len(out):02d}", T, D, V, cr, ign, mode, red, w_std, tr))
+    return out
+
+
+CASES = _cases()
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_random_shape_parity(case):
+    name, T, D, V, cr, ign, mode, red, w_std, tr = case
+    print(f"case {name}: T {T} D {D} V {V} chunk_rows {cr} ignore {ign} {mode} {red} "
+          f"w_std {w_std} transform {tr}", flush=True)
+    kw = {}
+    if red == "none":   # zero upstream gradient on the first 300 of every 700 tokens
+        kw = dict(seq_len=700, prompt_len=300)
+    w = synth.custom(name, T=T, H=D, V=V, chunk_rows=cr, ignore_frac=ign, mode=mode,
+                     reduction=red, w_std=w_std, seed=int(name[1:]) + 500, **kw)
+    x = synth.make_inputs(w)
+    r = gu.run(x, transform=tr)
+    otr = o.LogitTransform(*tr) if tr is not None else None
+    f = o.forward(x.hidden, x.weight, x.labels, IGN, mode, transform=otr)
+    if x.grad_out is not None:
+        dh, dw = o.backward(x.hidden, x.weight, x.labels, IGN, mode, grad_out=x.grad_out,
+                            transform=otr)
+    else:
+        dh, dw = o.backward(x.hidden, x.weight, x.labels, IGN, mode, grad_mean=1.0,
+                            transform=otr)
+    e = (gu.max_abs(r["out"], f.out), gu.max_abs(r["lse"], f.lse), abs(r["mean"] - f.mean),
+         gu.rel_fro(r["dh"], dh), gu.rel_fro(r["dw"], dw))
+    print(f"  |d out| {e[0]:.2e} |d lse| {e[1]:.2e} |d mean| {e[2]:.2e} dH rel {e[3]:.2e} "
+          f"dW rel {e[4]:.2e}", flush=True)
+    assert e[0] <= gu.OUT_TOL and e[2] <= gu.OUT_TOL, e
+    assert e[3] <= gu.GRAD_TOL and e[4] <= gu.GRAD_TOL, e
+    ignored = x.labels == IGN
+    # lse is defined for every token, ignored ones included
+    assert e[1] <= gu.OUT_TOL, e
+    assert np.all(r["out"][ignored] == 0.0) and np.all(r["dh"][ignored] == 0.0)
