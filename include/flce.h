@@ -167,7 +167,10 @@ flce_status flce_forward_noalloc(const void *hidden, const void *weight, const i
  * grad_hidden skips the dH products, a NULL grad_weight skips the dW products
  * (a frozen lm_head); both NULL is FLCE_ERR_ARG.  lse must be the forward's
  * output for the same inputs and transform.  T == 0 is valid: grad_weight (if
- * given) is zeroed unless accumulating.
+ * given) is zeroed unless accumulating.  A tile of 256 consecutive tokens in
+ * which every c_t is 0 (prompt tokens of a policy loss, say) skips the GEMMs:
+ * its grad_hidden rows are written as zeros and it adds nothing to grad_weight,
+ * exactly what computing it gives.
  */
 flce_status flce_backward(const void *hidden, const void *weight, const int64_t *labels,
                           const float *lse, int64_t T, int64_t D, int64_t V,
