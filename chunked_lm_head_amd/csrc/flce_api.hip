@@ -56,7 +56,10 @@ constexpr int64_t kRowBlockMax = 8192;
 // one bit per 256-token tile of a row block in a 32-bit mask (bwd_prep_kernel)
 static_assert(kRowBlockMax / kTile <= 32, "row block tiles exceed the tile mask");
 constexpr int64_t kFwdTargetWG = 2048;
-constexpr int64_t kDhTargetWG = 512;
+// dH split-K target: about one workgroup per CU.  Where a row block has fewer dH tiles
+// than CUs (short token shares, one-tile batches), more splits mean more partial sums
+// for bwd_dh_out to read, and two rounds of workgroups measured slower than one.
+constexpr int64_t kDhTargetWG = 256;
 constexpr int64_t kCUs = 256;  // compute units of an MI355X (8 XCDs of 32)
 constexpr int64_t kDhPartialCap = (int64_t)128 << 20;  // bytes of split-K partial sums
 constexpr int64_t kI32Bytes = ((int64_t)1 << 31) - 1;
