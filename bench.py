@@ -567,10 +567,12 @@ def policy_main(args):
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    # prompt tokens carry no label and so no gradient: the backward skips their tiles
+    # prompt tokens carry no label and so no gradient: the backward skips their tiles, and
+    # so does the log-prob forward (nothing needs their log-probs), the same tiles as the
+    # recompute's
     bwd = backward_flops(x.labels != synth.IGNORE_INDEX,
                          flce.describe_plan(T, D, V, chunk_rows)["row_block"], V, D)
-    gemm_flops = {"fwd_lse": 2.0 * T * V * D,
+    gemm_flops = {"fwd_lse": bwd["bwd_grad"],
                   **{k: bwd[k] for k in ("bwd_grad", "bwd_dh", "bwd_dw")}}
     flops = sum(gemm_flops.values())
     achieved = flops / (ms / 1e3)
@@ -593,8 +595,8 @@ def policy_main(args):
                        "skipped_token_tiles": f"{bwd['skipped_token_tiles']} of "
                                               f"{bwd['token_tiles']}",
                        "note": "log-prob forward, loss kernels, recompute, dH, dW: FLOPs "
-                               "executed (the forward computes the prompt rows, the backward "
-                               "skips token tiles without gradient)"},
+                               "executed (token tiles holding prompt tokens only are skipped "
+                               "by the forward and the backward)"},
         "roofline": {
             "kernel": dom, "bound": "mfma", "achieved": kernels[dom]["achieved"],
             "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": kernels[dom]["frac"],

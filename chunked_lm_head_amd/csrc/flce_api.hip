@@ -297,7 +297,8 @@ const char *kernel_name(int id) {
       "?",           "fwd_lse",     "fwd_combine", "fwd_mean",    "bwd_prep",
       "bwd_ht",      "bwd_grad",    "bwd_dh",      "bwd_dw",      "bwd_dh_out",
       "fill",        "dst_lse",     "dst_prep",    "dst_teacher", "dst_student",
-      "dst_reduce",  "dst_dh",      "dst_dw",      "dst_combine", "policy"};
+      "dst_reduce",  "dst_dh",      "dst_dw",      "dst_combine", "policy",
+      "fwd_skip_prep"};
   return id > 0 && id < FLCE_KERNEL_COUNT ? names[id] : "?";
 }
 
@@ -390,10 +391,13 @@ flce_status make_xform(const flce_logit_transform *t, Xform &x, bool &cap) {
   return FLCE_OK;
 }
 
+// Every kernel parameter block below is value-initialised ({}), so a field that a
+// launch does not set is zero (null pointers, flags off).
+
 // H^T of a row block for the dW kernel's K-contiguous operand.
 flce_status launch_ht(const void *hidden, uint16_t *ht, int64_t D, int64_t R, int64_t rb0,
                       int64_t rcount, hipStream_t s) {
-  BwdHtParams t;
+  BwdHtParams t{};
   t.hidden = (const uint16_t *)hidden;
   t.ht = ht;
   t.D = (int)D;
@@ -416,7 +420,7 @@ flce_status launch_dh_dw(const uint16_t *G, int Gp, int64_t gcols, bool grouped,
                          float *dhacc, float *grad_weight, bool acc_dh, bool acc_dw,
                          const uint32_t *rb_mask, hipStream_t s) {
   const int tiles_h = (int)cdiv(D, kTile);
-  BwdDhParams h;
+  BwdDhParams h{};
   h.G = G;
   h.weight = (const uint16_t *)weight;
   h.Gp = Gp;
@@ -442,7 +446,7 @@ flce_status launch_dh_dw(const uint16_t *G, int Gp, int64_t gcols, bool grouped,
   }
   if (!grad_weight) return FLCE_OK;
 
-  BwdDwParams w;
+  BwdDwParams w{};
   w.G = G;
   w.ht = ht;
   w.Gp = Gp;
@@ -466,7 +470,7 @@ flce_status launch_dh_dw(const uint16_t *G, int Gp, int64_t gcols, bool grouped,
 // dH rows of a row block: sum of the split-K partials, rounded to bf16.
 flce_status launch_dh_out(const float *dhacc, void *grad_hidden, int64_t D, int64_t R,
                           int64_t dh_splits, int64_t rb0, int64_t rcount, hipStream_t s) {
-  BwdDhOutParams o;
+  BwdDhOutParams o{};
   o.acc = dhacc;
   o.dH = (uint16_t *)grad_hidden;
   o.D = (int)D;
@@ -551,7 +555,7 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
 
   // Log-sum-exp of each head: the fused forward kernel without labels.
   for (int head = 0; head < 2; ++head) {
-    FwdLseParams a;
+    FwdLseParams a{};
     a.hidden = (const uint16_t *)(head ? student_hidden : teacher_hidden);
     a.weight = (const uint16_t *)(head ? student_weight : teacher_weight);
     a.labels = nullptr;
@@ -572,7 +576,7 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
     else
       fwd_lse_kernel<false><<<(unsigned)(p.n_tt * p.splits), kThreads, 0, s>>>(a);
     FLCE_TRY(launched(FLCE_KERNEL_FWD_LSE, s));
-    DstLseParams l;
+    DstLseParams l{};
     l.part_m = a.part_m;
     l.part_s = a.part_s;
     l.T = (int)T;
@@ -586,7 +590,7 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
     FLCE_TRY(launched(FLCE_KERNEL_DST_LSE, s));
   }
 
-  DstPrepParams pr;
+  DstPrepParams pr{};
   pr.labels = labels;
   pr.grad_out = grad_out;
   pr.grad_mean = grad_mean;
@@ -603,7 +607,7 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
     const int64_t vc0 = vc * p.Vc;
     const int64_t vcount = std::min<int64_t>(p.Vc, V - vc0);
     const bool teacher = role == kRoleTeacher;
-    DstTileParams d;
+    DstTileParams d{};
     d.hidden = (const uint16_t *)(teacher ? teacher_hidden : student_hidden);
     d.weight = (const uint16_t *)(teacher ? teacher_weight : student_weight);
     d.lse2 = teacher ? l2t : l2s;
@@ -690,7 +694,7 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
       FLCE_TRY(launch_dh_out(dhacc, grad_student_hidden, Ds, p.R, p.dh_splits, rb0, rcount, s));
   }
 
-  DstCombineParams c;
+  DstCombineParams c{};
   c.jsd = jsd ? 1 : 0;
   c.A = Abuf;
   c.B = Bbuf;
@@ -736,12 +740,32 @@ flce_status forward_checks(const void *hidden, const void *weight, const int64_t
 flce_status forward_launch(const Plan &p, const Xform &xf, bool cap, const void *hidden,
                            const void *weight, const int64_t *labels, int64_t ignore_index,
                            int mode, float *out, float *lse, float *mean_out, char *ws,
-                           hipStream_t s) {
+                           hipStream_t s, char *skip_buf = nullptr) {
   const int64_t T = p.T, D = p.D, V = p.V;
   timing_start(s);
   if (T == 0) return mean_out ? fill(mean_out, 1, 0.f, s) : FLCE_OK;
 
-  FwdLseParams a;
+  // skip_buf (4 + 5 n_tt bytes, 4-aligned): the count and list of the token tiles with a
+  // label, then a flag per tile; tiles whose labels are all ignore_index are left out.
+  int *n_act = nullptr, *act_list = nullptr;
+  uint8_t *tile_act = nullptr;
+  if (skip_buf && labels) {
+    n_act = (int *)skip_buf;
+    act_list = n_act + 1;
+    tile_act = (uint8_t *)(act_list + p.n_tt);
+    FwdSkipPrepParams q{};
+    q.labels = labels;
+    q.ignore_index = ignore_index;
+    q.T = (int)T;
+    q.n_tt = (int)p.n_tt;
+    q.tile_act = tile_act;
+    q.act_list = act_list;
+    q.n_act = n_act;
+    fwd_skip_prep_kernel<<<1, 1024, 0, s>>>(q);
+    FLCE_TRY(launched(FLCE_KERNEL_FWD_SKIP_PREP, s));
+  }
+
+  FwdLseParams a{};
   a.hidden = (const uint16_t *)hidden;
   a.weight = (const uint16_t *)weight;
   a.labels = labels;
@@ -757,16 +781,19 @@ flce_status forward_launch(const Plan &p, const Xform &xf, bool cap, const void 
   a.part_m = (float *)(ws + p.off_pm);
   a.part_s = (float *)(ws + p.off_ps);
   a.zlab = (float *)(ws + p.off_zl);
+  a.act_list = act_list;
+  a.n_act = n_act;
   if (cap)
     fwd_lse_kernel<true><<<(unsigned)(p.n_tt * p.splits), kThreads, 0, s>>>(a);
   else
     fwd_lse_kernel<false><<<(unsigned)(p.n_tt * p.splits), kThreads, 0, s>>>(a);
   FLCE_TRY(launched(FLCE_KERNEL_FWD_LSE, s));
 
-  FwdCombineParams c;
+  FwdCombineParams c{};
   c.part_m = a.part_m;
   c.part_s = a.part_s;
   c.zlab = a.zlab;
+  c.tile_act = tile_act;
   c.labels = labels;
   c.ignore_index = ignore_index;
   c.T = (int)T;
@@ -916,12 +943,15 @@ flce_status flce_timing_end(int32_t *ids, float *ms, int32_t capacity, int32_t *
   return st;
 }
 
-flce_status flce_forward(const void *hidden, const void *weight, const int64_t *labels,
-                         int64_t T, int64_t D, int64_t V, int64_t ignore_index,
-                         int64_t chunk_rows, int mode, const flce_logit_transform *transform,
-                         float *out, float *lse, float *mean_out,
-                         void *workspace, size_t workspace_bytes, void *stream) {
-  g_last_error[0] = 0;
+// flce_forward, or (skip_buf non-null: 4 + 5 ceil(T / 256) bytes of scratch) the same
+// with the token tiles whose labels are all ignore_index left out: their out is 0 as
+// always, their lse -inf.
+static flce_status forward_entry(const void *hidden, const void *weight, const int64_t *labels,
+                                 int64_t T, int64_t D, int64_t V, int64_t ignore_index,
+                                 int64_t chunk_rows, int mode,
+                                 const flce_logit_transform *transform, float *out, float *lse,
+                                 float *mean_out, void *workspace, size_t workspace_bytes,
+                                 void *stream, char *skip_buf) {
   Plan p;
   Xform xf;
   bool cap;
@@ -937,7 +967,18 @@ flce_status flce_forward(const void *hidden, const void *weight, const int64_t *
   }
   FLCE_TRY(check_device());
   return forward_launch(p, xf, cap, hidden, weight, labels, ignore_index, mode, out, lse,
-                        mean_out, (char *)workspace, (hipStream_t)stream);
+                        mean_out, (char *)workspace, (hipStream_t)stream, skip_buf);
+}
+
+flce_status flce_forward(const void *hidden, const void *weight, const int64_t *labels,
+                         int64_t T, int64_t D, int64_t V, int64_t ignore_index,
+                         int64_t chunk_rows, int mode, const flce_logit_transform *transform,
+                         float *out, float *lse, float *mean_out,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+  g_last_error[0] = 0;
+  return forward_entry(hidden, weight, labels, T, D, V, ignore_index, chunk_rows, mode,
+                       transform, out, lse, mean_out, workspace, workspace_bytes, stream,
+                       nullptr);
 }
 
 flce_status flce_forward_noalloc(const void *hidden, const void *weight, const int64_t *labels,
@@ -1010,7 +1051,7 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
   float *dhacc = (float *)(ws + p.off_dh);
   uint16_t *ht = (uint16_t *)(ws + p.off_ht);
 
-  BwdPrepParams pr;
+  BwdPrepParams pr{};
   pr.labels = labels;
   pr.lse = lse;
   pr.grad_out = grad_out;
@@ -1037,7 +1078,7 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
       const int64_t vcount = std::min<int64_t>(p.Vc, V - vc0);
       if (vcount <= 0) break;
 
-      BwdGradParams g;
+      BwdGradParams g{};
       g.hidden = (const uint16_t *)hidden;
       g.weight = (const uint16_t *)weight;
       g.labels = labels;
@@ -1266,10 +1307,14 @@ flce_status policy_loss(int kind, const PolicyInputs &in, const flce_policy_para
   char *ws = (char *)workspace;
   float *logp = logp_out ? logp_out : (float *)(ws + l.off_logp);
   float *lse = (float *)(ws + l.off_lse);
-  FLCE_TRY(flce_forward(hidden, weight, labels, T, D, V, ignore_index, chunk_rows,
-                        FLCE_MODE_LOGPROB, transform, logp, lse, nullptr, workspace, l.flce,
-                        stream));
-  PolicyParams pp;
+  // Non-completion tokens need neither a log-prob nor an lse: tiles holding only those
+  // are left out here as in the backward.  Their list borrows the per-token gradient
+  // buffer (align256(4 T) >= 4 + 5 ceil(T / 256) bytes), which the loss kernels write
+  // only after the forward has read the list.
+  FLCE_TRY(forward_entry(hidden, weight, labels, T, D, V, ignore_index, chunk_rows,
+                         FLCE_MODE_LOGPROB, transform, logp, lse, nullptr, workspace, l.flce,
+                         stream, ws + l.off_c));
+  PolicyParams pp{};
   pp.labels = labels;
   pp.ignore_index = ignore_index;
   pp.T = (int)T;

@@ -107,6 +107,8 @@ struct FwdLseParams {
   float *part_m;            // [splits, T_pad] running max of z*log2(e)
   float *part_s;            // [splits, T_pad] sum of 2^(z*log2(e) - max)
   float *zlab;              // [T_pad] logit of the label
+  const int *act_list;      // token tiles to compute (fwd_skip_prep_kernel), or null: all
+  const int *n_act;         // their count
 };
 
 constexpr int kLdsFwd = kPipeBytes;  // the partial-merge exchange reuses the ring
@@ -120,8 +122,18 @@ __global__ void __launch_bounds__(kThreads)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
+  // With a tile list, the first n_act * splits workgroups take the listed tiles, spread
+  // over the XCDs as the whole grid would be (a workgroup's XCD is its index mod 8),
+  // and the rest exit: the work stays balanced whichever tiles drop out.
+  int n_rows = p.n_tt, n_wg = (int)gridDim.x;
+  if (p.act_list) {
+    n_rows = *p.n_act;
+    n_wg = n_rows * p.splits;
+    if ((int)blockIdx.x >= n_wg) return;
+  }
   int tt, sp;
-  grouped_tile(xcd_contiguous(blockIdx.x, gridDim.x), p.n_tt, p.splits, 8, tt, sp);
+  grouped_tile(xcd_contiguous(blockIdx.x, n_wg), n_rows, p.splits, 8, tt, sp);
+  if (p.act_list) tt = p.act_list[tt];
   const int vt0 = (int)((int64_t)sp * p.n_vt / p.splits);
   const int vt1 = (int)((int64_t)(sp + 1) * p.n_vt / p.splits);
   const int t0 = tt * kTile;
@@ -236,8 +248,55 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
+// The token tiles holding at least one token whose label is not ignore_index, in
+// order, for a forward that leaves the others out: act_list[0, *n_act) and a flag per
+// tile.  One block; a wave tests a tile (four labels per lane), then a block-wide scan
+// numbers the active tiles of each group of 1024.
+struct FwdSkipPrepParams {
+  const int64_t *labels;
+  int64_t ignore_index;
+  int T, n_tt;
+  uint8_t *tile_act;  // [n_tt]
+  int *act_list;      // [n_tt]
+  int *n_act;
+};
+
+__global__ void __launch_bounds__(1024) fwd_skip_prep_kernel(FwdSkipPrepParams p) {
+  __shared__ int scan[1024];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int tt = wave; tt < p.n_tt; tt += 1024 / 64) {
+    int any = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = tt * kTile + lane * 4 + j;
+      if (t < p.T) any |= p.labels[t] != p.ignore_index;
+    }
+    const bool act = __builtin_amdgcn_ballot_w64(any) != 0;
+    if (lane == 0) p.tile_act[tt] = act;
+  }
+  __syncthreads();  // the block's flag stores are visible to it
+  int base = 0;
+  for (int g = 0; g < p.n_tt; g += 1024) {
+    const int tt = g + (int)threadIdx.x;
+    const int f = tt < p.n_tt ? p.tile_act[tt] : 0;
+    scan[threadIdx.x] = f;
+    __syncthreads();
+    for (int w = 1; w < 1024; w <<= 1) {  // inclusive Hillis-Steele scan
+      const int v = (int)threadIdx.x >= w ? scan[threadIdx.x - w] : 0;
+      __syncthreads();
+      scan[threadIdx.x] += v;
+      __syncthreads();
+    }
+    if (f) p.act_list[base + scan[threadIdx.x] - 1] = tt;
+    base += scan[1023];
+    __syncthreads();  // scan[1023] read by all before the next group overwrites it
+  }
+  if (threadIdx.x == 0) *p.n_act = base;
+}
+
 struct FwdCombineParams {
   const float *part_m, *part_s, *zlab;
+  const uint8_t *tile_act;  // token tiles the forward computed, or null: all
   const int64_t *labels;
   int64_t ignore_index;
   int T, V, splits, T_pad, mode;
@@ -261,8 +320,8 @@ __global__ void __launch_bounds__(256) fwd_combine_kernel(FwdCombineParams p) {
   int cnt = 0;
   {
     const int t = blockIdx.x * per + g;
-    float M = -kInf, S = 0.f;
-    if (t < p.T) {
+    float M = -kInf, S = 0.f;  // a tile left out keeps the empty sum: lse -inf
+    if (t < p.T && (!p.tile_act || p.tile_act[t / kTile])) {
       for (int s = j; s < p.splits; s += L)
         lse_merge(M, S, p.part_m[(size_t)s * p.T_pad + t], p.part_s[(size_t)s * p.T_pad + t]);
     }

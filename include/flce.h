@@ -419,7 +419,8 @@ enum {
   FLCE_KERNEL_DST_DW = 17,        /* distillation: dW update */
   FLCE_KERNEL_DST_COMBINE = 18,   /* distillation: per-token divergence */
   FLCE_KERNEL_POLICY = 19,        /* policy losses: the loss kernels (2 or 3 launches) */
-  FLCE_KERNEL_COUNT = 20
+  FLCE_KERNEL_FWD_SKIP_PREP = 20, /* policy losses: list of the token tiles with a label */
+  FLCE_KERNEL_COUNT = 21
 };
 
 flce_status flce_timing_begin(int32_t capacity);

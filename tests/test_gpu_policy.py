@@ -39,8 +39,11 @@ CASES = [
      dict(beta=0.3, empty=1)),
     ("grpo_many_sequences", "grpo", (2048, 8, 2, 64, 300, 256), dict(beta=0.3)),
     ("grpo_long_sequence", "grpo", (1, 70000, 1000, 64, 300, 256), dict(beta=0.3)),
+    # prompts spanning whole 256-token tiles, which the forward and the backward skip
+    ("grpo_prompt_tiles", "grpo", (4, 1024, 600, 136, 3001, 256), dict(beta=0.04)),
     ("dpo", "dpo", (4, 300, 50, 256, 5000, 64), dict(beta=0.1)),
     ("dpo_many_pairs", "dpo", (1200, 16, 4, 64, 300, 256), dict(beta=0.5)),
+    ("dpo_prompt_tiles", "dpo", (2, 1536, 700, 128, 2000, 64), dict(beta=0.1)),
     ("dpo_scaled", "dpo", (2, 260, 60, 200, 3001, 256),
      dict(beta=0.2, transform=(1.3, 0.0, 0.0, 0.7))),
     ("kto", "kto", (5, 260, 60, 200, 3001, 256),
@@ -49,6 +52,10 @@ CASES = [
     ("kto_negative_reference_point", "kto", (1500, 8, 2, 64, 300, 256),
      dict(beta=0.5, kl_ref=-1.0, wd=0.8, wu=1.2)),
 ]
+
+
+def _case(name):
+    return next(c for c in CASES if c[0] == name)
 
 
 def _kink_free(lp, old, eps_low, eps_high, mask):
@@ -171,7 +178,7 @@ def test_policy_parity(case):
 
 
 def test_forward_only_and_accumulate():
-    case = CASES[0]
+    case = _case("grpo_ragged")
     _, kind, _, opt = case
     x, labels, tr, side = _prepare(case)
     full = _run(kind, x, labels, tr, side, opt)
@@ -183,7 +190,7 @@ def test_forward_only_and_accumulate():
 
 
 def test_repeat_calls_give_identical_bits():
-    case = CASES[7]  # DPO
+    case = _case("dpo")
     _, kind, _, opt = case
     x, labels, tr, side = _prepare(case)
     a = _run(kind, x, labels, tr, side, opt)
@@ -212,7 +219,7 @@ def test_autograd_wrappers():
     from chunked_lm_head_amd import flce
 
     dev = gu.device()
-    for case in (CASES[0], CASES[7], CASES[10]):  # GRPO, DPO, KTO
+    for case in (_case("grpo_ragged"), _case("dpo"), _case("kto")):
         _, kind, _, opt = case
         x, labels, tr, side = _prepare(case)
         want, dh, dw = _oracle(kind, x, labels, tr, side, opt)   # upstream GRAD_LOSS

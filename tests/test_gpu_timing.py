@@ -135,8 +135,9 @@ def test_timing_of_a_policy_loss_and_the_allocation_free_forward():
         assert (r is None and t is None) or torch.equal(r, t)
     names = [k for k, _ in rows]
     plan = flce.describe_plan(w.T, w.H, w.V, w.chunk_rows)
-    # log-prob forward, the loss kernels, the log-prob backward, then the second forward
-    want = (["fwd_lse", "fwd_combine", "policy", "bwd_prep"]
+    # the tile list and log-prob forward, the loss kernels, the log-prob backward, then the
+    # second forward
+    want = (["fwd_skip_prep", "fwd_lse", "fwd_combine", "policy", "bwd_prep"]
             + (["bwd_ht"] + ["bwd_grad", "bwd_dh", "bwd_dw"] * plan["vocab_chunks"]
                + ["bwd_dh_out"]) * plan["row_blocks"]
             + ["fwd_lse", "fwd_combine"])
