@@ -41,6 +41,8 @@ CASES = [
     ("grpo_long_sequence", "grpo", (1, 70000, 1000, 64, 300, 256), dict(beta=0.3)),
     # prompts spanning whole 256-token tiles, which the forward and the backward skip
     ("grpo_prompt_tiles", "grpo", (4, 1024, 600, 136, 3001, 256), dict(beta=0.04)),
+    # more than 1,024 token tiles: the forward's tile list is numbered in several groups
+    ("grpo_many_tiles", "grpo", (2, 140000, 1000, 32, 300, 256), dict(beta=0.3)),
     ("dpo", "dpo", (4, 300, 50, 256, 5000, 64), dict(beta=0.1)),
     ("dpo_many_pairs", "dpo", (1200, 16, 4, 64, 300, 256), dict(beta=0.5)),
     ("dpo_prompt_tiles", "dpo", (2, 1536, 700, 128, 2000, 64), dict(beta=0.1)),
