@@ -319,9 +319,9 @@ def main():
 def backward_flops(active, row_block: int, V: int, D: int) -> dict:
     """FLOPs per step that the three backward GEMM kernels execute, given which tokens
     carry a gradient (a label that is not ignored and a non-zero upstream gradient).  A
-    256-token tile without any such token is skipped by the recompute and by dH; dW runs
-    its token loop, per row block, from the first to the last tile with a gradient.  With
-    every tile active each kernel does 2TVD."""
+    256-token tile without any such token is left out of the recompute, dH and dW: the
+    tiles with a gradient are packed into the leading row blocks.  With every tile active
+    each kernel does 2TVD.  (row_block is the planner's, kept for the caller's record.)"""
     import numpy as np
 
     T = int(active.shape[0])
@@ -331,14 +331,10 @@ def backward_flops(active, row_block: int, V: int, D: int) -> dict:
     tile_any = pad.reshape(n_t, 256).any(axis=1)
     tile_tokens = np.minimum(256, T - 256 * np.arange(n_t))
     gd = int(tile_tokens[tile_any].sum())
-    dw = 0
-    per_rb = row_block // 256
-    for b in range(0, n_t, per_rb):
-        idx = np.nonzero(tile_any[b:b + per_rb])[0]
-        if idx.size:
-            dw += min(T, (b + idx[-1] + 1) * 256) - (b + idx[0]) * 256
-    return {"bwd_grad": 2.0 * V * D * gd, "bwd_dh": 2.0 * V * D * gd, "bwd_dw": 2.0 * V * D * dw,
-            "skipped_token_tiles": int(n_t - tile_any.sum()), "token_tiles": int(n_t)}
+    f = 2.0 * V * D * gd
+    return {"bwd_grad": f, "bwd_dh": f, "bwd_dw": f,
+            "skipped_token_tiles": int(n_t - tile_any.sum()), "token_tiles": int(n_t),
+            "row_block": int(row_block)}
 
 
 def kernel_breakdown(step, steps: int, flops: dict) -> tuple:

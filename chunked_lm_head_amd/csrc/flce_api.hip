@@ -53,8 +53,6 @@ flce_status fail(flce_status s, const char *fmt, ...) {
 constexpr int64_t kMaxD = 1 << 16;
 constexpr int64_t kMaxTV = (int64_t)1 << 30;  // T and V each
 constexpr int64_t kRowBlockMax = 8192;
-// one bit per 256-token tile of a row block in a 32-bit mask (bwd_prep_kernel)
-static_assert(kRowBlockMax / kTile <= 32, "row block tiles exceed the tile mask");
 constexpr int64_t kFwdTargetWG = 2048;
 // dH split-K target: about one workgroup per CU.  Where a row block has fewer dH tiles
 // than CUs (short token shares, one-tile batches), more splits mean more partial sums
@@ -74,7 +72,7 @@ struct Plan {
   int64_t R, n_rb, Vc, n_vc, dh_splits, Tb;   // backward; Tb = n_rb * R
   int64_t comb_lanes, n_cblk;  // forward combine: lanes per token, blocks
   size_t off_pm, off_ps, off_zl, off_bs, off_bc, fwd_bytes;
-  size_t off_c, off_l2, off_mask, off_G, off_dh, off_ht, bwd_bytes;
+  size_t off_c, off_l2, off_list, off_G, off_dh, off_ht, bwd_bytes;
   size_t gtile_bytes, chunk_bound;
   size_t total;
 };
@@ -172,7 +170,7 @@ flce_status make_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows, Plan 
   off = 0;
   p.off_c = off;  off = align256(off + (size_t)p.Tb * 4);
   p.off_l2 = off; off = align256(off + (size_t)p.Tb * 4);
-  p.off_mask = off; off = align256(off + (size_t)p.n_rb * 4);
+  p.off_list = off; off = align256(off + 4 + (size_t)p.Tb / kTile * 5);  // count, list, flags
   p.off_G = off;  off = align256(off + (size_t)p.R * p.Vc * 2);
   p.off_dh = off; off = align256(off + (size_t)p.dh_splits * p.R * p.D * 4);
   p.off_ht = off; off = align256(off + (size_t)p.R * p.D * 2);
@@ -298,7 +296,7 @@ const char *kernel_name(int id) {
       "bwd_ht",      "bwd_grad",    "bwd_dh",      "bwd_dw",      "bwd_dh_out",
       "fill",        "dst_lse",     "dst_prep",    "dst_teacher", "dst_student",
       "dst_reduce",  "dst_dh",      "dst_dw",      "dst_combine", "policy",
-      "fwd_skip_prep"};
+      "fwd_skip_prep", "bwd_zero_rows"};
   return id > 0 && id < FLCE_KERNEL_COUNT ? names[id] : "?";
 }
 
@@ -395,16 +393,23 @@ flce_status make_xform(const flce_logit_transform *t, Xform &x, bool &cap) {
 // launch does not set is zero (null pointers, flags off).
 
 // H^T of a row block for the dW kernel's K-contiguous operand.
+// With a list in `map` the rows are its tiles' (T: the token count).
 flce_status launch_ht(const void *hidden, uint16_t *ht, int64_t D, int64_t R, int64_t rb0,
-                      int64_t rcount, hipStream_t s) {
+                      int64_t rcount, hipStream_t s, const RowMap &map = RowMap{},
+                      int64_t T = 0) {
   BwdHtParams t{};
   t.hidden = (const uint16_t *)hidden;
   t.ht = ht;
+  t.T = (int)T;
   t.D = (int)D;
   t.R = (int)R;
   t.rb0 = (int)rb0;
   t.rcount = (int)rcount;
-  bwd_ht_kernel<<<dim3((unsigned)cdiv(rcount, 64), (unsigned)cdiv(D, 64)), 256, 0, s>>>(t);
+  t.tiles_id = (int)cdiv(rcount, kTile);
+  t.map = map;
+  // a list never holds more tiles for a block than it has as laid out
+  const int64_t rows = map.list ? t.tiles_id * kTile : rcount;
+  bwd_ht_kernel<<<dim3((unsigned)cdiv(rows, 64), (unsigned)cdiv(D, 64)), 256, 0, s>>>(t);
   return launched(FLCE_KERNEL_BWD_HT, s);
 }
 
@@ -412,13 +417,13 @@ flce_status launch_ht(const void *hidden, uint16_t *ht, int64_t D, int64_t R, in
 // its bf16 gradient block G: token rows of pitch Gp, gcols vocabulary columns
 // (a multiple of 256), plain or grouped (written over an fp32 block: Gp =
 // 2 gcols, each 128-column group in the first half of its fp32 bytes).  A
-// NULL dhacc skips dH, a NULL grad_weight skips dW.  rb_mask (or NULL: no
-// skipping) marks the row block's token tiles that carry a gradient.
+// NULL dhacc skips dH, a NULL grad_weight skips dW.  `map` gives the row block's
+// token tiles (no list: as laid out).
 flce_status launch_dh_dw(const uint16_t *G, int Gp, int64_t gcols, bool grouped,
                          const void *weight, const uint16_t *ht, int64_t D, int64_t V, int64_t R,
                          int64_t rcount, int64_t vc0, int64_t vcount, int64_t dh_splits,
                          float *dhacc, float *grad_weight, bool acc_dh, bool acc_dw,
-                         const uint32_t *rb_mask, hipStream_t s) {
+                         const RowMap &map, hipStream_t s) {
   const int tiles_h = (int)cdiv(D, kTile);
   BwdDhParams h{};
   h.G = G;
@@ -435,7 +440,7 @@ flce_status launch_dh_dw(const uint16_t *G, int Gp, int64_t gcols, bool grouped,
   h.splits = (int)dh_splits;
   h.acc = dhacc;
   h.accumulate = acc_dh ? 1 : 0;
-  h.rb_mask = rb_mask;
+  h.map = map;
   const unsigned dh_grid = (unsigned)(h.tiles_m * h.tiles_n * h.splits);
   if (dhacc) {
     if (grouped)
@@ -459,7 +464,7 @@ flce_status launch_dh_dw(const uint16_t *G, int Gp, int64_t gcols, bool grouped,
   w.tiles_n = tiles_h;
   w.dW = grad_weight;
   w.accumulate = acc_dw ? 1 : 0;
-  w.rb_mask = rb_mask;
+  w.map = map;
   if (grouped)
     dst_dw_kernel<<<(unsigned)(w.tiles_m * w.tiles_n), kThreads, 0, s>>>(w);
   else
@@ -469,16 +474,20 @@ flce_status launch_dh_dw(const uint16_t *G, int Gp, int64_t gcols, bool grouped,
 
 // dH rows of a row block: sum of the split-K partials, rounded to bf16.
 flce_status launch_dh_out(const float *dhacc, void *grad_hidden, int64_t D, int64_t R,
-                          int64_t dh_splits, int64_t rb0, int64_t rcount, hipStream_t s) {
+                          int64_t dh_splits, int64_t rb0, int64_t rcount, hipStream_t s,
+                          const RowMap &map = RowMap{}, int64_t T = 0) {
   BwdDhOutParams o{};
   o.acc = dhacc;
   o.dH = (uint16_t *)grad_hidden;
+  o.T = (int)T;
+  o.map = map;
   o.D = (int)D;
   o.R = (int)R;
   o.splits = (int)dh_splits;
   o.rb0 = (int)rb0;
   o.rcount = (int)rcount;
-  const int64_t work = rcount * (D / 8);
+  // a list never holds more tiles for a block than it has as laid out
+  const int64_t work = (map.list ? cdiv(rcount, kTile) * kTile : rcount) * (D / 8);
   bwd_dh_out_kernel<<<(unsigned)std::min<int64_t>(cdiv(work, 256), 8192), 256, 0, s>>>(o);
   return launched(FLCE_KERNEL_BWD_DH_OUT, s);
 }
@@ -649,7 +658,7 @@ flce_status distill_run(bool jsd, float beta, const void *student_hidden,
     return launch_dh_dw(G, (int)(2 * p.Vc), p.Vc, true, student_weight, ht, Ds, V, p.R, rcount,
                         vc0, vcount, p.dh_splits, want_dh ? dhacc : nullptr,
                         want_dw ? grad_student_weight : nullptr, vc > 0,
-                        accumulate_grad_weight || rb > 0, nullptr, s);
+                        accumulate_grad_weight || rb > 0, RowMap{}, s);
   };
   const int nparts = (int)(p.n_vc * p.vsplits);
   auto reduce = [&](int64_t rb0, int64_t rcount) -> flce_status {
@@ -1046,7 +1055,11 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
   char *ws = (char *)workspace;
   float *cbuf = (float *)(ws + p.off_c);
   float *l2buf = (float *)(ws + p.off_l2);
-  uint32_t *rb_mask = (uint32_t *)(ws + p.off_mask);
+  // the token tiles with a gradient: their count, their list, a flag per tile
+  int *n_act = (int *)(ws + p.off_list);
+  int *act_list = n_act + 1;
+  uint8_t *tile_act = (uint8_t *)(act_list + p.Tb / kTile);
+  const int64_t n_real = cdiv(T, kTile);
   uint16_t *G = (uint16_t *)(ws + p.off_G);
   float *dhacc = (float *)(ws + p.off_dh);
   uint16_t *ht = (uint16_t *)(ws + p.off_ht);
@@ -1063,16 +1076,33 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
   pr.mode = mode;
   pr.c = cbuf;
   pr.lse2 = l2buf;
-  pr.tiles_rb = (int)(p.R / kTile);
-  pr.rb_mask = rb_mask;
+  pr.n_real = (int)n_real;
+  pr.tile_act = tile_act;
+  pr.act_list = act_list;
+  pr.n_act = n_act;
   bwd_prep_kernel<<<1, 1024, 0, s>>>(pr);
   FLCE_TRY(launched(FLCE_KERNEL_BWD_PREP, s));
+  if (grad_hidden) {  // the rows of tiles left out
+    bwd_zero_rows_kernel<<<(unsigned)n_real, 256, 0, s>>>(tile_act, (int)T, (int)D,
+                                                          (uint16_t *)grad_hidden);
+    FLCE_TRY(launched(FLCE_KERNEL_BWD_ZERO_ROWS, s));
+  }
 
+  // Row block rb takes tiles [rb * TR, rb * TR + TR) of the list: tiles without gradient
+  // are left out and the rest packed into the leading row blocks (with every tile
+  // listed, the blocks are the tiles as laid out).
+  const int64_t TR = p.R / kTile;
   for (int64_t rb = 0; rb < p.n_rb; ++rb) {
     const int64_t rb0 = rb * p.R;
     const int64_t rcount = std::min<int64_t>(p.R, T - rb0);
     if (rcount <= 0) break;
-    if (grad_weight) FLCE_TRY(launch_ht(hidden, ht, D, p.R, rb0, rcount, s));
+    RowMap map{};
+    map.list = act_list;
+    map.count = n_act;
+    map.n_real = (int)n_real;
+    map.tile0 = (int)(rb * TR);
+    map.tiles_rb = (int)TR;
+    if (grad_weight) FLCE_TRY(launch_ht(hidden, ht, D, p.R, rb0, rcount, s, map, T));
     for (int64_t vc = 0; vc < p.n_vc; ++vc) {
       const int64_t vc0 = vc * p.Vc;
       const int64_t vcount = std::min<int64_t>(p.Vc, V - vc0);
@@ -1088,29 +1118,31 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
       g.T = (int)T;
       g.D = (int)D;
       g.V = (int)V;
-      g.rb0 = (int)rb0;
       g.vc0 = (int)vc0;
       g.n_vt = (int)cdiv(vcount, kTile);
       g.tiles_n = (int)cdiv(rcount, kTile);
-      // about one workgroup per CU, each walking n_vt / vsplits vocabulary tiles
-      g.vsplits = (int)std::min<int64_t>(g.n_vt, std::max<int64_t>(1, cdiv(kCUs, g.tiles_n)));
+      g.map = map;
       g.xf = xf;
       g.G = G;
       g.Gp = (int)p.Vc;
-      g.rb_mask = rb_mask + rb;
-      const unsigned grid = (unsigned)(g.tiles_n * g.vsplits);
+      // About one workgroup per CU, each walking n_vt / vsplits vocabulary tiles, for
+      // the n tiles the block turns out to hold (at most tiles_n): the grid covers the
+      // largest n * vsplits(n), and the kernel's workgroups past its own count exit.
+      int64_t grid = 0;
+      for (int64_t n = 1; n <= g.tiles_n; ++n)
+        grid = std::max(grid, n * std::min<int64_t>(g.n_vt, std::max<int64_t>(1, cdiv(kCUs, n))));
       if (cap)
-        bwd_grad_kernel<true><<<grid, kThreads, 0, s>>>(g);
+        bwd_grad_kernel<true><<<(unsigned)grid, kThreads, 0, s>>>(g);
       else
-        bwd_grad_kernel<false><<<grid, kThreads, 0, s>>>(g);
+        bwd_grad_kernel<false><<<(unsigned)grid, kThreads, 0, s>>>(g);
       FLCE_TRY(launched(FLCE_KERNEL_BWD_GRAD, s));
 
       FLCE_TRY(launch_dh_dw(G, (int)p.Vc, p.Vc, false, weight, ht, D, V, p.R, rcount, vc0, vcount,
                             p.dh_splits, grad_hidden ? dhacc : nullptr, grad_weight, vc > 0,
-                            accumulate_grad_weight || rb > 0, rb_mask + rb, s));
+                            accumulate_grad_weight || rb > 0, map, s));
     }
     if (grad_hidden)
-      FLCE_TRY(launch_dh_out(dhacc, grad_hidden, D, p.R, p.dh_splits, rb0, rcount, s));
+      FLCE_TRY(launch_dh_out(dhacc, grad_hidden, D, p.R, p.dh_splits, rb0, rcount, s, map, T));
   }
   return FLCE_OK;
 }

@@ -261,6 +261,31 @@ struct FwdSkipPrepParams {
   int *n_act;
 };
 
+// Numbers the flagged tiles (flags[0, n) of 0 / 1, written by this block before the
+// call) in order: list[0, *count) by a block-wide scan over groups of 1024 flags.  For
+// a block of 1024 threads; scan is 1024 ints of LDS.
+__device__ __forceinline__ void list_flagged(const uint8_t *flags, int n, int *list, int *count,
+                                             int *scan) {
+  __syncthreads();  // the block's flag stores are visible to it
+  int base = 0;
+  for (int g = 0; g < n; g += 1024) {
+    const int tt = g + (int)threadIdx.x;
+    const int f = tt < n ? flags[tt] : 0;
+    scan[threadIdx.x] = f;
+    __syncthreads();
+    for (int w = 1; w < 1024; w <<= 1) {  // inclusive Hillis-Steele scan
+      const int v = (int)threadIdx.x >= w ? scan[threadIdx.x - w] : 0;
+      __syncthreads();
+      scan[threadIdx.x] += v;
+      __syncthreads();
+    }
+    if (f) list[base + scan[threadIdx.x] - 1] = tt;
+    base += scan[1023];
+    __syncthreads();  // scan[1023] read by all before the next group overwrites it
+  }
+  if (threadIdx.x == 0) *count = base;
+}
+
 __global__ void __launch_bounds__(1024) fwd_skip_prep_kernel(FwdSkipPrepParams p) {
   __shared__ int scan[1024];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -274,24 +299,7 @@ __global__ void __launch_bounds__(1024) fwd_skip_prep_kernel(FwdSkipPrepParams p
     const bool act = __builtin_amdgcn_ballot_w64(any) != 0;
     if (lane == 0) p.tile_act[tt] = act;
   }
-  __syncthreads();  // the block's flag stores are visible to it
-  int base = 0;
-  for (int g = 0; g < p.n_tt; g += 1024) {
-    const int tt = g + (int)threadIdx.x;
-    const int f = tt < p.n_tt ? p.tile_act[tt] : 0;
-    scan[threadIdx.x] = f;
-    __syncthreads();
-    for (int w = 1; w < 1024; w <<= 1) {  // inclusive Hillis-Steele scan
-      const int v = (int)threadIdx.x >= w ? scan[threadIdx.x - w] : 0;
-      __syncthreads();
-      scan[threadIdx.x] += v;
-      __syncthreads();
-    }
-    if (f) p.act_list[base + scan[threadIdx.x] - 1] = tt;
-    base += scan[1023];
-    __syncthreads();  // scan[1023] read by all before the next group overwrites it
-  }
-  if (threadIdx.x == 0) *p.n_act = base;
+  list_flagged(p.tile_act, p.n_tt, p.act_list, p.n_act, scan);
 }
 
 struct FwdCombineParams {
@@ -391,6 +399,36 @@ __global__ void __launch_bounds__(256)
 // ---------------------------------------------------------------------------
 // Backward.
 // ---------------------------------------------------------------------------
+// Token rows of a backward row block.  Without a list, row r of the block is token
+// 256 tile0 + r.  With one (the token tiles that hold a token with a gradient, in order,
+// from bwd_prep_kernel), the block holds list entries [tile0, tile0 + tiles_rb) and row r
+// is token 256 list[tile0 + r / 256] + r % 256: tiles without gradient are left out and
+// the others packed into the leading row blocks.  When every tile that holds a token is
+// listed (*count == n_real) that is the same as no list.
+struct RowMap {
+  const int *list;   // or null
+  const int *count;  // number of listed tiles
+  int n_real;        // tiles that hold tokens: ceil(T / 256)
+  int tile0;         // first tile (no list) or list entry of the block
+  int tiles_rb;      // tiles per row block
+};
+
+// Tiles of the block to compute: `fallback` (the count as laid out) unless a list leaves
+// tiles out; `ident` tells whether rows are laid out as without a list.  `cnt` is *count
+// (read early by the caller, so that its latency overlaps other work), unused without a
+// list.
+__device__ __forceinline__ int rowmap_tiles(const RowMap &m, int cnt, int fallback, bool &ident) {
+  ident = !m.list || cnt == m.n_real;
+  return ident ? fallback : min(max(cnt - m.tile0, 0), m.tiles_rb);
+}
+__device__ __forceinline__ int rowmap_count(const RowMap &m) { return m.list ? *m.count : 0; }
+// Token tile of the block's tile i.
+__device__ __forceinline__ int rowmap_tile(const RowMap &m, bool ident, int i) {
+  return ident ? m.tile0 + i : m.list[m.tile0 + i];
+}
+
+constexpr int kCuCount = 256;  // compute units of an MI355X (8 XCDs of 32)
+
 struct BwdPrepParams {
   const int64_t *labels;
   const float *lse;
@@ -400,9 +438,10 @@ struct BwdPrepParams {
   int T, V, T_pad, mode;
   float *c;     // [T_pad] per-token scale (0 where the row has no gradient)
   float *lse2;  // [T_pad] lse * log2(e); +inf where c == 0 so softmax terms vanish
-  int tiles_rb;        // 256-token tiles per row block (<= 32)
-  uint32_t *rb_mask;   // [T_pad / (256 tiles_rb)]: bit i set if tile i of the row block
-                       // holds a token with c != 0
+  int n_real;          // tiles that hold tokens: ceil(T / 256)
+  uint8_t *tile_act;   // [n_real]: the tile holds a token with c != 0
+  int *act_list;       // [n_real]: those tiles in order, *n_act of them
+  int *n_act;
 };
 
 __global__ void __launch_bounds__(1024) bwd_prep_kernel(BwdPrepParams p) {
@@ -416,8 +455,6 @@ __global__ void __launch_bounds__(1024) bwd_prep_kernel(BwdPrepParams p) {
     __syncthreads();
   }
   const int n_valid = scnt[0];
-  const int n_tiles = p.T_pad / kTile;
-  for (int b = threadIdx.x; b * p.tiles_rb < n_tiles; b += 1024) p.rb_mask[b] = 0u;
   const float sign = p.mode == 0 ? 1.f : -1.f;
   float gm = 0.f;
   if (!p.grad_out && n_valid > 0) gm = p.grad_mean[0] / (float)n_valid;
@@ -434,17 +471,29 @@ __global__ void __launch_bounds__(1024) bwd_prep_kernel(BwdPrepParams p) {
     p.c[t] = c;
     p.lse2[t] = l2;
   }
-  // Which token tiles carry any gradient, one bit per tile and a mask per row block:
-  // the backward GEMMs skip the others (their G rows are zero, so their dH rows are
-  // zero and they add nothing to dW).
-  // One wave per tile: each lane tests four of its 256 values.
-  __syncthreads();  // the block's writes of c and of the cleared masks are visible to it
+  // Which token tiles carry any gradient, and their list: the backward GEMMs take only
+  // those (G rows of the others are zero, so their dH rows are zero and they add
+  // nothing to dW).  One wave per tile: each lane tests four of its 256 values.
+  __syncthreads();  // the block's writes of c are visible to it
   const int lane = threadIdx.x & 63;
-  for (int tt = threadIdx.x >> 6; tt < n_tiles; tt += 1024 / 64) {
+  for (int tt = threadIdx.x >> 6; tt < p.n_real; tt += 1024 / 64) {
     const f32x4 v = *(const f32x4 *)(p.c + (size_t)tt * kTile + lane * 4);
     const bool nz = (v[0] != 0.f) | (v[1] != 0.f) | (v[2] != 0.f) | (v[3] != 0.f);
-    if (__builtin_amdgcn_ballot_w64(nz) != 0 && lane == 0)
-      atomicOr(p.rb_mask + tt / p.tiles_rb, 1u << (tt % p.tiles_rb));
+    const bool act = __builtin_amdgcn_ballot_w64(nz) != 0;
+    if (lane == 0) p.tile_act[tt] = act;
+  }
+  list_flagged(p.tile_act, p.n_real, p.act_list, p.n_act, scnt);
+}
+
+// dH rows of the token tiles without gradient are zero.  A block per tile.
+__global__ void __launch_bounds__(256) bwd_zero_rows_kernel(const uint8_t *tile_act, int T,
+                                                            int D, uint16_t *dH) {
+  const int tt = blockIdx.x;
+  if (tile_act[tt]) return;
+  const int t0 = tt * kTile, rows = min(kTile, T - t0), per_row = D >> 3;
+  for (int i = threadIdx.x; i < rows * per_row; i += 256) {
+    const int r = i / per_row, c8 = (i - r * per_row) * 8;
+    *(u32x4 *)(dH + (size_t)(t0 + r) * D + c8) = u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -454,13 +503,13 @@ struct BwdGradParams {
   const float *c, *lse2;
   int64_t ignore_index;
   int T, D, V;
-  int rb0, vc0;          // first token / vocabulary row of this block
+  int vc0;               // first vocabulary row of this chunk
   int n_vt;              // vocabulary tiles of the chunk that hold rows < V
-  int tiles_n, vsplits;  // token tiles of the row block; vocabulary ranges per token tile
+  int tiles_n;           // token tiles of the row block as laid out
+  RowMap map;            // the row block's token tiles
   Xform xf;              // logit transform; G is the gradient with respect to the raw logits
-  uint16_t *G;           // [R, Gp] bf16, row = token - rb0, col = vocab - vc0
+  uint16_t *G;           // [R, Gp] bf16, row = row of the block, col = vocab - vc0
   int Gp;
-  const uint32_t *rb_mask;  // this row block's tiles with a gradient (bwd_prep_kernel)
 };
 
 // G tiles of one row block and vocabulary chunk.  A workgroup keeps one
@@ -480,13 +529,19 @@ __global__ void __launch_bounds__(kThreads)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+  // About one workgroup per CU: n_here token tiles x vs vocabulary ranges, spread over
+  // the XCDs as a grid of exactly that size would be; the rest of the grid exits.
+  bool ident;
+  const int n_here = rowmap_tiles(p.map, rowmap_count(p.map), p.tiles_n, ident);
+  const int vs = min(p.n_vt, max(1, (kCuCount + n_here - 1) / max(n_here, 1)));
+  const int n_wg = n_here * vs;
+  if ((int)blockIdx.x >= n_wg) return;
   int tn, sp;
-  grouped_tile(xcd_contiguous(blockIdx.x, gridDim.x), p.tiles_n, p.vsplits, 8, tn, sp);
-  const int vt0 = (int)((int64_t)sp * p.n_vt / p.vsplits);
-  const int vt1 = (int)((int64_t)(sp + 1) * p.n_vt / p.vsplits);
-  const int t0 = p.rb0 + tn * kTile;
+  grouped_tile(xcd_contiguous(blockIdx.x, n_wg), n_here, vs, 8, tn, sp);
+  const int vt0 = (int)((int64_t)sp * p.n_vt / vs);
+  const int vt1 = (int)((int64_t)(sp + 1) * p.n_vt / vs);
+  const int t0 = rowmap_tile(p.map, ident, tn) * kTile;
   if (t0 >= p.T || vt0 >= vt1) return;
-  const uint32_t mask = *p.rb_mask;  // read beside the per-token values below
 
   // Per-token values of this lane's 8 token columns, loaded before any DMA.
   float cc[8], l2[8];
@@ -512,17 +567,6 @@ __global__ void __launch_bounds__(kThreads)
   A.init(p.weight + (size_t)v0 * p.D, p.D, min(kTile, p.V - v0), p.D, wave, lane);
   wait_vmcnt<0>();
   __syncthreads();
-  if (!((mask >> tn) & 1u)) {
-    // No token of the tile has a gradient: its G rows are zeros (what the full
-    // computation writes for c = 0), without the GEMM.
-    const int per_row = (vt1 - vt0) * (kTile / 8);  // 16-byte chunks of a row's range
-    uint16_t *g0 = p.G + (size_t)(t0 - p.rb0) * p.Gp + vt0 * kTile;
-    for (int i = threadIdx.x; i < kTile * per_row; i += kThreads) {
-      const int r = i / per_row, ch = i - r * per_row;
-      *(u32x4 *)(g0 + (size_t)r * p.Gp + ch * 8) = u32x4{0u, 0u, 0u, 0u};
-    }
-    return;
-  }
   pipe_prologue(A, B, smem, wave);
   Acc acc;
   for (int vt = vt0; vt < vt1; ++vt) {
@@ -538,7 +582,7 @@ __global__ void __launch_bounds__(kThreads)
     uint16_t *gcol = p.G + (vw - p.vc0);
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-      const int tl = t0 - p.rb0 + wn * 128 + nb * 16 + (lane & 15);  // row of G
+      const int tl = tn * kTile + wn * 128 + nb * 16 + (lane & 15);  // row of G
       const float c = cc[nb];
       const int lr = label_reg(yy[nb] - vw, lane);
       const bool any_label = __builtin_amdgcn_ballot_w64(lr >= 0) != 0;
@@ -639,7 +683,7 @@ struct BwdDhParams {
   int tiles_m, tiles_n, splits;
   float *acc;            // [splits, R, D] fp32
   int accumulate;
-  const uint32_t *rb_mask;  // this row block's tiles with a gradient, or null (no skipping)
+  RowMap map;            // the row block's token tiles (tiles_m of them as laid out)
 };
 
 // One dH tile (split s of K): A = G rows, plain (OperandK) or grouped in
@@ -649,12 +693,15 @@ __device__ __forceinline__ void dh_tile(const BwdDhParams &p, lds_t *smem) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int L = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int per_split = p.tiles_m * p.tiles_n;
+  bool ident;
+  const int tiles_m = rowmap_tiles(p.map, rowmap_count(p.map), p.tiles_m, ident);
+  const int per_split = tiles_m * p.tiles_n;
+  const int n_wg = per_split * p.splits;  // the rest of the grid exits
+  if ((int)blockIdx.x >= n_wg) return;
+  const int L = xcd_contiguous(blockIdx.x, n_wg);
   const int s = L / per_split;
   int tm, tn;
-  grouped_tile(L - s * per_split, p.tiles_m, p.tiles_n, 8, tm, tn);
-  const uint32_t mask = p.rb_mask ? *p.rb_mask : ~0u;
+  grouped_tile(L - s * per_split, tiles_m, p.tiles_n, 8, tm, tn);
   const int ktiles = (p.Kc + kBK - 1) / kBK;
   const int kbeg = (int)((int64_t)s * ktiles / p.splits) * kBK;
   const int kend = min(p.Kc, (int)((int64_t)(s + 1) * ktiles / p.splits) * kBK);
@@ -670,25 +717,7 @@ __device__ __forceinline__ void dh_tile(const BwdDhParams &p, lds_t *smem) {
          min(kend, p.vcount) - kbeg, wave, lane);
   Acc acc;
   acc.zero();
-  const int nk = (kend - kbeg + kKS - 1) / kKS;
-  // The first stages are issued before the row block's mask is looked at, so that its
-  // read overlaps their loads.
-  if (nk > 0) pipe_prologue(A, B, smem, wave);
-  if (!((mask >> tm) & 1u)) {
-    // A token tile without gradient: its dH rows are zero.  The first chunk writes the
-    // zeros, later chunks (accumulating) have nothing to add.
-    wait_vmcnt<0>();  // the issued loads still write LDS: let them land first
-    if (!p.accumulate) {
-      const int cols = min(kTile, p.D - h0);
-      float *t = p.acc + ((size_t)s * p.R + (size_t)tm * kTile) * p.D + h0;
-      for (int i = threadIdx.x; i < kTile * (cols / 4); i += kThreads) {
-        const int r = i / (cols / 4), c4 = i - r * (cols / 4);
-        *(f32x4 *)(t + (size_t)r * p.D + c4 * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-    return;
-  }
-  if (nk > 0) pipe_run(A, B, nk, smem, acc, wave, lane);
+  tile_mainloop(A, B, (kend - kbeg + kKS - 1) / kKS, smem, acc, wave, lane);
 
   // rows [tm*256, tm*256 + 256) of split s, all inside the R x D slice
   const float *tile = p.acc + ((size_t)s * p.R + (size_t)tm * kTile) * p.D;
@@ -708,18 +737,31 @@ __global__ void __launch_bounds__(kThreads)
 struct BwdHtParams {
   const uint16_t *hidden;  // [T, D]
   uint16_t *ht;            // [D, R]
-  int D, R, rb0, rcount;
+  int T, D, R, rb0, rcount;
+  int tiles_id;            // token tiles of the block as laid out
+  RowMap map;              // the row block's token tiles
 };
 
 __global__ void __launch_bounds__(256) bwd_ht_kernel(BwdHtParams p) {
   __shared__ uint16_t tile[64][72];  // [d][t]; 8 columns of padding
   const int t0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
   const int r8 = threadIdx.x >> 3, c8 = (threadIdx.x & 7) * 8;
+  // Rows [t0, t0 + 64) lie in one token tile: as laid out, tokens rb0 + t (t < rcount);
+  // from a list, that tile's tokens (rows of tiles past the list are not needed).
+  bool ident;
+  const int n_here = rowmap_tiles(p.map, rowmap_count(p.map), p.tiles_id, ident);
+  int src0 = p.rb0 + t0, nsrc = p.rcount - t0;
+  if (!ident) {
+    const int i = t0 / kTile;
+    if (i >= n_here) return;
+    src0 = rowmap_tile(p.map, false, i) * kTile + t0 % kTile;
+    nsrc = p.T - src0;
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int tr = r8 + 32 * j, t = t0 + tr, d = d0 + c8;  // d % 8 == 0 and D % 8 == 0
+    const int tr = r8 + 32 * j, d = d0 + c8;  // d % 8 == 0 and D % 8 == 0
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (t < p.rcount && d < p.D) v = *(const u32x4 *)(p.hidden + (size_t)(p.rb0 + t) * p.D + d);
+    if (tr < nsrc && d < p.D) v = *(const u32x4 *)(p.hidden + (size_t)(src0 + tr) * p.D + d);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       tile[c8 + 2 * e][tr] = (uint16_t)(v[e] & 0xffffu);
@@ -749,7 +791,7 @@ struct BwdDwParams {
   int tiles_m, tiles_n;
   float *dW;             // [V, D] fp32
   int accumulate;
-  const uint32_t *rb_mask;  // this row block's tiles with a gradient, or null (no skipping)
+  RowMap map;            // the row block's token tiles
 };
 
 // One dW tile: A = G^T, plain (OperandMN) or grouped (OperandMNG).
@@ -763,11 +805,10 @@ __device__ __forceinline__ void dw_tile(const BwdDwParams &p, lds_t *smem) {
   const int v0 = p.vc0 + tm * kTile;
   if (v0 >= p.V) return;  // the whole tile lies past the vocabulary
   const int h0 = tn * kTile;
+  const int cnt = rowmap_count(p.map);  // used after the first stages are issued
 
-  const uint32_t mask = p.rb_mask ? *p.rb_mask : ~0u;
-
-  // G^T: G[k = token][m = vocabulary]; H^T[h0 + n][k = token], K-contiguous, zeros past
-  // rcount.  K (tokens) [kbeg, kend) starts as the whole row block.
+  // G^T: G[k = row][m = vocabulary]; H^T[h0 + n][k = row], K-contiguous, zeros past
+  // rcount.  K (rows of the block) starts as laid out, [0, rcount).
   const uint16_t *g_col = p.G + (OA::kGrouped ? grouped_col(tm * kTile) : tm * kTile);
   const uint16_t *ht_row = p.ht + (size_t)h0 * p.R;
   const int hrows = min(kTile, p.D - h0);
@@ -779,22 +820,20 @@ __device__ __forceinline__ void dw_tile(const BwdDwParams &p, lds_t *smem) {
   acc.zero();
   int nk = (p.rcount + kKS - 1) / kKS;
   if (nk > 0) pipe_prologue(A, B, smem, wave);
-  // K runs from the first to the last token tile with a gradient: the G rows outside
-  // add exact zeros (inside, the recompute wrote zeros for tiles without gradient).
-  // The mask is looked at after the first stages are issued, so that its read overlaps
-  // their loads; a narrower range drains them and starts again.
-  const int nt = (p.rcount + kTile - 1) / kTile;
-  const uint32_t m = mask & (nt >= 32 ? ~0u : (1u << nt) - 1u);
-  const int kbeg = m ? __builtin_ctz(m) * kTile : 0;
-  const int kend = m ? min(p.rcount, (32 - __builtin_clz(m)) * kTile) : 0;
-  if (kbeg != 0 || kend != p.rcount) {
+  // A list that leaves tiles out packs the others into whole tiles of rows: K is then
+  // 256 rows per tile of the block.  The count is looked at after the first stages are
+  // issued, so that its read overlaps their loads; another K drains them and starts again.
+  bool ident;
+  const int n_here = rowmap_tiles(p.map, cnt, 0, ident);
+  if (!ident && n_here * kTile != p.rcount) {
+    const int kend = n_here * kTile;
     wait_vmcnt<0>();  // the issued loads still write LDS: let them land first
     __syncthreads();
-    nk = (kend - kbeg + kKS - 1) / kKS;
+    nk = (kend + kKS - 1) / kKS;
     if (nk <= 0 && p.accumulate) return;  // nothing to add to dW
     if (nk > 0) {
-      A.init(g_col + (size_t)kbeg * p.Gp, p.Gp, kTile, kend - kbeg, wave, lane);
-      B.init(ht_row + kbeg, p.R, hrows, ((kend + 7) & ~7) - kbeg, wave, lane);
+      A.init(g_col, p.Gp, kTile, kend, wave, lane);
+      B.init(ht_row, p.R, hrows, kend, wave, lane);
       pipe_prologue(A, B, smem, wave);
     }
   }
@@ -815,14 +854,24 @@ __global__ void __launch_bounds__(kThreads)
 struct BwdDhOutParams {
   const float *acc;   // [splits, R, D]
   uint16_t *dH;       // [T, D] bf16
-  int D, R, splits, rb0, rcount;
+  int T, D, R, splits, rb0, rcount;
+  RowMap map;         // the row block's token tiles
 };
 
 __global__ void __launch_bounds__(256) bwd_dh_out_kernel(BwdDhOutParams p) {
+  bool ident;
+  const int n_here = rowmap_tiles(p.map, rowmap_count(p.map), 0, ident);
   const int per_row = p.D >> 3;
-  const int64_t n = (int64_t)p.rcount * per_row;
+  const int64_t n = (int64_t)(ident ? p.rcount : n_here * kTile) * per_row;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     const int row = (int)(i / per_row), c8 = (int)(i - (int64_t)row * per_row) * 8;
+    // token of the row: rb0 + row as laid out (row < rcount), else through the list
+    // (rows of the batch's last tile may lie past T)
+    int tok = p.rb0 + row;
+    if (!ident) {
+      tok = rowmap_tile(p.map, false, row / kTile) * kTile + row % kTile;
+      if (tok >= p.T) continue;
+    }
     f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < p.splits; ++s) {
       const float *src = p.acc + ((size_t)s * p.R + row) * p.D + c8;
@@ -834,7 +883,7 @@ __global__ void __launch_bounds__(256) bwd_dh_out_kernel(BwdDhOutParams p) {
     o[1] = pack_bf16(lo[2], lo[3]);
     o[2] = pack_bf16(hi[0], hi[1]);
     o[3] = pack_bf16(hi[2], hi[3]);
-    *(u32x4 *)(p.dH + (size_t)(p.rb0 + row) * p.D + c8) = o;
+    *(u32x4 *)(p.dH + (size_t)tok * p.D + c8) = o;
   }
 }
 

@@ -168,8 +168,9 @@ flce_status flce_forward_noalloc(const void *hidden, const void *weight, const i
  * (a frozen lm_head); both NULL is FLCE_ERR_ARG.  lse must be the forward's
  * output for the same inputs and transform.  T == 0 is valid: grad_weight (if
  * given) is zeroed unless accumulating.  A tile of 256 consecutive tokens in
- * which every c_t is 0 (prompt tokens of a policy loss, say) skips the GEMMs:
- * its grad_hidden rows are written as zeros and it adds nothing to grad_weight,
+ * which every c_t is 0 (prompt tokens of a policy loss, say) is left out of the
+ * GEMMs (the other tiles are packed into the leading row blocks): its
+ * grad_hidden rows are written as zeros and it adds nothing to grad_weight,
  * exactly what computing it gives.
  */
 flce_status flce_backward(const void *hidden, const void *weight, const int64_t *labels,
@@ -420,7 +421,8 @@ enum {
   FLCE_KERNEL_DST_COMBINE = 18,   /* distillation: per-token divergence */
   FLCE_KERNEL_POLICY = 19,        /* policy losses: the loss kernels (2 or 3 launches) */
   FLCE_KERNEL_FWD_SKIP_PREP = 20, /* policy losses: list of the token tiles with a label */
-  FLCE_KERNEL_COUNT = 21
+  FLCE_KERNEL_BWD_ZERO_ROWS = 21, /* backward: dH rows of token tiles without gradient */
+  FLCE_KERNEL_COUNT = 22
 };
 
 flce_status flce_timing_begin(int32_t capacity);

@@ -108,9 +108,9 @@ def test_timing_rejects_before_any_device_call(flce):
     assert lib.flce_timing_end(ids, ms, 4, ctypes.byref(n), None) == 1     # timing is off
     assert b"not on" in lib.flce_last_error()
     assert lib.flce_timing_end(None, ms, 4, ctypes.byref(n), None) == 1
-    names = [lib.flce_kernel_name(i).decode() for i in range(1, 21)]
-    assert len(set(names)) == 20 and "?" not in names
-    assert lib.flce_kernel_name(0) == b"?" and lib.flce_kernel_name(21) == b"?"
+    names = [lib.flce_kernel_name(i).decode() for i in range(1, 22)]
+    assert len(set(names)) == 21 and "?" not in names
+    assert lib.flce_kernel_name(0) == b"?" and lib.flce_kernel_name(22) == b"?"
     assert names[5:8] == ["bwd_grad", "bwd_dh", "bwd_dw"]
 
 

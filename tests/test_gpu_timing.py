@@ -12,7 +12,8 @@ pytestmark = pytest.mark.gpu
 
 
 def _expected_ce(plan, with_mean=True):
-    names = ["fwd_lse", "fwd_combine"] + (["fwd_mean"] if with_mean else []) + ["bwd_prep"]
+    names = (["fwd_lse", "fwd_combine"] + (["fwd_mean"] if with_mean else [])
+             + ["bwd_prep", "bwd_zero_rows"])
     for _ in range(plan["row_blocks"]):
         names.append("bwd_ht")
         names += ["bwd_grad", "bwd_dh", "bwd_dw"] * plan["vocab_chunks"]
@@ -137,7 +138,7 @@ def test_timing_of_a_policy_loss_and_the_allocation_free_forward():
     plan = flce.describe_plan(w.T, w.H, w.V, w.chunk_rows)
     # the tile list and log-prob forward, the loss kernels, the log-prob backward, then the
     # second forward
-    want = (["fwd_skip_prep", "fwd_lse", "fwd_combine", "policy", "bwd_prep"]
+    want = (["fwd_skip_prep", "fwd_lse", "fwd_combine", "policy", "bwd_prep", "bwd_zero_rows"]
             + (["bwd_ht"] + ["bwd_grad", "bwd_dh", "bwd_dw"] * plan["vocab_chunks"]
                + ["bwd_dh_out"]) * plan["row_blocks"]
             + ["fwd_lse", "fwd_combine"])
