@@ -1,8 +1,9 @@
 """Token tiles without any gradient (a per-token upstream gradient that is zero on whole
-256-token tiles, as on the prompt tokens of a policy loss) skip the backward GEMMs: the
-recompute writes zero G rows without its GEMM, dH leaves their rows at zero and dW runs
-its K loop only from the first to the last tile with a gradient.  The results must match
-the oracle as everywhere else, and the skipped tokens' dH rows must be exact zeros."""
+256-token tiles, as on the prompt tokens of a policy loss) are left out of the backward
+GEMMs: the tiles with a gradient are listed on the device and packed into the leading row
+blocks, the recompute, dH and dW of each row block run over the tiles it holds, and the
+left-out tiles' dH rows are written as zeros.  The results must match the oracle as
+everywhere else, and the left-out tokens' dH rows must be exact zeros."""
 import numpy as np
 import pytest
 import torch
@@ -26,8 +27,8 @@ def _zero_tiles(T, tiles):
 
 
 # name, T, D, V, chunk_rows, zero tiles, mode: one row block with holes at the start, in
-# the middle and at the ragged end; many one-tile row blocks (chunk_rows 16) with whole
-# blocks and a whole-batch-but-one pattern
+# the middle and at the ragged end; many one-tile row blocks (chunk_rows 16), of which the
+# trailing ones end up empty once the active tiles are packed; all tiles but one
 CASES = [
     ("holes_one_block", 2600, 264, 3100, 200, (0, 1, 5, 10), "logprob"),
     ("holes_nll", 2600, 264, 3100, 200, (2, 3, 4), "nll"),
