@@ -238,7 +238,8 @@ flce_status make_distill_plan(int64_t T, int64_t Ds, int64_t Dt, int64_t V, int6
   p.Tb = p.n_rb * R;
   p.Vc = tiles_per_chunk * kTile;
   p.n_vc = n_vc;
-  p.vsplits = std::min<int64_t>(tiles_per_chunk, std::max<int64_t>(1, cdiv(kCUs, R / kTile)));
+  // at most one workgroup per CU (a second round would double the launch)
+  p.vsplits = std::min<int64_t>(tiles_per_chunk, std::max<int64_t>(1, kCUs / (R / kTile)));
   // dH: one workgroup per output tile once the tiles fill the chip (split-K
   // would add a read-modify-write of the partial sums per chunk).
   const int64_t dh_tiles = (R / kTile) * cdiv(Ds, kTile);
@@ -1125,12 +1126,12 @@ flce_status flce_backward(const void *hidden, const void *weight, const int64_t 
       g.xf = xf;
       g.G = G;
       g.Gp = (int)p.Vc;
-      // About one workgroup per CU, each walking n_vt / vsplits vocabulary tiles, for
+      // At most one workgroup per CU, each walking n_vt / vsplits vocabulary tiles, for
       // the n tiles the block turns out to hold (at most tiles_n): the grid covers the
       // largest n * vsplits(n), and the kernel's workgroups past its own count exit.
       int64_t grid = 0;
       for (int64_t n = 1; n <= g.tiles_n; ++n)
-        grid = std::max(grid, n * std::min<int64_t>(g.n_vt, std::max<int64_t>(1, cdiv(kCUs, n))));
+        grid = std::max(grid, n * std::min<int64_t>(g.n_vt, std::max<int64_t>(1, kCUs / n)));
       if (cap)
         bwd_grad_kernel<true><<<(unsigned)grid, kThreads, 0, s>>>(g);
       else

@@ -529,11 +529,12 @@ __global__ void __launch_bounds__(kThreads)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  // About one workgroup per CU: n_here token tiles x vs vocabulary ranges, spread over
-  // the XCDs as a grid of exactly that size would be; the rest of the grid exits.
+  // At most one workgroup per CU: n_here token tiles x vs vocabulary ranges with
+  // n_here * vs <= 256 (so that no workgroup waits for a second round), spread over the
+  // XCDs as a grid of exactly that size would be; the rest of the grid exits.
   bool ident;
   const int n_here = rowmap_tiles(p.map, rowmap_count(p.map), p.tiles_n, ident);
-  const int vs = min(p.n_vt, max(1, (kCuCount + n_here - 1) / max(n_here, 1)));
+  const int vs = min(p.n_vt, max(1, kCuCount / max(n_here, 1)));
   const int n_wg = n_here * vs;
   if ((int)blockIdx.x >= n_wg) return;
   int tn, sp;
