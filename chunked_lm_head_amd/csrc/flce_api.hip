@@ -54,16 +54,26 @@ constexpr int64_t kMaxD = 1 << 16;
 constexpr int64_t kMaxTV = (int64_t)1 << 30;  // T and V each
 constexpr int64_t kRowBlockMax = 8192;
 constexpr int64_t kFwdTargetWG = 2048;
-// dH split-K target: about one workgroup per CU.  Where a row block has fewer dH tiles
-// than CUs (short token shares, one-tile batches), more splits mean more partial sums
-// for bwd_dh_out to read, and two rounds of workgroups measured slower than one.
-constexpr int64_t kDhTargetWG = 256;
 constexpr int64_t kCUs = 256;  // compute units of an MI355X (8 XCDs of 32)
 constexpr int64_t kDhPartialCap = (int64_t)128 << 20;  // bytes of split-K partial sums
+
 constexpr int64_t kI32Bytes = ((int64_t)1 << 31) - 1;
 constexpr size_t kScratchBytes = FLCE_FORWARD_SCRATCH_BYTES;  // flce_forward_noalloc's array
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// dH split-K count for a row block of `tiles` output tiles, at most `sp_max`: the fewest
+// splits s that minimise ceil(tiles * s / 256) / s, the rounds of one workgroup per CU
+// each split's K range takes (a launch lasts about rounds * K / s).  Where a row block has
+// fewer dH tiles than CUs (short token shares, one-tile batches), splits fill the chip;
+// a split count that leaves a few workgroups for a second round costs a whole round.
+int64_t dh_split_count(int64_t tiles, int64_t sp_max) {
+  int64_t best = 1;
+  for (int64_t s = 2; s <= sp_max; ++s)
+    if (cdiv(tiles * s, kCUs) * best < cdiv(tiles * best, kCUs) * s) best = s;
+  return best;
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
@@ -155,10 +165,8 @@ flce_status make_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows, Plan 
   p.Vc = tiles_per_chunk * kTile;
   p.n_vc = n_vc;
   const int64_t dh_tiles = (R / kTile) * cdiv(D, kTile);
-  int64_t sp = std::max<int64_t>(1, cdiv(kDhTargetWG, dh_tiles));
-  sp = std::min(sp, std::max<int64_t>(1, kDhPartialCap / (R * D * 4)));
-  sp = std::min(sp, cdiv(p.Vc, kBK));
-  p.dh_splits = sp;
+  p.dh_splits = dh_split_count(
+      dh_tiles, std::min(std::max<int64_t>(1, kDhPartialCap / (R * D * 4)), cdiv(p.Vc, kBK)));
 
   size_t off = 0;
   p.off_pm = off; off = align256(off + (size_t)p.splits * p.T_pad * 4);
@@ -243,10 +251,8 @@ flce_status make_distill_plan(int64_t T, int64_t Ds, int64_t Dt, int64_t V, int6
   // dH: one workgroup per output tile once the tiles fill the chip (split-K
   // would add a read-modify-write of the partial sums per chunk).
   const int64_t dh_tiles = (R / kTile) * cdiv(Ds, kTile);
-  int64_t sp = std::max<int64_t>(1, cdiv(kCUs, dh_tiles));
-  sp = std::min(sp, std::max<int64_t>(1, kDhPartialCap / (R * Ds * 4)));
-  sp = std::min(sp, cdiv(p.Vc, kBK));
-  p.dh_splits = sp;
+  p.dh_splits = dh_split_count(
+      dh_tiles, std::min(std::max<int64_t>(1, kDhPartialCap / (R * Ds * 4)), cdiv(p.Vc, kBK)));
 
   size_t off = 0;
   p.off_pm = off;    off = align256(off + (size_t)p.splits * p.T_pad * 4);
