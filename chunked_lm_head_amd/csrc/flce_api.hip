@@ -53,6 +53,8 @@ flce_status fail(flce_status s, const char *fmt, ...) {
 constexpr int64_t kMaxD = 1 << 16;
 constexpr int64_t kMaxTV = (int64_t)1 << 30;  // T and V each
 constexpr int64_t kRowBlockMax = 8192;
+// Forward workgroups: token tiles x vocabulary splits, at most this many (8 per CU), so
+// that no launch ends with a ninth round of a few workgroups.
 constexpr int64_t kFwdTargetWG = 2048;
 constexpr int64_t kCUs = 256;  // compute units of an MI355X (8 XCDs of 32)
 constexpr int64_t kDhPartialCap = (int64_t)128 << 20;  // bytes of split-K partial sums
@@ -62,15 +64,17 @@ constexpr size_t kScratchBytes = FLCE_FORWARD_SCRATCH_BYTES;  // flce_forward_no
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// dH split-K count for a row block of `tiles` output tiles, at most `sp_max`: the fewest
-// splits s that minimise ceil(tiles * s / 256) / s, the rounds of one workgroup per CU
-// each split's K range takes (a launch lasts about rounds * K / s).  Where a row block has
-// fewer dH tiles than CUs (short token shares, one-tile batches), splits fill the chip;
-// a split count that leaves a few workgroups for a second round costs a whole round.
+// dH split-K count for a row block of `tiles` output tiles, at most `sp_max`.  A launch
+// lasts about ceil(tiles * s / 256) / s of a whole K walk: the rounds of one workgroup per
+// CU, each over 1/s of K.  Where a row block has fewer dH tiles than CUs (short token
+// shares, one-tile batches), splits fill the chip: the most that keep one round, and more
+// (several rounds) only for a gain of 10% or more, since every split adds partial sums for
+// bwd_dh_out to read.  A split count that leaves a few workgroups for a second round
+// costs a whole round.
 int64_t dh_split_count(int64_t tiles, int64_t sp_max) {
-  int64_t best = 1;
-  for (int64_t s = 2; s <= sp_max; ++s)
-    if (cdiv(tiles * s, kCUs) * best < cdiv(tiles * best, kCUs) * s) best = s;
+  int64_t best = std::max<int64_t>(1, std::min(kCUs / tiles, sp_max));
+  for (int64_t s = best + 1; s <= sp_max; ++s)
+    if (cdiv(tiles * s, kCUs) * best * 10 <= cdiv(tiles * best, kCUs) * s * 9) best = s;
   return best;
 }
 
@@ -152,7 +156,7 @@ flce_status make_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows, Plan 
   p.n_tt = cdiv(Tn, kTile);
   p.n_vt = cdiv(V, kTile);
   p.T_pad = p.n_tt * kTile;
-  p.splits = std::min<int64_t>(std::max<int64_t>(cdiv(kFwdTargetWG, p.n_tt), 1), p.n_vt);
+  p.splits = std::min<int64_t>(std::max<int64_t>(kFwdTargetWG / p.n_tt, 1), p.n_vt);
   p.comb_lanes = combine_lanes(p.splits);
   p.n_cblk = cdiv(Tn, 256 / p.comb_lanes);
 
@@ -221,7 +225,7 @@ flce_status make_distill_plan(int64_t T, int64_t Ds, int64_t Dt, int64_t V, int6
   p.n_tt = cdiv(Tn, kTile);
   p.n_vt = cdiv(V, kTile);
   p.T_pad = p.n_tt * kTile;
-  p.splits = std::min<int64_t>(std::max<int64_t>(cdiv(kFwdTargetWG, p.n_tt), 1), p.n_vt);
+  p.splits = std::min<int64_t>(std::max<int64_t>(kFwdTargetWG / p.n_tt, 1), p.n_vt);
   p.n_cblk = cdiv(Tn, 256);
   int64_t R, tiles_per_chunk, n_vc;
   block_shape(p.n_tt, p.n_vt, std::max(Ds, Dt), V, chunk_rows, 4, 4, R, tiles_per_chunk, n_vc);

@@ -68,9 +68,13 @@ def test_distill_workspace_within_the_chunk_bound(flce, T, Ds, Dt, V, cr):
     n = flce.distill_workspace_bytes(T, Ds, Dt, V, cr)
     R_max = 8192
     # the fp32 p_t block (G over it) within one chunk of fp32 logits (at least one tile),
-    # plus O(T) per-token arrays, per-workgroup partial sums and O(R D) student terms
+    # plus O(T) per-token arrays, per-workgroup partial sums, the forward's partials, the
+    # student's dH partial sums (split-K sums capped at 128 MiB, or one row block's) and
+    # its H^T (O(R D))
     block = max(cr * V * 4, 256 * 256 * 4)
-    linear = 64 * (T + R_max) + 2 * 4 * V * 64 + R_max * max(Ds, 8) * 4 * 2 + (40 << 20)
+    dh_sums = max(R_max * max(Ds, 8) * 4, 128 << 20)
+    linear = (64 * (T + R_max) + 2 * 4 * V * 64 + dh_sums + R_max * max(Ds, 8) * 2
+              + (8 << 20))
     assert 0 < n <= block + linear, (T, Ds, Dt, V, cr, n)
 
 
