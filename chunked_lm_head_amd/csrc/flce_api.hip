@@ -136,6 +136,90 @@ void block_shape(int64_t n_tt, int64_t n_vt, int64_t D, int64_t V, int64_t chunk
   n_vc = cdiv(n_vt, tiles_per_chunk);
 }
 
+// Backward time of a plan, in microseconds, from a model fitted to 72 measured kernel
+// times of 24 plans on MI355X (hidden sizes 1,024 to 5,120, 2,048 to 20,480 tokens): a
+// round of 256 workgroups over a 256 x 256 x 256 tile takes kModelTile us (the recompute,
+// which also writes G, kModelGrad times that), a partly filled round (f of the CUs busy)
+// 0.8 + 0.2 f of a full one (its CUs hold a higher clock), the dH and dW epilogues'
+// read-modify-writes move kModelBwDh and kModelBwDw bytes per us, and a launch costs
+// kModelLaunch us.  r: token tiles per row block (the last one may be shorter), t:
+// vocabulary tiles per chunk, s: dH split count.
+constexpr double kModelTile = 6.0, kModelGrad = 1.12, kModelBwDh = 9.0e6, kModelBwDw = 4.5e6,
+                 kModelLaunch = 20.0;
+
+double model_rounds(int64_t wgs, double k) {
+  const int64_t full = wgs / kCUs, rem = wgs % kCUs;
+  return (double)full * k + (rem ? (0.8 + 0.2 * (double)rem / kCUs) * k : 0.0);
+}
+
+double model_bwd(int64_t n_tt, int64_t n_vt, int64_t D, int64_t r, int64_t t, int64_t s) {
+  const int64_t Dt = cdiv(D, kTile);
+  const int64_t n_rb = cdiv(n_tt, r), n_vc = cdiv(n_vt, t);
+  const int64_t rs[2] = {r, n_tt - (n_rb - 1) * r}, rn[2] = {n_rb - 1, 1};
+  const int64_t ts[2] = {t, n_vt - (n_vc - 1) * t}, tn[2] = {n_vc - 1, 1};
+  double us = 0.0;
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j) {
+      const double n = (double)(rn[i] * tn[j]);
+      if (n == 0.0) continue;
+      const int64_t ri = rs[i], tc = ts[j];
+      const int64_t vs = std::min<int64_t>(tc, std::max<int64_t>(1, kCUs / ri));
+      const double grad = (double)(cdiv(tc, vs) * Dt) * kModelTile * kModelGrad;
+      const double dh = model_rounds(ri * Dt * s, (double)tc / (double)s) * kModelTile;
+      const double dw = model_rounds(tc * Dt, (double)ri) * kModelTile;
+      us += n * (grad + dh + dw + 3.0 * kModelLaunch);
+    }
+  const double tile_bytes = (double)kTile * (double)D * 4.0;
+  us += (double)n_tt * tile_bytes * (double)s * (double)(2 * n_vc - 1) / kModelBwDh;  // dH sums
+  us += (double)n_vt * tile_bytes * (double)(2 * n_rb - 1) / kModelBwDw;              // dW
+  us += (double)n_tt * tile_bytes * ((double)s + 0.5) / kModelBwDh;                   // dh_out
+  us += 2.0 * (double)n_rb * kModelLaunch;
+  return us;
+}
+
+int64_t dh_splits_for(int64_t r, int64_t t, int64_t D) {
+  const int64_t cap = std::max<int64_t>(1, kDhPartialCap / (r * kTile * D * 4));
+  return dh_split_count(r * cdiv(D, kTile), std::min(cap, cdiv(t * kTile, kBK)));
+}
+
+// The cross-entropy backward's row block and chunk: where the model puts another choice
+// at least 5% below the one block_shape makes (partial rounds of 256 workgroups in dH or
+// dW, or a last chunk or row block that fills the chip poorly), that choice, among row
+// blocks of [half, all] of R (equalised over the tokens) and chunks of [half, all] of the
+// widest the budget allows for them.
+void fit_backward(int64_t n_tt, int64_t n_vt, int64_t D, int64_t V, int64_t chunk_rows,
+                  int64_t &R, int64_t &tiles_per_chunk, int64_t &n_vc) {
+  const int64_t r0 = R / kTile, t0 = tiles_per_chunk;
+  const double base = model_bwd(n_tt, n_vt, D, r0, t0, dh_splits_for(r0, t0, D));
+  double best = base;
+  int64_t br = r0, bt = t0;
+  if (chunk_rows > kMaxTV) chunk_rows = kMaxTV;
+  const int64_t cap = std::max<int64_t>(chunk_rows * V * 2, (int64_t)kTile * kTile);
+  int64_t last_r = 0;
+  for (int64_t rc = (r0 + 1) / 2; rc <= r0; ++rc) {
+    const int64_t r = cdiv(n_tt, cdiv(n_tt, rc));
+    if (r == last_r) continue;
+    last_r = r;
+    int64_t tm = cap / (r * kTile) / kTile;
+    tm = std::min(tm, (kI32Bytes / (2 * D)) / kTile);
+    tm = std::min(tm, (kI32Bytes / (2 * r * kTile)) / kTile);
+    tm = std::min(tm, n_vt);
+    for (int64_t t = std::max<int64_t>(1, tm / 2); t <= tm; ++t) {
+      const double c = model_bwd(n_tt, n_vt, D, r, t, dh_splits_for(r, t, D));
+      if (c < best) {
+        best = c;
+        br = r;
+        bt = t;
+      }
+    }
+  }
+  if (best < 0.95 * base) {
+    R = br * kTile;
+    tiles_per_chunk = bt;
+    n_vc = cdiv(n_vt, bt);
+  }
+}
+
 // Lanes that merge one token's split partials: the power of two covering the
 // splits, at most a wave.  A 256-thread block then takes 256 / lanes tokens.
 int64_t combine_lanes(int64_t splits) {
@@ -163,6 +247,7 @@ flce_status make_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows, Plan 
   // Backward blocking: bf16 gradient values, 2 bytes each.
   int64_t R, n_vc, tiles_per_chunk;
   block_shape(p.n_tt, p.n_vt, D, V, chunk_rows, 2, 2, R, tiles_per_chunk, n_vc);
+  fit_backward(p.n_tt, p.n_vt, D, V, chunk_rows, R, tiles_per_chunk, n_vc);
   p.R = R;
   p.n_rb = cdiv(p.n_tt * kTile, R);
   p.Tb = p.n_rb * R;
