@@ -172,6 +172,14 @@ def test_plan_at_the_workload_shapes(flce):
     assert p["token_tiles"] * p["fwd_splits"] >= 1024
     p = flce.describe_plan(256, 2048, 248320, 256)
     assert p["vocab_chunks"] == 1 and p["row_blocks"] == 1
+    # the full-size goldens sample tokens and dW rows on both sides of these row-block and
+    # vocabulary-chunk edges, so the plans at those shapes are fixed here
+    for T, V, rb, vc in [(16384, 151936, 8192, 8192), (32768, 128000, 8192, 7936),
+                         (131072, 151936, 8192, 8192)]:
+        p = flce.describe_plan(T, 4096, V, 256)
+        assert (p["row_block"], p["vocab_chunk"], p["dh_splits"]) == (rb, vc, 1), (T, V, p)
+    p = flce.describe_plan(256, 2048, 248320, 256)
+    assert (p["row_block"], p["vocab_chunk"], p["dh_splits"]) == (256, 248320, 32), p
 
 
 def _dst(flce, **over):
