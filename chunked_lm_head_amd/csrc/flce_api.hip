@@ -143,16 +143,24 @@ void block_shape(int64_t n_tt, int64_t n_vt, int64_t D, int64_t V, int64_t chunk
 // 0.8 + 0.2 f of a full one (its CUs hold a higher clock), the dH and dW epilogues'
 // read-modify-writes move kModelBwDh and kModelBwDw bytes per us, and a launch costs
 // kModelLaunch us.  r: token tiles per row block (the last one may be shorter), t:
-// vocabulary tiles per chunk, s: dH split count.
+// vocabulary tiles per chunk, s: dH split count, D: the hidden size of dH and dW, and
+// pass_units: the per-tile work of the passes that walk the vocabulary tiles of a
+// (row block, chunk), in 256-deep K tiles weighted by their epilogues (the recompute:
+// D / 256 x kModelGrad).
 constexpr double kModelTile = 6.0, kModelGrad = 1.12, kModelBwDh = 9.0e6, kModelBwDw = 4.5e6,
                  kModelLaunch = 20.0;
+// The distillation's block passes relative to a plain K walk, from the measured rates of
+// its teacher (p_t written in fp32) and KL student (p_t read, G written) passes against
+// the recompute's at distill_qwen3.
+constexpr double kModelTeacher = 1.15, kModelStudent = 1.29;
 
 double model_rounds(int64_t wgs, double k) {
   const int64_t full = wgs / kCUs, rem = wgs % kCUs;
   return (double)full * k + (rem ? (0.8 + 0.2 * (double)rem / kCUs) * k : 0.0);
 }
 
-double model_bwd(int64_t n_tt, int64_t n_vt, int64_t D, int64_t r, int64_t t, int64_t s) {
+double model_bwd(int64_t n_tt, int64_t n_vt, int64_t D, int64_t r, int64_t t, int64_t s,
+                 double pass_units) {
   const int64_t Dt = cdiv(D, kTile);
   const int64_t n_rb = cdiv(n_tt, r), n_vc = cdiv(n_vt, t);
   const int64_t rs[2] = {r, n_tt - (n_rb - 1) * r}, rn[2] = {n_rb - 1, 1};
@@ -164,10 +172,10 @@ double model_bwd(int64_t n_tt, int64_t n_vt, int64_t D, int64_t r, int64_t t, in
       if (n == 0.0) continue;
       const int64_t ri = rs[i], tc = ts[j];
       const int64_t vs = std::min<int64_t>(tc, std::max<int64_t>(1, kCUs / ri));
-      const double grad = (double)(cdiv(tc, vs) * Dt) * kModelTile * kModelGrad;
+      const double grad = (double)cdiv(tc, vs) * pass_units * kModelTile;
       const double dh = model_rounds(ri * Dt * s, (double)tc / (double)s) * kModelTile;
       const double dw = model_rounds(tc * Dt, (double)ri) * kModelTile;
-      us += n * (grad + dh + dw + 3.0 * kModelLaunch);
+      us += n * (grad + dh + dw + 3.0 * kModelLaunch);  // (one more launch per pass aside)
     }
   const double tile_bytes = (double)kTile * (double)D * 4.0;
   us += (double)n_tt * tile_bytes * (double)s * (double)(2 * n_vc - 1) / kModelBwDh;  // dH sums
@@ -182,30 +190,34 @@ int64_t dh_splits_for(int64_t r, int64_t t, int64_t D) {
   return dh_split_count(r * cdiv(D, kTile), std::min(cap, cdiv(t * kTile, kBK)));
 }
 
-// The cross-entropy backward's row block and chunk: where the model puts another choice
-// at least 5% below the one block_shape makes (partial rounds of 256 workgroups in dH or
-// dW, or a last chunk or row block that fills the chip poorly), that choice, among row
-// blocks of [half, all] of R (equalised over the tokens) and chunks of [half, all] of the
-// widest the budget allows for them.
-void fit_backward(int64_t n_tt, int64_t n_vt, int64_t D, int64_t V, int64_t chunk_rows,
-                  int64_t &R, int64_t &tiles_per_chunk, int64_t &n_vc) {
+// The backward's row block and chunk: where the model puts another choice at least 5%
+// below the one the budget rules make (partial rounds of 256 workgroups in dH or dW, or a
+// last chunk or row block that fills the chip poorly), that choice, among row blocks of
+// [half, all] of R (equalised over the tokens) and chunks of [half, all] of the widest the
+// budget allows for them.  The budget is block_shape's: elem_bytes per staged element
+// within chunk_rows * V * 4 bytes, widest_bytes per element of the widest array and the
+// lm_head rows of a chunk (D_max bf16 values each) below 2 GiB.
+void fit_backward(int64_t n_tt, int64_t n_vt, int64_t D, int64_t D_max, int64_t V,
+                  int64_t chunk_rows, int64_t elem_bytes, int64_t widest_bytes,
+                  double pass_units, int64_t &R, int64_t &tiles_per_chunk, int64_t &n_vc) {
   const int64_t r0 = R / kTile, t0 = tiles_per_chunk;
-  const double base = model_bwd(n_tt, n_vt, D, r0, t0, dh_splits_for(r0, t0, D));
+  const double base =
+      model_bwd(n_tt, n_vt, D, r0, t0, dh_splits_for(r0, t0, D), pass_units);
   double best = base;
   int64_t br = r0, bt = t0;
   if (chunk_rows > kMaxTV) chunk_rows = kMaxTV;
-  const int64_t cap = std::max<int64_t>(chunk_rows * V * 2, (int64_t)kTile * kTile);
+  const int64_t cap = std::max<int64_t>(chunk_rows * V * 4 / elem_bytes, (int64_t)kTile * kTile);
   int64_t last_r = 0;
   for (int64_t rc = (r0 + 1) / 2; rc <= r0; ++rc) {
     const int64_t r = cdiv(n_tt, cdiv(n_tt, rc));
     if (r == last_r) continue;
     last_r = r;
     int64_t tm = cap / (r * kTile) / kTile;
-    tm = std::min(tm, (kI32Bytes / (2 * D)) / kTile);
-    tm = std::min(tm, (kI32Bytes / (2 * r * kTile)) / kTile);
+    tm = std::min(tm, (kI32Bytes / (2 * D_max)) / kTile);
+    tm = std::min(tm, (kI32Bytes / (widest_bytes * r * kTile)) / kTile);
     tm = std::min(tm, n_vt);
     for (int64_t t = std::max<int64_t>(1, tm / 2); t <= tm; ++t) {
-      const double c = model_bwd(n_tt, n_vt, D, r, t, dh_splits_for(r, t, D));
+      const double c = model_bwd(n_tt, n_vt, D, r, t, dh_splits_for(r, t, D), pass_units);
       if (c < best) {
         best = c;
         br = r;
@@ -247,7 +259,8 @@ flce_status make_plan(int64_t T, int64_t D, int64_t V, int64_t chunk_rows, Plan 
   // Backward blocking: bf16 gradient values, 2 bytes each.
   int64_t R, n_vc, tiles_per_chunk;
   block_shape(p.n_tt, p.n_vt, D, V, chunk_rows, 2, 2, R, tiles_per_chunk, n_vc);
-  fit_backward(p.n_tt, p.n_vt, D, V, chunk_rows, R, tiles_per_chunk, n_vc);
+  fit_backward(p.n_tt, p.n_vt, D, D, V, chunk_rows, 2, 2,
+               (double)cdiv(D, kTile) * kModelGrad, R, tiles_per_chunk, n_vc);
   p.R = R;
   p.n_rb = cdiv(p.n_tt * kTile, R);
   p.Tb = p.n_rb * R;
@@ -330,6 +343,10 @@ flce_status make_distill_plan(int64_t T, int64_t Ds, int64_t Dt, int64_t V, int6
     tiles_per_chunk = tiles;
     n_vc = cdiv(p.n_vt, tiles);
   }
+  // per (row block, chunk): the teacher's block pass over Dt and the student's over Ds
+  fit_backward(p.n_tt, p.n_vt, Ds, std::max(Ds, Dt), V, chunk_rows, 4, 4,
+               (double)cdiv(Dt, kTile) * kModelTeacher + (double)cdiv(Ds, kTile) * kModelStudent,
+               R, tiles_per_chunk, n_vc);
   p.R = R;
   p.n_rb = cdiv(p.n_tt * kTile, R);
   p.Tb = p.n_rb * R;
