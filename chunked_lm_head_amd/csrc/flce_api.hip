@@ -867,22 +867,27 @@ flce_status forward_launch(const Plan &p, const Xform &xf, bool cap, const void 
   timing_start(s);
   if (T == 0) return mean_out ? fill(mean_out, 1, 0.f, s) : FLCE_OK;
 
-  // skip_buf (4 + 5 n_tt bytes, 4-aligned): the count and list of the token tiles with a
-  // label, then a flag per tile; tiles whose labels are all ignore_index are left out.
-  int *n_act = nullptr, *act_list = nullptr;
+  // skip_buf (8 + 5 n_tt bytes, 4-aligned): the count of the token tiles with a label,
+  // the forward's split count for them, their list, then a flag per tile; tiles whose
+  // labels are all ignore_index are left out.
+  int *n_act = nullptr, *act_list = nullptr, *splits_eff = nullptr;
   uint8_t *tile_act = nullptr;
   if (skip_buf && labels) {
     n_act = (int *)skip_buf;
-    act_list = n_act + 1;
+    splits_eff = n_act + 1;
+    act_list = n_act + 2;
     tile_act = (uint8_t *)(act_list + p.n_tt);
     FwdSkipPrepParams q{};
     q.labels = labels;
     q.ignore_index = ignore_index;
     q.T = (int)T;
     q.n_tt = (int)p.n_tt;
+    q.n_vt = (int)p.n_vt;
+    q.max_splits = (int)p.splits;
     q.tile_act = tile_act;
     q.act_list = act_list;
     q.n_act = n_act;
+    q.splits_eff = splits_eff;
     fwd_skip_prep_kernel<<<1, 1024, 0, s>>>(q);
     FLCE_TRY(launched(FLCE_KERNEL_FWD_SKIP_PREP, s));
   }
@@ -905,6 +910,7 @@ flce_status forward_launch(const Plan &p, const Xform &xf, bool cap, const void 
   a.zlab = (float *)(ws + p.off_zl);
   a.act_list = act_list;
   a.n_act = n_act;
+  a.splits_eff = splits_eff;
   if (cap)
     fwd_lse_kernel<true><<<(unsigned)(p.n_tt * p.splits), kThreads, 0, s>>>(a);
   else
@@ -916,6 +922,7 @@ flce_status forward_launch(const Plan &p, const Xform &xf, bool cap, const void 
   c.part_s = a.part_s;
   c.zlab = a.zlab;
   c.tile_act = tile_act;
+  c.splits_eff = splits_eff;
   c.labels = labels;
   c.ignore_index = ignore_index;
   c.T = (int)T;
@@ -1065,7 +1072,7 @@ flce_status flce_timing_end(int32_t *ids, float *ms, int32_t capacity, int32_t *
   return st;
 }
 
-// flce_forward, or (skip_buf non-null: 4 + 5 ceil(T / 256) bytes of scratch) the same
+// flce_forward, or (skip_buf non-null: 8 + 5 ceil(T / 256) bytes of scratch) the same
 // with the token tiles whose labels are all ignore_index left out: their out is 0 as
 // always, their lse -inf.
 static flce_status forward_entry(const void *hidden, const void *weight, const int64_t *labels,
@@ -1454,7 +1461,7 @@ flce_status policy_loss(int kind, const PolicyInputs &in, const flce_policy_para
   float *lse = (float *)(ws + l.off_lse);
   // Non-completion tokens need neither a log-prob nor an lse: tiles holding only those
   // are left out here as in the backward.  Their list borrows the per-token gradient
-  // buffer (align256(4 T) >= 4 + 5 ceil(T / 256) bytes), which the loss kernels write
+  // buffer (align256(4 T) >= 8 + 5 ceil(T / 256) bytes), which the loss kernels write
   // only after the forward has read the list.
   FLCE_TRY(forward_entry(hidden, weight, labels, T, D, V, ignore_index, chunk_rows,
                          FLCE_MODE_LOGPROB, transform, logp, lse, nullptr, workspace, l.flce,

@@ -109,6 +109,7 @@ struct FwdLseParams {
   float *zlab;              // [T_pad] logit of the label
   const int *act_list;      // token tiles to compute (fwd_skip_prep_kernel), or null: all
   const int *n_act;         // their count
+  const int *splits_eff;    // with a list: the vocabulary splits to use (<= splits)
 };
 
 constexpr int kLdsFwd = kPipeBytes;  // the partial-merge exchange reuses the ring
@@ -125,17 +126,18 @@ __global__ void __launch_bounds__(kThreads)
   // With a tile list, the first n_act * splits workgroups take the listed tiles, spread
   // over the XCDs as the whole grid would be (a workgroup's XCD is its index mod 8),
   // and the rest exit: the work stays balanced whichever tiles drop out.
-  int n_rows = p.n_tt, n_wg = (int)gridDim.x;
+  int n_rows = p.n_tt, n_wg = (int)gridDim.x, splits = p.splits;
   if (p.act_list) {
     n_rows = *p.n_act;
-    n_wg = n_rows * p.splits;
+    splits = *p.splits_eff;
+    n_wg = n_rows * splits;
     if ((int)blockIdx.x >= n_wg) return;
   }
   int tt, sp;
-  grouped_tile(xcd_contiguous(blockIdx.x, n_wg), n_rows, p.splits, 8, tt, sp);
+  grouped_tile(xcd_contiguous(blockIdx.x, n_wg), n_rows, splits, 8, tt, sp);
   if (p.act_list) tt = p.act_list[tt];
-  const int vt0 = (int)((int64_t)sp * p.n_vt / p.splits);
-  const int vt1 = (int)((int64_t)(sp + 1) * p.n_vt / p.splits);
+  const int vt0 = (int)((int64_t)sp * p.n_vt / splits);
+  const int vt1 = (int)((int64_t)(sp + 1) * p.n_vt / splits);
   const int t0 = tt * kTile;
 
   OperandK B;
@@ -248,24 +250,32 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
+constexpr int kCuCount = 256;  // compute units of an MI355X (8 XCDs of 32)
+
 // The token tiles holding at least one token whose label is not ignore_index, in
 // order, for a forward that leaves the others out: act_list[0, *n_act) and a flag per
 // tile.  One block; a wave tests a tile (four labels per lane), then a block-wide scan
-// numbers the active tiles of each group of 1024.
+// numbers the active tiles of each group of 1024.  It also picks the forward's
+// vocabulary splits for that many tiles (*splits_eff, at most max_splits, the partial
+// buffers' capacity): the s that minimises ceil(n_act * s / 256) * ceil(n_vt / s), the
+// rounds of one workgroup per CU times the vocabulary tiles each walks (ties: the
+// larger s).
 struct FwdSkipPrepParams {
   const int64_t *labels;
   int64_t ignore_index;
-  int T, n_tt;
+  int T, n_tt, n_vt, max_splits;
   uint8_t *tile_act;  // [n_tt]
   int *act_list;      // [n_tt]
   int *n_act;
+  int *splits_eff;
 };
 
 // Numbers the flagged tiles (flags[0, n) of 0 / 1, written by this block before the
-// call) in order: list[0, *count) by a block-wide scan over groups of 1024 flags.  For
-// a block of 1024 threads; scan is 1024 ints of LDS.
-__device__ __forceinline__ void list_flagged(const uint8_t *flags, int n, int *list, int *count,
-                                             int *scan) {
+// call) in order: list[0, *count) by a block-wide scan over groups of 1024 flags, and
+// returns the count to every thread.  For a block of 1024 threads; scan is 1024 ints of
+// LDS.
+__device__ __forceinline__ int list_flagged(const uint8_t *flags, int n, int *list, int *count,
+                                            int *scan) {
   __syncthreads();  // the block's flag stores are visible to it
   int base = 0;
   for (int g = 0; g < n; g += 1024) {
@@ -284,6 +294,7 @@ __device__ __forceinline__ void list_flagged(const uint8_t *flags, int n, int *l
     __syncthreads();  // scan[1023] read by all before the next group overwrites it
   }
   if (threadIdx.x == 0) *count = base;
+  return base;
 }
 
 __global__ void __launch_bounds__(1024) fwd_skip_prep_kernel(FwdSkipPrepParams p) {
@@ -299,12 +310,25 @@ __global__ void __launch_bounds__(1024) fwd_skip_prep_kernel(FwdSkipPrepParams p
     const bool act = __builtin_amdgcn_ballot_w64(any) != 0;
     if (lane == 0) p.tile_act[tt] = act;
   }
-  list_flagged(p.tile_act, p.n_tt, p.act_list, p.n_act, scan);
+  const int n = max(list_flagged(p.tile_act, p.n_tt, p.act_list, p.n_act, scan), 1);
+  if (threadIdx.x == 0) {
+    int best = 1;
+    int64_t best_cost = (int64_t)((n + kCuCount - 1) / kCuCount) * p.n_vt;
+    for (int s = 2; s <= min(p.max_splits, p.n_vt); ++s) {
+      const int64_t cost = (((int64_t)n * s + kCuCount - 1) / kCuCount) * ((p.n_vt + s - 1) / s);
+      if (cost <= best_cost) {
+        best = s;
+        best_cost = cost;
+      }
+    }
+    *p.splits_eff = best;
+  }
 }
 
 struct FwdCombineParams {
   const float *part_m, *part_s, *zlab;
   const uint8_t *tile_act;  // token tiles the forward computed, or null: all
+  const int *splits_eff;    // the forward's split count when it took a tile list, or null
   const int64_t *labels;
   int64_t ignore_index;
   int T, V, splits, T_pad, mode;
@@ -324,13 +348,14 @@ __global__ void __launch_bounds__(256) fwd_combine_kernel(FwdCombineParams p) {
   __shared__ double ssum[256];
   __shared__ int scnt[256];
   const int L = p.lanes, g = threadIdx.x / L, j = threadIdx.x % L, per = 256 / L;
+  const int splits = p.splits_eff ? *p.splits_eff : p.splits;
   double contrib = 0.0;
   int cnt = 0;
   {
     const int t = blockIdx.x * per + g;
     float M = -kInf, S = 0.f;  // a tile left out keeps the empty sum: lse -inf
     if (t < p.T && (!p.tile_act || p.tile_act[t / kTile])) {
-      for (int s = j; s < p.splits; s += L)
+      for (int s = j; s < splits; s += L)
         lse_merge(M, S, p.part_m[(size_t)s * p.T_pad + t], p.part_s[(size_t)s * p.T_pad + t]);
     }
     for (int w = 1; w < L; w <<= 1) {  // lanes of a group stay within one wave
@@ -427,7 +452,6 @@ __device__ __forceinline__ int rowmap_tile(const RowMap &m, bool ident, int i) {
   return ident ? m.tile0 + i : m.list[m.tile0 + i];
 }
 
-constexpr int kCuCount = 256;  // compute units of an MI355X (8 XCDs of 32)
 
 struct BwdPrepParams {
   const int64_t *labels;
