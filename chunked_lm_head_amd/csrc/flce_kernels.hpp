@@ -453,6 +453,24 @@ __device__ __forceinline__ int rowmap_tile(const RowMap &m, bool ident, int i) {
 }
 
 
+// Split layout of a row block's dH partial sums in the [splits, R, D] buffer: `s_eff` K
+// splits whose sums lie `stride` rows apart.  As planned (splits, R apart) unless the block
+// holds a list of tiles_m tiles, fewer than the planned splits can spread over the CUs:
+// then as many splits as keep one round of workgroups, stacked tiles_m * 256 rows apart so
+// that they fit the same buffer.  The dH kernel and bwd_dh_out_kernel both use it, and it
+// depends on the block alone, so every chunk of the block lays its sums out alike.
+__device__ __forceinline__ void dh_layout(bool ident, int tiles_m, int tiles_n, int splits,
+                                          int tiles_rb, int R, int &s_eff, int &stride) {
+  s_eff = splits;
+  stride = R;
+  if (ident || tiles_m <= 0) return;
+  const int s2 = min(kCuCount / (tiles_m * tiles_n), splits * tiles_rb / tiles_m);
+  if (s2 > splits) {
+    s_eff = s2;
+    stride = tiles_m * kTile;
+  }
+}
+
 struct BwdPrepParams {
   const int64_t *labels;
   const float *lse;
@@ -720,16 +738,18 @@ __device__ __forceinline__ void dh_tile(const BwdDhParams &p, lds_t *smem) {
   const int wm = wave >> 1, wn = wave & 1;
   bool ident;
   const int tiles_m = rowmap_tiles(p.map, rowmap_count(p.map), p.tiles_m, ident);
+  int splits, stride;
+  dh_layout(ident, tiles_m, p.tiles_n, p.splits, p.map.tiles_rb, p.R, splits, stride);
   const int per_split = tiles_m * p.tiles_n;
-  const int n_wg = per_split * p.splits;  // the rest of the grid exits
+  const int n_wg = per_split * splits;  // the rest of the grid exits
   if ((int)blockIdx.x >= n_wg) return;
   const int L = xcd_contiguous(blockIdx.x, n_wg);
   const int s = L / per_split;
   int tm, tn;
   grouped_tile(L - s * per_split, tiles_m, p.tiles_n, 8, tm, tn);
   const int ktiles = (p.Kc + kBK - 1) / kBK;
-  const int kbeg = (int)((int64_t)s * ktiles / p.splits) * kBK;
-  const int kend = min(p.Kc, (int)((int64_t)(s + 1) * ktiles / p.splits) * kBK);
+  const int kbeg = (int)((int64_t)s * ktiles / splits) * kBK;
+  const int kend = min(p.Kc, (int)((int64_t)(s + 1) * ktiles / splits) * kBK);
   const int h0 = tn * kTile;
 
   OA A;            // G rows of this tile, K = vocabulary (contiguous)
@@ -744,8 +764,8 @@ __device__ __forceinline__ void dh_tile(const BwdDhParams &p, lds_t *smem) {
   acc.zero();
   tile_mainloop(A, B, (kend - kbeg + kKS - 1) / kKS, smem, acc, wave, lane);
 
-  // rows [tm*256, tm*256 + 256) of split s, all inside the R x D slice
-  const float *tile = p.acc + ((size_t)s * p.R + (size_t)tm * kTile) * p.D;
+  // rows [tm*256, tm*256 + 256) of split s, all inside the buffer
+  const float *tile = p.acc + ((size_t)s * stride + (size_t)tm * kTile) * p.D;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, (uint32_t)kTile * (uint32_t)p.D * 4u);
   store_acc_block(acc, rs, p.D, wm * 128, h0 + wn * 128, p.D, p.accumulate != 0, lane);
 }
@@ -886,6 +906,9 @@ struct BwdDhOutParams {
 __global__ void __launch_bounds__(256) bwd_dh_out_kernel(BwdDhOutParams p) {
   bool ident;
   const int n_here = rowmap_tiles(p.map, rowmap_count(p.map), 0, ident);
+  int splits, stride;
+  dh_layout(ident, n_here, (p.D + kTile - 1) / kTile, p.splits, p.map.tiles_rb, p.R, splits,
+            stride);
   const int per_row = p.D >> 3;
   const int64_t n = (int64_t)(ident ? p.rcount : n_here * kTile) * per_row;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
@@ -898,8 +921,8 @@ __global__ void __launch_bounds__(256) bwd_dh_out_kernel(BwdDhOutParams p) {
       if (tok >= p.T) continue;
     }
     f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < p.splits; ++s) {
-      const float *src = p.acc + ((size_t)s * p.R + row) * p.D + c8;
+    for (int s = 0; s < splits; ++s) {
+      const float *src = p.acc + ((size_t)s * stride + row) * p.D + c8;
       lo += *(const f32x4 *)src;
       hi += *(const f32x4 *)(src + 4);
     }

@@ -34,6 +34,11 @@ CASES = [
     ("holes_nll", 2600, 264, 3100, 200, (2, 3, 4), "nll"),
     ("zero_row_blocks", 2100, 128, 3100, 16, (0, 3, 4, 8), "logprob"),
     ("all_but_one", 1500, 136, 2000, 200, (0, 1, 2, 4, 5), "nll"),
+    # a last packed row block of one or two tiles, whose dH spreads its K range over many
+    # more splits than planned (stacked in the same partial-sum buffer), over several
+    # vocabulary chunks; the second with the batch's ragged last tile in that block
+    ("small_packed_block", 4096, 264, 3100, 256, tuple(range(9, 16)), "logprob"),
+    ("small_packed_ragged", 6000, 520, 3100, 1024, tuple(range(10)), "nll"),
 ]
 
 
