@@ -15,7 +15,7 @@ import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 IGN = synth.IGNORE_INDEX
-N_CASES = 24
+N_CASES = 40
 MAX_WORK = 6e9        # T * V * D, so that the float64 oracle takes about a second per case
 
 
